@@ -1,0 +1,209 @@
+#!/usr/bin/env python3
+"""Benchmark: KDA chunked prefill tokens/s on one MI355X (plus decode tok/s).
+
+One step = one kda_chunk_fwd call over the prefill workload (B=4, H=16,
+T=2048, d_k=d_v=128, bf16 q/k/v, fp32 gates, chunk 64), inputs resident in
+HBM.  Steps rotate over NSETS independently seeded input sets (about 0.8 GB
+in total, well above the 256 MB Infinity Cache) so each call reads its inputs
+from HBM rather than from a cache warmed by the previous call.
+
+Printed: ONE JSON line with the headline prefill rate, the roofline of the
+prefill call (compulsory HBM bytes / measured call time against 8 TB/s), the
+decode workload (256 sequences x 32 heads, 512 MiB fp32 state, 1024 steps)
+with its own roofline, and the fp64 CPU oracle timed on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+METRIC = "KDA chunked prefill tokens/s at H=16,d=128; decode tok/s; % of roofline"
+NSETS = 4
+
+
+def prefill_bytes(B, T, H, dk, dv, esize=2, s0=False):
+    """Compulsory HBM bytes of one prefill call: q, k, v, o at their dtype,
+    alpha fp32 per key channel, beta fp32, S_final (and S0) fp32."""
+    tok = B * T * H
+    return (tok * (2 * dk + 2 * dv) * esize + tok * dk * 4 + tok * 4
+            + (2 if s0 else 1) * B * H * dv * dk * 4)
+
+
+def prefill_flops(B, T, H, dk, dv, C=64):
+    """Algorithmic flops of the chunked form per head-token, as executed:
+    6 dk dv + 2C(3dk + 2dv) + C^2/3."""
+    return B * T * H * (6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3)
+
+
+def decode_bytes(N, H, dk, dv, esize=2):
+    units = N * H
+    return units * (2 * dv * dk * 4 + (2 * dk + 2 * dv) * esize + dk * 4 + 4)
+
+
+def bench_prefill(args, torch, kda, inputs):
+    w = inputs.WORKLOADS["prefill"]
+    B, T, H, dk, dv = w["B"], w["T"], w["H"], w["dk"], w["dv"]
+    dev = torch.device("cuda:0")
+    sets = []
+    for s in range(NSETS):
+        inp = inputs.workload("prefill", seed=s, device=dev)
+        ws = torch.empty(kda.chunk_fwd_workspace_size(B, T, H, dk, dv, -1, kda.KDA_BF16),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty_like(inp["v"])
+        S = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+        sets.append((inp, ws, o, S))
+    torch.cuda.synchronize()
+
+    def step(i):
+        inp, ws, o, S = sets[i % NSETS]
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], out=o,
+                      S_final=S, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    call_ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(call_ms) / len(call_ms)
+    return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=wall, ms_per_step=wall * 1e3 / args.steps,
+                call_ms_mean=mean_ms, call_ms_median=call_ms[len(call_ms) // 2],
+                call_ms_min=call_ms[0], tokens=B * T)
+
+
+def bench_decode(args, torch, kda, inputs):
+    w = inputs.WORKLOADS["decode"]
+    N, H, dk, dv, steps = w["N"], w["H"], w["dk"], w["dv"], args.decode_steps
+    dev = torch.device("cuda:0")
+    S = inputs.decode_state(N, H, dk, dv, w["s0_std"], seed=0, device=dev)
+    toks = [inputs.decode_token(N, H, dk, dv, w["dtype"], w["alpha_lo"], step=s, device=dev)
+            for s in range(steps)]
+    o = torch.empty((N, H, dv), dtype=w["dtype"], device=dev)
+    # warm-up on a copy of the state (the timed run starts from the seeded state)
+    S_w = S.clone()
+    for s in range(min(8, steps)):
+        t = toks[s]
+        kda.decode_step(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S_w, out=o)
+    del S_w
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s in range(steps):
+        t = toks[s]
+        kda.decode_step(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S, out=o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    step_us = total_ms * 1e3 / steps
+    nbytes = decode_bytes(N, H, dk, dv)
+    achieved = nbytes / (step_us * 1e-6) / 1e9
+    return {"workload": f"decode N={N} H={H} d_k=d_v={dk} bf16, fp32 state {N * H * dv * dk * 4 >> 20} MiB",
+            "steps": steps, "tokens_per_s": N * steps / (total_ms * 1e-3), "us_per_step": step_us,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "bytes_per_step": nbytes}}
+
+
+def cpu_baseline(inputs, torch):
+    """The fp64 oracle on the prefill workload (all 64 (sequence, head) units,
+    2048 tokens each), timed on this host's cores."""
+    import oracle
+    inp = inputs.workload("prefill", seed=0, device="cpu")
+    args = [oracle._to_f64(inp[n]) for n in ("q", "k", "v", "alpha", "beta")]
+    threads = oracle.default_threads()
+    orc = oracle.get()
+    t0 = time.perf_counter()
+    orc.fwd(*args, n_threads=threads)
+    dt = time.perf_counter() - t0
+    w = inputs.WORKLOADS["prefill"]
+    tokens = w["B"] * w["T"]
+    return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole prefill workload (B=4 x T=2048 tokens, 16 heads, d=128) in fp64; "
+                      f"{dt:.2f} s wall on {threads} threads of {os.cpu_count()} host CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--decode-steps", type=int, default=1024)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calib-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus "
+              f"{args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_kda_amd as kda
+    from linear_attention_kda_amd import inputs
+
+    pf = bench_prefill(args, torch, kda, inputs)
+    nbytes = prefill_bytes(pf["B"], pf["T"], pf["H"], pf["dk"], pf["dv"])
+    flops = prefill_flops(pf["B"], pf["T"], pf["H"], pf["dk"], pf["dv"])
+    call_s = pf["call_ms_mean"] * 1e-3
+    achieved = nbytes / call_s / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(pf["tokens"] / (pf["ms_per_step"] * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pf["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill B=4 H=16 T=2048 d_k=d_v=128, bf16 q/k/v, fp32 gates, "
+                               "chunk 64, S0=0", "B": pf["B"], "T": pf["T"], "H": pf["H"],
+                   "d_k": pf["dk"], "d_v": pf["dv"], "chunk": 64, "input_sets": NSETS},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "kda_chunk_fwd call (chunk_prep_kernel + chunk_scan_kernel)",
+                     "algorithmic_bytes": nbytes,
+                     "call_us_mean": round(pf["call_ms_mean"] * 1e3, 2),
+                     "call_us_median": round(pf["call_ms_median"] * 1e3, 2),
+                     "mfma_frac": round(flops / call_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
+    }
+    if not args.no_decode:
+        result["decode"] = bench_decode(args, torch, kda, inputs)
+    if args.copy_calib_mib:
+        n = args.copy_calib_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calib_bytes"] = n
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inputs, torch)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,130 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * The operation.  Page "Kimi Delta Attention (KDA)" (brain.bigb.es), opening
+ * update equation and section "KDA: a separate gate per key channel", defines
+ * one head of KDA on a state S of shape d_v x d_k (keys to values; key
+ * channels are the columns of S):
+ *
+ *     S~_t   = S_{t-1} Diag(alpha_t)          forget, alpha_t in [0,1]^{d_k}
+ *     e_t    = beta_t (v_t - S~_t k_t)        predict and correct, beta_t in [0,1]
+ *     S_t    = S~_t + e_t k_t^T               write
+ *     o_t    = scale * S_t q_t                read, after the write
+ *
+ * with scale = d_k^{-1/2} by default and k_t of unit norm (a caller
+ * precondition; the library does not normalise).  The same page, section
+ * "Two schedules for one recurrence", states that a token-by-token schedule
+ * and a chunkwise schedule reach identical states and outputs; kda_chunk_fwd
+ * runs the chunkwise one (chunks of 64 tokens) and kda_decode_step the
+ * token-by-token one.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are DEVICE pointers, owned by the caller.  The
+ *    library allocates nothing and keeps no pointer after a call returns.
+ *  - Layouts are dense row-major with the last dimension contiguous; every
+ *    tensor pointer must be 16-byte aligned.
+ *  - Calls are asynchronous on `stream` (0 = the null stream); results are
+ *    valid once the stream reaches them.  No call synchronises the host.
+ *  - dtype selects the element type of q, k, v and o (KDA_F32 or KDA_BF16).
+ *    alpha, beta and every state tensor are always fp32.
+ *  - d_k and d_v must each be one of 16, 32, 64, 128.
+ *  - Errors are returned, never printed; nothing aborts.  Only conditions the
+ *    host can check are validated.  Values outside alpha, beta in [0,1],
+ *    non-monotone cu_seqlens or a non-unit k are not detected: the result is
+ *    then unspecified, but every memory access stays inside the buffers the
+ *    shapes describe.  A launch failure reported by the HIP runtime returns
+ *    KDA_ERR_HIP.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The stream type of the HIP runtime (same definition as HIP's own header). */
+typedef struct ihipStream_t *hipStream_t;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL_ARG = 1,            /* a required pointer is NULL              */
+  KDA_ERR_BAD_SHAPE = 2,           /* a size is negative or inconsistent     */
+  KDA_ERR_UNSUPPORTED_DIM = 3,     /* d_k or d_v not in {16, 32, 64, 128}    */
+  KDA_ERR_UNSUPPORTED_DTYPE = 4,   /* dtype is not KDA_F32 or KDA_BF16        */
+  KDA_ERR_MISALIGNED = 5,          /* a tensor pointer is not 16-B aligned   */
+  KDA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the query result */
+  KDA_ERR_VARLEN_REQUIRES_B1 = 7,  /* cu_seqlens given with B != 1           */
+  KDA_ERR_ALIAS = 8,               /* o overlaps an input                    */
+  KDA_ERR_HIP = 9                  /* the HIP runtime reported an error      */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Text for a status code (static storage; never NULL). */
+const char *kda_status_string(kda_status s);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes (host-only
+ * arithmetic, no device call).  For a packed batch pass B = 1 and N = the
+ * number of sequences; for a dense batch N may be anything (with B = 1 and
+ * N >= 0 the result covers both readings).  Returns 0 for invalid sizes.
+ */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v,
+                                    int N, kda_dtype dtype);
+
+/*
+ * Chunked prefill over whole sequences (page "Kimi Delta Attention (KDA)",
+ * section "Two schedules for one recurrence", the chunkwise schedule).
+ *
+ *  q, k     [B, T, H, d_k]  dtype      queries, unit-norm keys
+ *  v        [B, T, H, d_v]  dtype      values
+ *  alpha    [B, T, H, d_k]  fp32       per-key-channel forget gates
+ *  beta     [B, T, H]       fp32       write strengths
+ *  S0       [N, H, d_v, d_k] fp32      initial states, or NULL for zeros
+ *  cu_seqlens [N+1] int32, device, or NULL.  With offsets the batch is a
+ *           packed one: B must be 1, T is the packed token count, and
+ *           sequence n owns tokens [cu_seqlens[n], cu_seqlens[n+1]) (a
+ *           zero-length sequence leaves its state unchanged).  No state flows
+ *           between sequences.  Without offsets N is ignored (N = B).
+ *  scale    read scale; <= 0 selects d_k^{-1/2}
+ *  o        [B, T, H, d_v]  dtype      outputs (must not overlap an input)
+ *  S_final  [N, H, d_v, d_k] fp32      final states; may be the same buffer
+ *           as S0 (in-place update)
+ *  workspace / workspace_bytes: device scratch of at least
+ *           kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, N, dtype) bytes,
+ *           16-B aligned; its contents on entry do not matter.
+ *
+ * T = 0 (or an empty packed batch) copies S0 (or zeros) to S_final.
+ */
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
+                         const float *alpha, const float *beta,
+                         const float *S0, const int32_t *cu_seqlens, int N,
+                         int B, int T, int H, int d_k, int d_v, float scale,
+                         kda_dtype dtype, void *o, float *S_final,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
+ * One decode step for N independent sequences (page "Kimi Delta Attention
+ * (KDA)", section "Two schedules for one recurrence", the fused recurrent
+ * schedule): every (n, h) state takes one token and is updated in place.
+ *
+ *  q, k     [N, H, d_k]  dtype     v [N, H, d_v]  dtype
+ *  alpha    [N, H, d_k]  fp32      beta [N, H]   fp32
+ *  S        [N, H, d_v, d_k] fp32  read and overwritten with the new state
+ *  o        [N, H, d_v]  dtype     must not overlap S or an input
+ *  scale    <= 0 selects d_k^{-1/2}
+ */
+kda_status kda_decode_step(const void *q, const void *k, const void *v,
+                           const float *alpha, const float *beta, float *S,
+                           int N, int H, int d_k, int d_v, float scale,
+                           kda_dtype dtype, void *o, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

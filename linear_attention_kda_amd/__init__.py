@@ -1,0 +1,20 @@
+"""Kimi Delta Attention (KDA) on MI355X (gfx950): chunked prefill and decode.
+
+The computation runs in hand-written HIP kernels behind the C ABI declared
+in ``include/kda.h`` (library ``libkda.so`` in this directory).  This package
+is the thin Python binding over that ABI; torch supplies device memory and
+streams.  The library is loaded on first use of a binding name; if it is
+missing that raises ImportError (there is no fallback).
+"""
+_BINDING_NAMES = ("EXPORTED", "KDA_BF16", "KDA_F32", "LIB_PATH", "KdaError", "chunk_fwd",
+                  "chunk_fwd_workspace_size", "decode_step", "lib", "status_string")
+
+
+def __getattr__(name):
+    if name in _BINDING_NAMES:
+        from . import _binding
+        return getattr(_binding, name)
+    raise AttributeError(name)
+
+
+__all__ = list(_BINDING_NAMES)

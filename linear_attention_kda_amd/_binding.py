@@ -1,0 +1,167 @@
+"""ctypes binding of ``libkda.so`` (C ABI in ``include/kda.h``).
+
+Argument marshalling only: shapes and dtypes are checked, outputs and the
+workspace are allocated with torch on the inputs' device, and raw device
+pointers plus torch's current HIP stream are handed to the library.  Every
+step of the computation runs in the library's HIP kernels.  There is no
+fallback: if the library is missing the import fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libkda.so")
+
+KDA_F32 = 0
+KDA_BF16 = 1
+
+# names exported by include/kda.h
+EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
+            "kda_decode_step")
+
+
+class KdaError(RuntimeError):
+    """A non-OK status returned by the library."""
+
+    def __init__(self, where: str, status: int):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [i32]
+    lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    lib.kda_chunk_fwd.restype = i32
+    lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                  f32, i32, vp, vp, vp, sz, vp]
+    lib.kda_decode_step.restype = i32
+    lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status: int) -> str:
+    return lib.kda_status_string(int(status)).decode()
+
+
+def chunk_fwd_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, N: int = -1,
+                             dtype: int = KDA_BF16) -> int:
+    return int(lib.kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, N, dtype))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _prep(t):
+    """Contiguous and 16-byte aligned (the ABI's layout contract); a view that
+    starts mid-allocation at an unaligned address is copied."""
+    if t is None:
+        return None
+    t = t.contiguous()
+    if t.data_ptr() % 16:
+        t = t.clone()
+    return t
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, out=None,
+              S_final=None, workspace=None):
+    """Chunked prefill.  Returns (o, S_final).
+
+    Dense batch: q, k, alpha [B, T, H, d_k]; v [B, T, H, d_v]; beta [B, T, H].
+    Packed batch: pass ``cu_seqlens`` (int32, device, N+1 offsets) and tensors
+    with a packed token axis, [T, H, d] or [1, T, H, d].
+    S0: [N, H, d_v, d_k] fp32 or None.  ``S_final`` may be ``S0`` (in place).
+    """
+    import torch
+    dt = _dtype_code(q)
+    q, k, v, alpha, beta = map(_prep, (q, k, v, alpha, beta))
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
+        raise TypeError("alpha and beta must be float32")
+    d_k, d_v, H = q.shape[-1], v.shape[-1], q.shape[-2]
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        cu_seqlens = _prep(cu_seqlens)
+        B, T = 1, q.numel() // (H * d_k)
+        N = cu_seqlens.numel() - 1
+    else:
+        if q.dim() != 4:
+            raise ValueError("dense q must be [B, T, H, d_k]")
+        B, T = q.shape[0], q.shape[1]
+        N = B
+    if k.shape != q.shape or alpha.shape != q.shape:
+        raise ValueError("k and alpha must have the shape of q")
+    if v.numel() != B * T * H * d_v or beta.numel() != B * T * H:
+        raise ValueError("v / beta sizes do not match q")
+    if S0 is not None:
+        if S0.dtype != torch.float32:
+            raise TypeError("S0 must be float32")
+        S0 = _prep(S0)
+        if S0.numel() != N * H * d_v * d_k:
+            raise ValueError("S0 must be [N, H, d_v, d_k]")
+    dev = q.device
+    if out is None:
+        out = torch.empty(v.shape, dtype=v.dtype, device=dev)
+    if S_final is None:
+        S_final = torch.empty((N, H, d_v, d_k), dtype=torch.float32, device=dev)
+    ws_need = chunk_fwd_workspace_size(B, T, H, d_k, d_v, N if cu_seqlens is not None else -1, dt)
+    if workspace is None or workspace.numel() < ws_need:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
+                           _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
+                           float(scale) if scale else 0.0, dt, _ptr(out), _ptr(S_final),
+                           _ptr(workspace), workspace.numel(), _stream(dev))
+    if st != 0:
+        raise KdaError("kda_chunk_fwd", st)
+    return out, S_final
+
+
+def decode_step(q, k, v, alpha, beta, S, scale=None, *, out=None):
+    """One token for N sequences: q, k, alpha [N, H, d_k]; v [N, H, d_v];
+    beta [N, H]; S [N, H, d_v, d_k] fp32, updated in place.  Returns o."""
+    import torch
+    dt = _dtype_code(q)
+    if not S.is_contiguous() or S.dtype != torch.float32 or S.data_ptr() % 16:
+        raise ValueError("S must be a contiguous, 16-byte aligned float32 tensor (updated in place)")
+    q, k, v, alpha, beta = map(_prep, (q, k, v, alpha, beta))
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if S.shape != (N, H, d_v, d_k):
+        raise ValueError("S must be [N, H, d_v, d_k]")
+    if out is None:
+        out = torch.empty((N, H, d_v), dtype=v.dtype, device=q.device)
+    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S), N, H,
+                             d_k, d_v, float(scale) if scale else 0.0, dt, _ptr(out),
+                             _stream(q.device))
+    if st != 0:
+        raise KdaError("kda_decode_step", st)
+    return out

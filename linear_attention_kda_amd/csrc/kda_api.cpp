@@ -1,0 +1,164 @@
+// kda_api.cpp -- the exported C ABI (include/kda.h): argument validation,
+// workspace sizing and dispatch to the HIP launchers.  Host code only; every
+// step of the computation runs in the kernels of kda_prefill.hip and
+// kda_decode.hip.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "kda_launch.h"
+
+namespace {
+
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+Range range_of(const void *p, size_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+float default_scale(float scale, int dk) {
+  return scale > 0.f ? scale : 1.0f / std::sqrt((float)dk);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case KDA_ERR_BAD_SHAPE: return "a size is negative or the sizes are inconsistent";
+    case KDA_ERR_UNSUPPORTED_DIM: return "d_k and d_v must each be 16, 32, 64 or 128";
+    case KDA_ERR_UNSUPPORTED_DTYPE: return "dtype must be KDA_F32 or KDA_BF16";
+    case KDA_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
+    case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace is smaller than kda_chunk_fwd_workspace_size()";
+    case KDA_ERR_VARLEN_REQUIRES_B1: return "cu_seqlens requires B == 1";
+    case KDA_ERR_ALIAS: return "the output overlaps an input";
+    case KDA_ERR_HIP: return "the HIP runtime reported an error";
+  }
+  return "unknown status";
+}
+
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int N, kda_dtype dtype) {
+  if (B < 0 || T < 0 || H <= 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
+  const int esize = dtype == KDA_BF16 ? 2 : 4;
+  size_t need = kda::plan_workspace(false, B, T, H, d_k, B, esize).total;
+  if (B == 1 && N >= 0) {  // may be a packed batch of N sequences
+    const size_t pk = kda::plan_workspace(true, 1, T, H, d_k, N, esize).total;
+    if (pk > need) need = pk;
+  }
+  return need;
+}
+
+kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                         const float *S0, const int32_t *cu_seqlens, int N, int B, int T, int H, int d_k,
+                         int d_v, float scale, kda_dtype dtype, void *o, float *S_final, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
+  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
+  const bool packed = cu_seqlens != nullptr;
+  if (packed) {
+    if (B != 1) return KDA_ERR_VARLEN_REQUIRES_B1;
+    if (N < 0) return KDA_ERR_BAD_SHAPE;
+  } else {
+    N = B;
+  }
+  const size_t es = dtype == KDA_BF16 ? 2 : 4;
+  const size_t ntok = (size_t)B * T;
+  const size_t qk_bytes = ntok * H * d_k * es, v_bytes = ntok * H * d_v * es;
+  const size_t a_bytes = ntok * H * d_k * sizeof(float), b_bytes = ntok * H * sizeof(float);
+  const size_t s_bytes = (size_t)N * H * d_v * d_k * sizeof(float);
+  if (ntok > 0 && (!q || !k || !v || !alpha || !beta || !o)) return KDA_ERR_NULL_ARG;
+  if (s_bytes > 0 && !S_final) return KDA_ERR_NULL_ARG;
+  if (ntok > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
+  const void *ptrs[] = {q, k, v, alpha, beta, S0, cu_seqlens, o, S_final, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+
+  const kda::WorkspacePlan plan = kda::plan_workspace(packed, B, T, H, d_k, N, (int)es);
+  if (plan.total > 0 && (!workspace || workspace_bytes < plan.total)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+  if (ntok > 0) {
+    const Range ro = range_of(o, ntok * H * d_v * es);
+    const Range ins[] = {range_of(q, qk_bytes), range_of(k, qk_bytes), range_of(v, v_bytes),
+                         range_of(alpha, a_bytes), range_of(beta, b_bytes),
+                         range_of(S0, S0 ? s_bytes : 0), range_of(S_final, s_bytes),
+                         range_of(workspace, plan.total)};
+    for (const Range &r : ins)
+      if (overlaps(ro, r)) return KDA_ERR_ALIAS;
+  }
+  if (N == 0) return KDA_OK;
+
+  kda::PrefillArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.S0 = S0;
+  a.cu_seqlens = cu_seqlens;
+  a.o = o;
+  a.S_final = S_final;
+  a.ws = static_cast<char *>(workspace);
+  a.plan = plan;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.scale = default_scale(scale, d_k);
+  a.bf16 = dtype == KDA_BF16;
+  return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
+                           float *S, int N, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
+                           hipStream_t stream) {
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
+  if (N < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
+  const size_t units = (size_t)N * H;
+  if (units == 0) return KDA_OK;
+  if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_NULL_ARG;
+  const void *ptrs[] = {q, k, v, alpha, beta, S, o};
+  for (const void *p : ptrs)
+    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+  if (units > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
+  const size_t es = dtype == KDA_BF16 ? 2 : 4;
+  const Range ro = range_of(o, units * d_v * es);
+  const Range ins[] = {range_of(q, units * d_k * es), range_of(k, units * d_k * es),
+                       range_of(v, units * d_v * es), range_of(alpha, units * d_k * sizeof(float)),
+                       range_of(beta, units * sizeof(float)), range_of(S, units * d_v * d_k * sizeof(float))};
+  for (const Range &r : ins)
+    if (overlaps(ro, r)) return KDA_ERR_ALIAS;
+
+  kda::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.S = S;
+  a.o = o;
+  a.N = N;
+  a.H = H;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.scale = default_scale(scale, d_k);
+  a.bf16 = dtype == KDA_BF16;
+  return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// kda_launch.h -- internal interface between the C ABI (kda_api.cpp) and the
+// kernel launchers (kda_prefill.hip, kda_decode.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kChunkTokens = 64;
+
+// One record per (chunk, head) of the prefill workspace, written by the
+// chunk-prep kernel and read by the scan kernel.  Element type E is the
+// dtype of q/k/v (2 or 4 bytes).  Offsets in bytes.
+struct ChunkRecordLayout {
+  size_t kh;    // [64][dk]  keys decayed from the chunk start   (k_i * D_{0:i})
+  size_t qh;    // [64][dk]  queries decayed from the chunk start (q_i * D_{0:i})
+  size_t ktt;   // [dk][64]  keys decayed to the chunk end, transposed
+  size_t tb;    // [64][64]  (I + R)^{-1} Diag(beta), zero above the diagonal
+  size_t aqk;   // [64][64]  scaled causal q-k scores incl. diagonal, zero above
+  size_t p63;   // [dk] fp32 whole-chunk decay D_{0:63}
+  size_t bytes; // record size (multiple of 256)
+};
+
+inline ChunkRecordLayout chunk_record_layout(int dk, int esize) {
+  ChunkRecordLayout L;
+  L.kh = 0;
+  L.qh = L.kh + (size_t)64 * dk * esize;
+  L.ktt = L.qh + (size_t)64 * dk * esize;
+  L.tb = L.ktt + (size_t)64 * dk * esize;
+  L.aqk = L.tb + (size_t)64 * 64 * esize;
+  L.p63 = L.aqk + (size_t)64 * 64 * esize;
+  size_t end = L.p63 + (size_t)dk * sizeof(float);
+  L.bytes = (end + 255) / 256 * 256;
+  return L;
+}
+
+// Workspace = [index tables (packed batches only)] [chunk records].
+struct WorkspacePlan {
+  int n_seq;           // sequences
+  long long max_chunks;// chunk slots (dense: exact count)
+  size_t tables_bytes; // 0 for dense batches
+  size_t record_bytes;
+  size_t total;
+  // int32 table offsets (in elements from the workspace start), packed only
+  size_t seq_tok0, seq_chunk0, chunk_t0, chunk_len;
+};
+
+inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
+                                    int N, int esize) {
+  WorkspacePlan P{};
+  ChunkRecordLayout L = chunk_record_layout(dk, esize);
+  P.record_bytes = L.bytes;
+  if (packed) {
+    P.n_seq = N;
+    P.max_chunks = ((long long)T + kChunkTokens - 1) / kChunkTokens + N;
+    P.seq_tok0 = 0;
+    P.seq_chunk0 = P.seq_tok0 + (size_t)N + 1;
+    P.chunk_t0 = P.seq_chunk0 + (size_t)N + 1;
+    P.chunk_len = P.chunk_t0 + (size_t)P.max_chunks;
+    size_t n_int = P.chunk_len + (size_t)P.max_chunks;
+    P.tables_bytes = (n_int * sizeof(int32_t) + 255) / 256 * 256;
+  } else {
+    P.n_seq = B;
+    P.max_chunks = (long long)B * (((long long)T + kChunkTokens - 1) / kChunkTokens);
+    P.tables_bytes = 0;
+  }
+  P.total = P.tables_bytes + (size_t)P.max_chunks * H * P.record_bytes;
+  return P;
+}
+
+struct PrefillArgs {
+  const void *q, *k, *v;
+  const float *alpha, *beta, *S0;
+  const int32_t *cu_seqlens;  // device, or null for a dense batch
+  void *o;
+  float *S_final;
+  char *ws;                   // workspace base
+  WorkspacePlan plan;
+  int B, T, H, dk, dv;
+  float scale;
+  bool bf16;
+};
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+struct DecodeArgs {
+  const void *q, *k, *v;
+  const float *alpha, *beta;
+  float *S;
+  void *o;
+  int N, H, dk, dv;
+  float scale;
+  bool bf16;
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,101 @@
+"""The C ABI library loads and exports what include/kda.h declares; host-side
+argument validation returns the documented status codes (CPU only: every
+call here is rejected before any HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import linear_attention_kda_amd as pkg
+    pkg.lib  # loads libkda.so (ImportError if it was not built)
+    return pkg
+
+
+def test_exports_every_declared_symbol(kda):
+    declared = _declared_functions()
+    assert declared == sorted(kda.EXPORTED)
+    for name in declared:
+        assert hasattr(kda.lib, name), f"{name} not exported"
+
+
+def test_status_strings(kda):
+    for s in range(10):
+        assert kda.status_string(s) and kda.status_string(s) != "unknown status"
+    assert kda.status_string(99) == "unknown status"
+
+
+def test_workspace_size(kda):
+    # dense: one record per (chunk, head); a record holds three 64 x d_k tiles,
+    # two 64 x 64 tiles and d_k floats, rounded up to 256 bytes
+    rec = (3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4 + 255) // 256 * 256
+    assert kda.chunk_fwd_workspace_size(4, 2048, 16, 128, 128, -1, kda.KDA_BF16) == 4 * 32 * 16 * rec
+    assert kda.chunk_fwd_workspace_size(2, 0, 3, 32, 32, -1, kda.KDA_F32) == 0
+    # packed: tables plus (ceil(T/64) + N) chunk slots
+    packed = kda.chunk_fwd_workspace_size(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)
+    rec64 = (3 * 64 * 64 * 2 + 2 * 64 * 64 * 2 + 64 * 4 + 255) // 256 * 256
+    assert packed >= (16 + 5) * 2 * rec64
+    # invalid sizes
+    assert kda.chunk_fwd_workspace_size(1, 10, 2, 48, 64, -1, kda.KDA_BF16) == 0
+    assert kda.chunk_fwd_workspace_size(1, 10, 0, 64, 64, -1, kda.KDA_BF16) == 0
+    assert kda.chunk_fwd_workspace_size(1, 10, 2, 64, 64, -1, 7) == 0
+
+
+def _fwd(kda, **kw):
+    """Call kda_chunk_fwd with fake (never dereferenced) aligned pointers."""
+    P = lambda a: ctypes.c_void_p(a)
+    args = dict(q=P(0x10000), k=P(0x20000), v=P(0x30000), alpha=P(0x40000), beta=P(0x50000),
+                S0=None, cu=None, N=2, B=2, T=8, H=2, dk=16, dv=16, scale=0.0, dt=kda.KDA_BF16,
+                o=P(0x60000), S_final=P(0x70000), ws=P(0x80000), ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return kda.lib.kda_chunk_fwd(args["q"], args["k"], args["v"], args["alpha"], args["beta"],
+                                 args["S0"], args["cu"], args["N"], args["B"], args["T"], args["H"],
+                                 args["dk"], args["dv"], args["scale"], args["dt"], args["o"],
+                                 args["S_final"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+def test_chunk_fwd_validation(kda):
+    P = ctypes.c_void_p
+    assert _fwd(kda, dt=5) == 4                      # unsupported dtype
+    assert _fwd(kda, dk=48) == 3                     # unsupported dim
+    assert _fwd(kda, dv=256) == 3
+    assert _fwd(kda, H=0) == 2                       # bad shape
+    assert _fwd(kda, T=-1) == 2
+    assert _fwd(kda, q=None) == 1                    # null input
+    assert _fwd(kda, S_final=None) == 1
+    assert _fwd(kda, o=P(0x60004)) == 5              # misaligned
+    assert _fwd(kda, cu=P(0x90000), B=2) == 7        # packed needs B == 1
+    assert _fwd(kda, ws_bytes=10) == 6               # workspace too small
+    assert _fwd(kda, ws=None) == 6
+    assert _fwd(kda, o=P(0x30000)) == 8              # o aliases v
+    assert _fwd(kda, o=P(0x80000)) == 8              # o aliases the workspace
+
+
+def test_decode_validation(kda):
+    P = ctypes.c_void_p
+    good = dict(q=P(0x10000), k=P(0x20000), v=P(0x30000), alpha=P(0x40000), beta=P(0x50000),
+                S=P(0x60000), N=2, H=2, dk=16, dv=16, scale=0.0, dt=kda.KDA_F32, o=P(0x90000))
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return kda.lib.kda_decode_step(a["q"], a["k"], a["v"], a["alpha"], a["beta"], a["S"], a["N"],
+                                       a["H"], a["dk"], a["dv"], a["scale"], a["dt"], a["o"], None)
+    assert call(dt=3) == 4
+    assert call(dk=8) == 3
+    assert call(H=0) == 2
+    assert call(N=0) == 0                            # nothing to do
+    assert call(S=None) == 1
+    assert call(beta=P(0x50008)) == 5
+    assert call(o=P(0x60000)) == 8                   # o aliases S

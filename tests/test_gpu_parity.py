@@ -1,0 +1,91 @@
+"""HIP path vs the fp64 oracle on the five workloads (GPU).
+
+Tolerances are relative L2 over a whole tensor: 1e-5 for the fp32 path and
+2e-2 for bf16 inputs, on both o and S_final.
+"""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_kda_amd import inputs
+from tests.gpu_cases import TOL, announce, check, gpu_prefill, oracle_prefill, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_fp32():
+    announce("tiny B1 H2 T64 d16 fp32 seed0")
+    inp = to_dev(inputs.workload("tiny"))
+    o, S = gpu_prefill(inp)
+    o_ref, S_ref = oracle_prefill(inp)
+    check("o", o, o_ref, TOL[torch.float32])
+    check("S_final", S, S_ref, TOL[torch.float32])
+
+
+def test_prefill_bf16_full():
+    announce("prefill B4 H16 T2048 d128 bf16 seed0 (all heads)")
+    inp = inputs.workload("prefill", device="cuda")
+    o, S = gpu_prefill(inp)
+    o_ref, S_ref = oracle_prefill(inp)
+    check("o", o, o_ref, TOL[torch.bfloat16])
+    check("S_final", S, S_ref, TOL[torch.bfloat16])
+
+
+def test_long_context_sampled_heads():
+    """Full T=65536 run; the oracle recomputes four of the 32 heads."""
+    announce("long B1 H32 T65536 d128 bf16 seed0 (oracle heads 0,9,22,31)")
+    inp = inputs.workload("long", device="cuda")
+    o, S = gpu_prefill(inp)
+    heads = [0, 9, 22, 31]
+    o_ref, S_ref = oracle_prefill(inp, heads=heads)
+    idx = torch.tensor(heads, device="cuda")
+    check("o[heads]", o.index_select(2, idx), o_ref, TOL[torch.bfloat16])
+    check("S_final[heads]", S.index_select(1, idx), S_ref, TOL[torch.bfloat16])
+
+
+def test_varlen_sampled_sequences():
+    """Full packed batch on the GPU; the oracle recomputes 8 of the 64
+    sequences (the longest, the shortest and six others) on all 16 heads,
+    which covers the slow-gate heads 0-3 and the beta = 1 heads 4-7."""
+    announce("varlen 64 seqs H16 d128 bf16 seed0 (oracle on 8 sequences)")
+    inp = inputs.workload("varlen", device="cuda")
+    o, S = gpu_prefill(inp)
+    lens = inp["lengths"]
+    cu = inp["cu_seqlens"].cpu().long()
+    order = torch.argsort(lens)
+    pick = sorted(set([int(order[0]), int(order[-1])] + [int(order[i]) for i in (9, 20, 31, 42, 53, 60)]))
+    sub_lens = [int(lens[n]) for n in pick]
+    toks = torch.cat([torch.arange(int(cu[n]), int(cu[n + 1])) for n in pick])
+    sub = dict(q=inp["q"][toks.cuda()], k=inp["k"][toks.cuda()], v=inp["v"][toks.cuda()],
+               alpha=inp["alpha"][toks.cuda()], beta=inp["beta"][toks.cuda()],
+               S0=inp["S0"][torch.tensor(pick).cuda()],
+               cu_seqlens=torch.tensor(np.concatenate([[0], np.cumsum(sub_lens)]), dtype=torch.int32))
+    o_ref, S_ref = oracle_prefill(sub)
+    check("o[sampled seqs]", o[toks.cuda()], o_ref, TOL[torch.bfloat16])
+    check("S_final[sampled seqs]", S[torch.tensor(pick).cuda()], S_ref, TOL[torch.bfloat16])
+    # the whole output must be finite and every state written
+    assert torch.isfinite(o).all() and torch.isfinite(S).all()
+
+
+def test_decode_full_size_steps():
+    """Decode workload at full size (256 x 32 heads, 512 MiB state) for 4
+    steps; the oracle follows 96 sampled (sequence, head) states."""
+    import linear_attention_kda_amd as kda
+    import oracle
+    announce("decode N256 H32 d128 bf16 seed0, 4 steps (oracle on 96 units)")
+    w = inputs.WORKLOADS["decode"]
+    N, H, dk, dv = w["N"], w["H"], w["dk"], w["dv"]
+    S = inputs.decode_state(N, H, dk, dv, w["s0_std"], seed=0, device="cuda")
+    g = torch.Generator().manual_seed(5)
+    units = torch.randperm(N * H, generator=g)[:96]
+    nsel, hsel = units // H, units % H
+    S_ref = S[nsel.cuda(), hsel.cuda()].double().cpu().numpy()[:, None]
+    for step in range(4):
+        tok = inputs.decode_token(N, H, dk, dv, w["dtype"], w["alpha_lo"], step=step, device="cuda")
+        o = kda.decode_step(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], S)
+        torch.cuda.synchronize()
+        sel = lambda x: x[nsel.cuda(), hsel.cuda()].cpu()[:, None]
+        o_ref, S_ref = oracle.decode(sel(tok["q"]), sel(tok["k"]), sel(tok["v"]), sel(tok["alpha"]),
+                                     sel(tok["beta"]), S_ref)
+        check(f"o step {step}", o[nsel.cuda(), hsel.cuda()][:, None], o_ref, TOL[torch.bfloat16])
+    check("S after 4 steps", S[nsel.cuda(), hsel.cuda()][:, None], S_ref, TOL[torch.bfloat16])
