@@ -16,7 +16,7 @@ constexpr int kChunk = 64;   // tokens per chunk of the chunkwise schedule
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 template <typename E> __device__ __forceinline__ float to_f(E x) { return (float)x; }
 template <typename E> __device__ __forceinline__ E from_f(float x) { return (E)x; }

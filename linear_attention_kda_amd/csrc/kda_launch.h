@@ -11,16 +11,19 @@ namespace kda {
 constexpr int kChunkTokens = 64;
 
 // One record per (chunk, head) of the prefill workspace, written by the
-// chunk-prep kernel and read by the scan kernel.  Element type E is the
-// dtype of q/k/v (2 or 4 bytes).  Offsets in bytes.
+// chunk-prep kernel and read by the scan kernel.  Element type E is the dtype
+// of q/k/v (2 or 4 bytes).  The five matrices are stored as A operands of the
+// 16x16 matrix-core products, in fragment order (see frag_index in
+// kda_prefill.hip): each lane's share of a 16-row x slab tile is 16 (or 8)
+// contiguous bytes.  Offsets in bytes.
 struct ChunkRecordLayout {
-  size_t kh;    // [64][dk]  keys decayed from the chunk start   (k_i * D_{0:i})
-  size_t qh;    // [64][dk]  queries decayed from the chunk start (q_i * D_{0:i})
-  size_t ktt;   // [dk][64]  keys decayed to the chunk end, transposed
-  size_t tb;    // [64][64]  (I + R)^{-1} Diag(beta), zero above the diagonal
-  size_t aqk;   // [64][64]  scaled causal q-k scores incl. diagonal, zero above
+  size_t kh;    // k_i D_{0:i}          rows i (64),  K = d_k
+  size_t qh;    // q_i D_{0:i}          rows i (64),  K = d_k
+  size_t ktt;   // k_j D_{j+1:63}       rows c (d_k), K = 64 tokens (transposed)
+  size_t tb;    // (I + R)^{-1} Diag(beta), rows i (64), K = 64, zero above the diagonal
+  size_t aqk;   // scaled causal q-k scores incl. diagonal, rows i, K = 64, zero above
   size_t p63;   // [dk] fp32 whole-chunk decay D_{0:63}
-  size_t bytes; // record size (multiple of 256)
+  size_t bytes; // record size (multiple of 1024)
 };
 
 inline ChunkRecordLayout chunk_record_layout(int dk, int esize) {
@@ -32,7 +35,7 @@ inline ChunkRecordLayout chunk_record_layout(int dk, int esize) {
   L.aqk = L.tb + (size_t)64 * 64 * esize;
   L.p63 = L.aqk + (size_t)64 * 64 * esize;
   size_t end = L.p63 + (size_t)dk * sizeof(float);
-  L.bytes = (end + 255) / 256 * 256;
+  L.bytes = (end + 1023) / 1024 * 1024;
   return L;
 }
 

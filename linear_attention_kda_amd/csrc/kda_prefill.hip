@@ -21,8 +21,8 @@
 //     forward substitution (16x16 diagonal blocks inverted on the vector
 //     ALUs, off-diagonal blocks by fp32 MFMA); writes Tb = T Diag(beta) and A
 //     to a per-chunk workspace record.
-//   kernel 2 (scan, one workgroup per (sequence, head, d_v tile)): walks the
-//     chunks in order with S^T held in MFMA accumulators (fp32):
+//   kernel 2 (scan, one wave per (sequence, head, 16 value columns)): walks
+//     the chunks in order with S^T held in MFMA accumulators (fp32):
 //     X = [Kbnd; Qbnd] S^T, Ebar = V - X_top, E = Tb Ebar,
 //     O = s X_bot + A E, S^T = D_{0:63} S^T + Kend^T E.
 //
@@ -33,6 +33,7 @@
 #include "kda_launch.h"
 
 #include <cstdlib>
+#include <type_traits>
 
 namespace kda {
 namespace {
@@ -122,6 +123,48 @@ __device__ __forceinline__ bool chunk_span(const ChunkSource &cs, long long c,
   return true;
 }
 
+// ======================================================= fragment order
+// A operands of the 16x16 products are stored so that each lane's share of a
+// (16-row tile, k-slab) fragment is contiguous.  bf16 with K % 32 == 0 uses
+// v_mfma_f32_16x16x32_bf16 slabs of 32 columns: lane (row r, group g) holds
+// columns 4g..4g+3 then 16+4g..16+4g+3 of the slab (8 elements, 16 bytes).
+// bf16 with K == 16 and fp32 use slabs of 16 columns: lane (r, g) holds columns
+// 4g..4g+3 (bf16: 8 bytes for 16x16x16; fp32: 16 bytes, four 16x16x4 steps).
+// The B operands that meet these fragments come from accumulator tiles, whose
+// lane (column, g) holds rows 4g..4g+3, so the k order matches with no shuffle.
+template <typename E, int K> struct FragShape {
+  static constexpr bool wide = sizeof(E) == 2 && K % 32 == 0;
+  static constexpr int W = wide ? 32 : 16;  // columns per slab
+  static constexpr int KS = W / 4;          // elements per lane per fragment
+  static constexpr int NU = K / W;          // slabs per 16-row tile
+};
+
+// Element offset of A(i, c) in fragment order.
+template <typename E, int K>
+__device__ __forceinline__ int frag_index(int i, int c) {
+  typedef FragShape<E, K> F;
+  const int ci = c % F::W;
+  int g, pos;
+  if constexpr (F::wide) {
+    const int cc = ci & 15;
+    g = cc >> 2;
+    pos = (ci >> 4) * 4 + (cc & 3);
+  } else {
+    g = ci >> 2;
+    pos = ci & 3;
+  }
+  return (((i >> 4) * F::NU + c / F::W) * 64 + (i & 15) + 16 * g) * F::KS + pos;
+}
+
+// Copy a 64 x 64 tile from padded LDS rows (stride ld) to fragment order.
+template <typename E>
+__device__ __forceinline__ void lds_to_global_frag64(E *dst, const E *src, int ld) {
+  for (int idx = threadIdx.x; idx < 64 * 64; idx += kThreads) {
+    const int i = idx >> 6, c = idx & 63;
+    dst[frag_index<E, 64>(i, c)] = src[i * ld + c];
+  }
+}
+
 // ======================================================= kernel 1: chunk prep
 struct PrepKArgs {
   const void *q, *k;
@@ -142,18 +185,6 @@ template <int DK, typename E> struct PrepSmem {
   static constexpr size_t b_bytes = (size_t)2 * 64 * LDR * sizeof(float) + (size_t)64 * LDT * sizeof(E);
   static constexpr size_t bytes = a_bytes > b_bytes ? a_bytes : b_bytes;
 };
-
-// Copy `rows` rows of `rowlen` elements from padded LDS rows (stride ld) to a
-// dense global array, 16 bytes per thread per step.
-template <typename E>
-__device__ __forceinline__ void lds_to_global(char *dst, const E *src, int rows, int rowlen, int ld) {
-  const int vpr = rowlen * (int)sizeof(E) / 16;
-  for (int idx = threadIdx.x; idx < rows * vpr; idx += kThreads) {
-    const int r = idx / vpr, cv = idx % vpr;
-    *reinterpret_cast<uint4 *>(dst + ((size_t)r * rowlen * sizeof(E)) + cv * 16) =
-        *reinterpret_cast<const uint4 *>(reinterpret_cast<const char *>(src + r * ld) + cv * 16);
-  }
-}
 
 // Off-diagonal block (I, J), I > J, of T = (I + R)^{-1}:
 //   T_IJ = -T_II * sum_{K=J}^{I-1} R_IK T_KJ      (16x16 fp32 blocks, one wave)
@@ -263,15 +294,14 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrepKArgs a) {
       float av[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
+        // branch-free: load a valid token, then substitute the padding values
         const int tok = 16 * b + i;
-        av[i] = 1.f;
-        kv[m][i] = qv[m][i] = 0.f;
-        if (tok < L) {
-          const size_t off = base + (size_t)tok * hs + ch;
-          av[i] = a.alpha[off];
-          kv[m][i] = to_f(k[off]);
-          qv[m][i] = to_f(q[off]);
-        }
+        const bool live = tok < L;
+        const size_t off = base + (size_t)min(tok, L - 1) * hs + ch;
+        const float al = a.alpha[off], kx = to_f(k[off]), qx = to_f(q[off]);
+        av[i] = live ? al : 1.f;
+        kv[m][i] = live ? kx : 0.f;
+        qv[m][i] = live ? qx : 0.f;
       }
       float run = 1.f;
 #pragma unroll
@@ -316,7 +346,6 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrepKArgs a) {
         sF[DK + ch] = t2_;
         sF[2 * DK + ch] = t1_ * t2_;
       }
-      E kt[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int row = 16 * b + i;
@@ -325,15 +354,10 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrepKArgs a) {
         sQr[row * LD + ch] = from_f<E>(qr);
         sKl[row * LD + ch] = from_f<E>(kv[m][i] * ps[m][i]);
         sKd[row * LD + ch] = from_f<E>(kv[m][i] * __builtin_amdgcn_rcpf(pa[m][i]));
-        gKh[(size_t)row * DK + ch] = from_f<E>(kr * fb);   // k_i D_{0:i}
-        gQh[(size_t)row * DK + ch] = from_f<E>(qr * fb);   // q_i D_{0:i}
-        kt[i] = from_f<E>(kv[m][i] * ps[m][i] * gb);       // k_j D_{j+1:63}
+        gKh[frag_index<E, DK>(row, ch)] = from_f<E>(kr * fb);                  // k_i D_{0:i}
+        gQh[frag_index<E, DK>(row, ch)] = from_f<E>(qr * fb);                  // q_i D_{0:i}
+        gKtT[frag_index<E, 64>(ch, row)] = from_f<E>(kv[m][i] * ps[m][i] * gb);  // k_j D_{j+1:63}
       }
-      // row ch of Kend^T, columns 16b..16b+15: contiguous
-      uint4 *dst = reinterpret_cast<uint4 *>(gKtT + (size_t)ch * 64 + 16 * b);
-      const uint4 *srcv = reinterpret_cast<const uint4 *>(kt);
-#pragma unroll
-      for (int v4 = 0; v4 < (int)(16 * sizeof(E) / 16); ++v4) dst[v4] = srcv[v4];
     }
   }
   __syncthreads();
@@ -416,7 +440,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrepKArgs a) {
     }
     __syncthreads();
   }
-  lds_to_global(rec + a.lay.aqk, sOut, 64, 64, LDT);
+  lds_to_global_frag64(reinterpret_cast<E *>(rec + a.lay.aqk), sOut, LDT);
 
   // ---- T = (I + R)^{-1}: diagonal 16x16 blocks by forward substitution.
   if (w == 0) {
@@ -446,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrepKArgs a) {
     sOut[i * LDT + j] = from_f<E>(j <= i ? sT[i * LDR + j] * sBeta[j] : 0.f);
   }
   __syncthreads();
-  lds_to_global(rec + a.lay.tb, sOut, 64, 64, LDT);
+  lds_to_global_frag64(reinterpret_cast<E *>(rec + a.lay.tb), sOut, LDT);
 }
 
 // ======================================================= kernel 2: chunk scan
@@ -460,24 +484,118 @@ struct ScanKArgs {
   int H, dv, T, nct;
   const int32_t *seq_tok0, *seq_chunk0;  // packed batch tables, or null
   float scale;
+  int n_units;                           // sequences * heads
+  int wg_per_unit;                       // workgroups per unit (value tiles / waves per WG)
 };
 
-template <int DK, int BV, typename E>
-__global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanKArgs a) {
-  typedef typename MmaFor<E, DK>::type MK;  // products over d_k
-  typedef Mma<E, 32> MC;                    // products over the 64 tokens
-  constexpr int NB = BV / 16;               // value-column tiles
-  constexpr int CT = DK / 16;               // key-channel tiles of the state
-  constexpr int CTW = (CT + 3) / 4;         // state tiles per wave
-  constexpr int PAD = sizeof(E) == 2 ? 8 : 4;
-  constexpr int LDS_ = DK + PAD, LDE = 64 + PAD;
-  __shared__ __attribute__((aligned(16))) E sS[BV * LDS_];   // S (bf16/fp32 copy), [v][c]
-  __shared__ __attribute__((aligned(16))) E sEb[BV * LDE];   // Ebar^T, [v][i]
-  __shared__ __attribute__((aligned(16))) E sE[BV * LDE];    // E^T, [v][i]
+// B operands built from accumulator tiles.  Tile q of a K x 16 operand holds
+// rows 16q..16q+15; lane l has rows 4g..4g+3 (g = l/16) of column l%16, which
+// is exactly the k order of the fragment-ordered A operands (FragShape).
+template <typename E, int K> struct BOps;
 
-  const int vt = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+template <int K> struct BOps<bf16, K> {
+  typedef FragShape<bf16, K> F;
+  typedef typename std::conditional<F::wide, bf16x8, bf16x4>::type frag;
+  frag f[F::NU];
+  __device__ __forceinline__ void build(const f32x4 *t) {
+#pragma unroll
+    for (int u = 0; u < F::NU; ++u) {
+      if constexpr (F::wide) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          f[u][r] = (bf16)t[2 * u][r];
+          f[u][4 + r] = (bf16)t[2 * u + 1][r];
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) f[u][r] = (bf16)t[u][r];
+      }
+    }
+  }
+  // acc += A(16 rows, k < KU) * B(k < KU); `a` points at the row tile's first
+  // fragment.  KU is rounded up to whole slabs (columns beyond KU are zero).
+  template <int KU>
+  __device__ __forceinline__ f32x4 mma(const bf16 *a, f32x4 acc) const {
+    const int l = lane_id();
+#pragma unroll
+    for (int u = 0; u < (KU + F::W - 1) / F::W; ++u) {
+      const frag x = *reinterpret_cast<const frag *>(a + (u * 64 + l) * F::KS);
+      if constexpr (F::wide)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, f[u], acc, 0, 0, 0);
+      else
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(x, f[u], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
+template <int K> struct BOps<float, K> {
+  typedef FragShape<float, K> F;
+  f32x4 f[F::NU];
+  __device__ __forceinline__ void build(const f32x4 *t) {
+#pragma unroll
+    for (int u = 0; u < F::NU; ++u) f[u] = t[u];
+  }
+  template <int KU>
+  __device__ __forceinline__ f32x4 mma(const float *a, f32x4 acc) const {
+    const int l = lane_id();
+#pragma unroll
+    for (int u = 0; u < (KU + 15) / 16; ++u) {
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(a + (u * 64 + l) * 4);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], f[u][s], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+};
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds_base + 16 l (global_load_lds_dwordx4; the LDS base goes through M0).
+// M0 is written here and nowhere else in the kernels that call this.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);  // wave-uniform by construction
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
+}
+
+// Compile-time copy of ChunkRecordLayout for the scan's LDS image of a record.
+template <int DK, typename E> struct RecordShape {
+  static constexpr int es = sizeof(E);
+  static constexpr int kh = 0, qh = 64 * DK * es, ktt = 128 * DK * es, tb = 192 * DK * es;
+  static constexpr int aqk = tb + 4096 * es, p63 = aqk + 4096 * es;
+  static constexpr int bytes = (p63 + DK * 4 + 1023) / 1024 * 1024;
+  static constexpr int nbuf = 2 * bytes <= 160 * 1024 ? 2 : 1;   // double buffer if it fits
+};
+
+// Scan.  A workgroup of WPB waves serves one unit (sequence, head); each wave
+// owns 16 value columns and keeps S^T (d_k x 16) in fp32 accumulator tiles.
+// The chunk records stream into LDS with global_load_lds (16 bytes per lane,
+// no registers): the copy of chunk c+1 is issued right after the barrier that
+// opens chunk c, so it overlaps chunk c's matrix-core work.  Each product takes
+// its A operand from the LDS record (fragment order: conflict-free 16-byte
+// reads) and its B operand from the wave's own accumulators.  Workgroups of one
+// unit get ids congruent mod 8, which the dispatcher sends to one XCD.
+template <int DK, typename E, int WPB>
+__global__ __launch_bounds__(64 * WPB) void chunk_scan_kernel(ScanKArgs a) {
+  typedef RecordShape<DK, E> RS;
+  constexpr int CT = DK / 16;
+  typedef FragShape<E, DK> FK;   // products over d_k
+  typedef FragShape<E, 64> FT;   // products over the 64 tokens
+  constexpr int TILE_K = FK::NU * 64 * FK::KS;   // elements per 16-row tile, K = d_k
+  constexpr int TILE_T = FT::NU * 64 * FT::KS;   // elements per 16-row tile, K = 64
+  __shared__ __attribute__((aligned(1024))) char rec0[RS::bytes];
+  __shared__ __attribute__((aligned(1024))) char rec1[RS::nbuf == 2 ? RS::bytes : 1024];
+  __shared__ __attribute__((aligned(16))) E vsl0[WPB * 64 * 16];
+  __shared__ __attribute__((aligned(16))) E vsl1[RS::nbuf == 2 ? WPB * 64 * 16 : 8];
+
   const int w = wave_id(), l = lane_id(), col = l & 15, g = l >> 4;
-  const int v0 = vt * BV;
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int u = (slot / a.wg_per_unit) * 8 + xcd;
+  if (u >= a.n_units) return;
+  const int n = u / a.H, h = u % a.H;
+  const int v0 = ((slot % a.wg_per_unit) * WPB + w) * 16;
   const int H = a.H, DV = a.dv;
 
   long long tstart, ntok, chunk0;
@@ -492,137 +610,147 @@ __global__ __launch_bounds__(kThreads) void chunk_scan_kernel(ScanKArgs a) {
   }
   const int nchunks = (int)((ntok + kChunk - 1) / kChunk);
 
-  // ---- state S^T tiles owned by this wave: channel tile ct = w*CTW + u
-  const size_t sbase = ((size_t)n * H + h) * DV * DK;
-  f32x4 st[CTW][NB];
+  const size_t sbase = ((size_t)n * H + h) * DV * DK + (size_t)(v0 + col) * DK;
+  f32x4 st[CT];
+  if (a.S0) {
 #pragma unroll
-  for (int u = 0; u < CTW; ++u) {
-    const int ct = w * CTW + u;
+    for (int ct = 0; ct < CT; ++ct) st[ct] = *reinterpret_cast<const f32x4 *>(a.S0 + sbase + 16 * ct + 4 * g);
+  } else {
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      st[u][nb] = zero4();
-      if (ct < CT) {
-        const int vv = 16 * nb + col, c4 = 16 * ct + 4 * g;
-        if (a.S0) st[u][nb] = *reinterpret_cast<const f32x4 *>(a.S0 + sbase + (size_t)(v0 + vv) * DK + c4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sS[vv * LDS_ + c4 + r] = from_f<E>(st[u][nb][r]);
-      }
-    }
+    for (int ct = 0; ct < CT; ++ct) st[ct] = zero4();
   }
-  __syncthreads();
 
   const E *V = reinterpret_cast<const E *>(a.v);
   E *O = reinterpret_cast<E *>(a.o);
   const size_t tok_stride = (size_t)H * DV;
+  const size_t vcol = (size_t)h * DV + v0 + col;
 
-  for (int ci = 0; ci < nchunks; ++ci) {
-    const char *rec = a.ws_records + ((size_t)(chunk0 + ci) * H + h) * a.lay.bytes;
+  // this wave's share of chunk ci's record -> LDS (1 KB per instruction).
+  // The copies are issued as inline asm so the compiler does not order the
+  // LDS reads of the other buffer behind them; completion is enforced by the
+  // explicit s_waitcnt + barrier before a buffer is read.
+  auto copy_record = [&](int ci, char *dst) {
+    const char *src = a.ws_records + ((size_t)(chunk0 + ci) * H + h) * RS::bytes + l * 16;
+    const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)dst;
+    for (int q = w; q < RS::bytes / 1024; q += WPB) lds_dma16(src + q * 1024, lds + q * 1024);
+  };
+  // this wave's 64 x 16 slice of V for chunk ci -> LDS, laid out as
+  // [16-byte column group][token][elements]; rows past the end of the sequence
+  // repeat its last token (they are zeroed when used)
+  constexpr int VG = 16 * (int)sizeof(E) / 16;  // 16-byte column groups per row
+  constexpr int VE = 16 / (int)sizeof(E);       // elements per group
+  auto copy_v = [&](int ci, E *dst) {
     const long long t0 = tstart + (long long)kChunk * ci;
     const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
-    const E *Kh = reinterpret_cast<const E *>(rec + a.lay.kh);
-    const E *Qh = reinterpret_cast<const E *>(rec + a.lay.qh);
-    const E *KtT = reinterpret_cast<const E *>(rec + a.lay.ktt);
-    const E *Tb = reinterpret_cast<const E *>(rec + a.lay.tb);
-    const E *Aqk = reinterpret_cast<const E *>(rec + a.lay.aqk);
-    const float *P63 = reinterpret_cast<const float *>(rec + a.lay.p63);
+    const E *src = V + (size_t)(t0 + min(l, L - 1)) * tok_stride + (size_t)h * DV + v0;
+    const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) E *)dst;
+#pragma unroll
+    for (int q = 0; q < VG; ++q) lds_dma16(src + q * VE, lds + q * 64 * 16);
+  };
+  auto compute = [&](int ci, const char *recb, const E *vs) {
+    const long long t0 = tstart + (long long)kChunk * ci;
+    const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
+    const E *Kh = reinterpret_cast<const E *>(recb + RS::kh);
+    const E *Qh = reinterpret_cast<const E *>(recb + RS::qh);
+    const E *KtT = reinterpret_cast<const E *>(recb + RS::ktt);
+    const E *Tb = reinterpret_cast<const E *>(recb + RS::tb);
+    const E *Aq = reinterpret_cast<const E *>(recb + RS::aqk);
+    const float *P63 = reinterpret_cast<const float *>(recb + RS::p63);
 
-    // ---- X = [Kbnd; Qbnd] S^T: wave w takes rows 32w..32w+31 of the stack
-    const E *Xsrc = w < 2 ? Kh + (size_t)(32 * w) * DK : Qh + (size_t)(32 * (w - 2)) * DK;
-    f32x4 x[2][NB];
+    // X_top = Kbnd S^T, X_bot = Qbnd S^T
+    BOps<E, DK> sb;
+    sb.build(st);
+    f32x4 xt[4], xb[4];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        x[rt][nb] = mma_rows<MK, DK>(Xsrc + (size_t)(16 * rt + col) * DK, sS + (16 * nb + col) * LDS_, zero4());
-
-    // ---- Ebar = V - Kbnd S^T  (waves 0, 1), stored transposed
-    if (w < 2) {
-#pragma unroll
-      for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int vv = 16 * nb + col, i0 = 32 * w + 16 * rt + 4 * g;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = i0 + r;
-            const float vval = i < L ? to_f(V[(size_t)(t0 + i) * tok_stride + (size_t)h * DV + v0 + vv]) : 0.f;
-            sEb[vv * LDE + i] = from_f<E>(vval - x[rt][nb][r]);
-          }
-        }
+    for (int I = 0; I < 4; ++I) {
+      xt[I] = sb.template mma<DK>(Kh + I * TILE_K, zero4());
+      xb[I] = sb.template mma<DK>(Qh + I * TILE_K, zero4());
     }
-    __syncthreads();
-
-    // ---- E = Tb Ebar: wave w takes rows 16w..16w+15
-    {
-      f32x4 e[NB];
-      const E *trow = Tb + (size_t)(16 * w + col) * 64;
-      const int kend = 16 * (w + 1);
+    // Ebar = V - X_top ; E = Tb Ebar (row block I needs columns < 16(I+1))
+    f32x4 eb[4];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        e[nb] = zero4();
-        const E *brow = sEb + (16 * nb + col) * LDE;
-        for (int k0 = 0; k0 < kend; k0 += MC::KS)
-          e[nb] = MC::mma(MC::load(trow + k0 + g * MC::KPL), MC::load(brow + k0 + g * MC::KPL), e[nb]);
+    for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sE[(16 * nb + col) * LDE + 16 * w + 4 * g + r] = from_f<E>(e[nb][r]);
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r;
+        const float x = to_f(vs[((col / VE) * 64 + i) * VE + col % VE]);
+        eb[I][r] = (i < L ? x : 0.f) - xt[I][r];
       }
-    }
-    __syncthreads();
-
-    // ---- O = s Qbnd S^T + A E  (waves 2, 3)
-    if (w >= 2) {
+    BOps<E, 64> ebo;
+    ebo.build(eb);
+    f32x4 e[4];
+    e[0] = ebo.template mma<16>(Tb + 0 * TILE_T, zero4());
+    e[1] = ebo.template mma<32>(Tb + 1 * TILE_T, zero4());
+    e[2] = ebo.template mma<48>(Tb + 2 * TILE_T, zero4());
+    e[3] = ebo.template mma<64>(Tb + 3 * TILE_T, zero4());
+    // O = s X_bot + A E
+    BOps<E, 64> eo;
+    eo.build(e);
+    f32x4 ov[4];
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        const int rb = 32 * (w - 2) + 16 * rt;
-        const E *arow = Aqk + (size_t)(rb + col) * 64;
+    for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          f32x4 ov;
+      for (int r = 0; r < 4; ++r) ov[I][r] = a.scale * xb[I][r];
+    ov[0] = eo.template mma<16>(Aq + 0 * TILE_T, ov[0]);
+    ov[1] = eo.template mma<32>(Aq + 1 * TILE_T, ov[1]);
+    ov[2] = eo.template mma<48>(Aq + 2 * TILE_T, ov[2]);
+    ov[3] = eo.template mma<64>(Aq + 3 * TILE_T, ov[3]);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ov[r] = a.scale * x[rt][nb][r];
-          const E *brow = sE + (16 * nb + col) * LDE;
-          for (int k0 = 0; k0 < rb + 16; k0 += MC::KS)
-            ov = MC::mma(MC::load(arow + k0 + g * MC::KPL), MC::load(brow + k0 + g * MC::KPL), ov);
+    for (int I = 0; I < 4; ++I)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = rb + 4 * g + r;
-            if (i < L) O[(size_t)(t0 + i) * tok_stride + (size_t)h * DV + v0 + 16 * nb + col] = from_f<E>(ov[r]);
-          }
-        }
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * I + 4 * g + r;
+        if (i < L) O[(size_t)(t0 + i) * tok_stride + vcol] = from_f<E>(ov[I][r]);
       }
+    // S^T = D_{0:63} S^T + Kend^T E
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const f32x4 p = *reinterpret_cast<const f32x4 *>(P63 + 16 * ct + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[ct][r] *= p[r];
+      st[ct] = eo.template mma<64>(KtT + ct * TILE_T, st[ct]);
     }
+  };
 
-    // ---- S^T = D_{0:63} S^T + Kend^T E
-#pragma unroll
-    for (int u = 0; u < CTW; ++u) {
-      const int ct = w * CTW + u;
-      if (ct < CT) {
-        const f32x4 p = *reinterpret_cast<const f32x4 *>(P63 + 16 * ct + 4 * g);
-        const E *arow = KtT + (size_t)(16 * ct + col) * 64;
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) st[u][nb][r] *= p[r];
-          st[u][nb] = mma_rows<MC, 64>(arow, sE + (16 * nb + col) * LDE, st[u][nb]);
-          const int vv = 16 * nb + col, c4 = 16 * ct + 4 * g;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sS[vv * LDS_ + c4 + r] = from_f<E>(st[u][nb][r]);
-        }
-      }
+  E *vs0 = vsl0 + w * 64 * 16, *vs1 = vsl1 + w * 64 * 16;
+  if (RS::nbuf == 2) {
+    if (nchunks > 0) {
+      copy_record(0, rec0);
+      copy_v(0, vs0);
     }
-    __syncthreads();
+    for (int ci = 0; ci < nchunks; ci += 2) {
+      // chunk ci from buffer 0; prefetch ci+1 into buffer 1
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (ci + 1 < nchunks) {
+        copy_record(ci + 1, rec1);
+        copy_v(ci + 1, vs1);
+      }
+      compute(ci, rec0, vs0);
+      if (ci + 1 >= nchunks) break;
+      // chunk ci+1 from buffer 1; prefetch ci+2 into buffer 0
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (ci + 2 < nchunks) {
+        copy_record(ci + 2, rec0);
+        copy_v(ci + 2, vs0);
+      }
+      compute(ci + 1, rec1, vs1);
+    }
+  } else {
+    for (int ci = 0; ci < nchunks; ++ci) {
+      __syncthreads();  // every wave is done reading the previous record
+      copy_record(ci, rec0);
+      copy_v(ci, vs0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      compute(ci, rec0, vs0);
+    }
   }
 
-  // ---- final state
 #pragma unroll
-  for (int u = 0; u < CTW; ++u) {
-    const int ct = w * CTW + u;
-    if (ct < CT) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)(v0 + 16 * nb + col) * DK + 16 * ct + 4 * g) = st[u][nb];
-    }
-  }
+  for (int ct = 0; ct < CT; ++ct)
+    *reinterpret_cast<f32x4 *>(a.S_final + sbase + 16 * ct + 4 * g) = st[ct];
 }
 
 // ================================================================ dispatch
@@ -680,22 +808,22 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     sa.seq_tok0 = packed ? tables + P.seq_tok0 : nullptr;
     sa.seq_chunk0 = packed ? tables + P.seq_chunk0 : nullptr;
     sa.scale = a.scale;
-    // value-tile width: enough workgroups to cover the chip
-    const long long units = (long long)P.n_seq * a.H;
-    int bv = 16;
-    if (a.dv >= 64 && units * (a.dv / 64) >= 1024) bv = 64;
-    else if (a.dv >= 32 && units * (a.dv / 32) >= 512) bv = 32;
-    if (const char *env = std::getenv("KDA_PREFILL_BV")) {
-      int b = std::atoi(env);
-      if ((b == 16 || b == 32 || b == 64) && b <= a.dv) bv = b;
+    sa.n_units = P.n_seq * a.H;
+    // waves per workgroup: each wave owns 16 value columns of one unit
+    int wpb = a.dv >= 32 ? 2 : 1;
+    if (const char *env = std::getenv("KDA_SCAN_WAVES")) {
+      const int x = std::atoi(env);
+      if ((x == 1 || x == 2 || x == 4) && 16 * x <= a.dv) wpb = x;
     }
-    const dim3 grid(a.dv / bv, a.H, P.n_seq);
-    if (bv == 64)
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, 64, E>), grid, dim3(kThreads), 0, stream, sa);
-    else if (bv == 32)
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, 32, E>), grid, dim3(kThreads), 0, stream, sa);
+    sa.wg_per_unit = a.dv / (16 * wpb);
+    const long long slots = ((long long)sa.n_units + 7) / 8 * 8 * sa.wg_per_unit;
+    const dim3 grid((unsigned)slots);
+    if (wpb == 4)
+      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, 4>), grid, dim3(256), 0, stream, sa);
+    else if (wpb == 2)
+      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, 2>), grid, dim3(128), 0, stream, sa);
     else
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, 16, E>), grid, dim3(kThreads), 0, stream, sa);
+      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, 1>), grid, dim3(64), 0, stream, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
