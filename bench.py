@@ -54,10 +54,11 @@ def bench_prefill(args, torch, kda, inputs):
     B, T, H, dk, dv = w["B"], w["T"], w["H"], w["dk"], w["dv"]
     dev = torch.device("cuda:0")
     sets = []
+    # one workspace, as a caller running layer after layer would hold
+    ws = torch.empty(kda.chunk_fwd_workspace_size(B, T, H, dk, dv, -1, kda.KDA_BF16),
+                     dtype=torch.uint8, device=dev)
     for s in range(NSETS):
         inp = inputs.workload("prefill", seed=s, device=dev)
-        ws = torch.empty(kda.chunk_fwd_workspace_size(B, T, H, dk, dv, -1, kda.KDA_BF16),
-                         dtype=torch.uint8, device=dev)
         o = torch.empty_like(inp["v"])
         S = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
         sets.append((inp, ws, o, S))

@@ -21,8 +21,9 @@
 //     forward substitution (16x16 diagonal blocks inverted on the vector
 //     ALUs, off-diagonal blocks by fp32 MFMA); writes Tb = T Diag(beta) and A
 //     to a per-chunk workspace record.
-//   kernel 2 (scan, one wave per (sequence, head, 16 value columns)): walks
-//     the chunks in order with S^T held in MFMA accumulators (fp32):
+//   kernel 2 (scan, one compute wave per (sequence, head, 16 value columns),
+//     fed by a copy wave that streams chunk records into LDS): walks the
+//     chunks in order with S^T held in MFMA accumulators (fp32):
 //     X = [Kbnd; Qbnd] S^T, Ebar = V - X_top, E = Tb Ebar,
 //     O = s X_bot + A E, S^T = D_{0:63} S^T + Kend^T E.
 //
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrepKArgs a) {
         sKl[row * LD + ch] = from_f<E>(kv[m][i] * ps[m][i]);
         sKd[row * LD + ch] = from_f<E>(kv[m][i] * __builtin_amdgcn_rcpf(pa[m][i]));
         gKh[frag_index<E, DK>(row, ch)] = from_f<E>(kr * fb);                  // k_i D_{0:i}
-        gQh[frag_index<E, DK>(row, ch)] = from_f<E>(qr * fb);                  // q_i D_{0:i}
+        gQh[frag_index<E, DK>(row, ch)] = from_f<E>(qr * fb * a.scale);        // s q_i D_{0:i}
         gKtT[frag_index<E, 64>(ch, row)] = from_f<E>(kv[m][i] * ps[m][i] * gb);  // k_j D_{j+1:63}
       }
     }
@@ -512,18 +513,28 @@ template <int K> struct BOps<bf16, K> {
       }
     }
   }
-  // acc += A(16 rows, k < KU) * B(k < KU); `a` points at the row tile's first
-  // fragment.  KU is rounded up to whole slabs (columns beyond KU are zero).
+  // A fragments of one 16-row tile (k < KU, whole slabs); `a` points at the
+  // tile's first fragment.
+  template <int KU> struct A {
+    frag x[(KU + F::W - 1) / F::W];
+  };
   template <int KU>
-  __device__ __forceinline__ f32x4 mma(const bf16 *a, f32x4 acc) const {
+  __device__ __forceinline__ static A<KU> load(const bf16 *a) {
+    A<KU> r;
     const int l = lane_id();
 #pragma unroll
+    for (int u = 0; u < (KU + F::W - 1) / F::W; ++u) r.x[u] = *reinterpret_cast<const frag *>(a + (u * 64 + l) * F::KS);
+    return r;
+  }
+  // acc += A(16 rows, k < KU) * B(k < KU); columns beyond KU are zero
+  template <int KU>
+  __device__ __forceinline__ f32x4 mma(const A<KU> &a, f32x4 acc) const {
+#pragma unroll
     for (int u = 0; u < (KU + F::W - 1) / F::W; ++u) {
-      const frag x = *reinterpret_cast<const frag *>(a + (u * 64 + l) * F::KS);
       if constexpr (F::wide)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, f[u], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.x[u], f[u], acc, 0, 0, 0);
       else
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(x, f[u], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.x[u], f[u], acc, 0, 0, 0);
     }
     return acc;
   }
@@ -536,15 +547,23 @@ template <int K> struct BOps<float, K> {
 #pragma unroll
     for (int u = 0; u < F::NU; ++u) f[u] = t[u];
   }
+  template <int KU> struct A {
+    f32x4 x[(KU + 15) / 16];
+  };
   template <int KU>
-  __device__ __forceinline__ f32x4 mma(const float *a, f32x4 acc) const {
+  __device__ __forceinline__ static A<KU> load(const float *a) {
+    A<KU> r;
     const int l = lane_id();
 #pragma unroll
-    for (int u = 0; u < (KU + 15) / 16; ++u) {
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(a + (u * 64 + l) * 4);
+    for (int u = 0; u < (KU + 15) / 16; ++u) r.x[u] = *reinterpret_cast<const f32x4 *>(a + (u * 64 + l) * 4);
+    return r;
+  }
+  template <int KU>
+  __device__ __forceinline__ f32x4 mma(const A<KU> &a, f32x4 acc) const {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], f[u][s], acc, 0, 0, 0);
-    }
+    for (int u = 0; u < (KU + 15) / 16; ++u)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[u][s], f[u][s], acc, 0, 0, 0);
     return acc;
   }
 };
@@ -566,37 +585,46 @@ template <int DK, typename E> struct RecordShape {
   static constexpr int kh = 0, qh = 64 * DK * es, ktt = 128 * DK * es, tb = 192 * DK * es;
   static constexpr int aqk = tb + 4096 * es, p63 = aqk + 4096 * es;
   static constexpr int bytes = (p63 + DK * 4 + 1023) / 1024 * 1024;
-  static constexpr int nbuf = 2 * bytes <= 160 * 1024 ? 2 : 1;   // double buffer if it fits
 };
 
-// Scan.  A workgroup of WPB waves serves one unit (sequence, head); each wave
-// owns 16 value columns and keeps S^T (d_k x 16) in fp32 accumulator tiles.
-// The chunk records stream into LDS with global_load_lds (16 bytes per lane,
-// no registers): the copy of chunk c+1 is issued right after the barrier that
-// opens chunk c, so it overlaps chunk c's matrix-core work.  Each product takes
-// its A operand from the LDS record (fragment order: conflict-free 16-byte
-// reads) and its B operand from the wave's own accumulators.  Workgroups of one
-// unit get ids congruent mod 8, which the dispatcher sends to one XCD.
-template <int DK, typename E, int WPB>
-__global__ __launch_bounds__(64 * WPB) void chunk_scan_kernel(ScanKArgs a) {
+// Scan.  A workgroup serves one unit (sequence, head): CW compute waves, each
+// owning 16*NT value columns and keeping S^T (d_k x 16*NT) in fp32
+// accumulator tiles, plus one copy wave that streams the chunk records (and
+// the compute waves' value slices) into a double-buffered LDS image with
+// global_load_lds, so the compute waves never issue memory loads.  While the
+// compute waves work on chunk c, the copy wave fills the other buffer with
+// chunk c+1; one workgroup barrier per chunk hands the buffers over.  Each
+// product takes its A operand from the LDS record (fragment order:
+// conflict-free 16-byte reads, shared by the NT column tiles) and its B
+// operand from the wave's own accumulators.  Workgroups of one unit get ids
+// congruent mod 8, which the dispatcher sends to one XCD.
+template <int DK, typename E, int NT, int CW>
+__global__ __launch_bounds__(64 * (CW + 1)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void chunk_scan_kernel(ScanKArgs a) {
   typedef RecordShape<DK, E> RS;
   constexpr int CT = DK / 16;
+  constexpr int VC = 16 * NT;                   // value columns per compute wave
   typedef FragShape<E, DK> FK;   // products over d_k
   typedef FragShape<E, 64> FT;   // products over the 64 tokens
   constexpr int TILE_K = FK::NU * 64 * FK::KS;   // elements per 16-row tile, K = d_k
   constexpr int TILE_T = FT::NU * 64 * FT::KS;   // elements per 16-row tile, K = 64
+  constexpr int VSL = 64 * VC;                   // value-slice elements per compute wave
+  constexpr int STAGE = RS::bytes + CW * VSL * (int)sizeof(E);
+  constexpr int NBUF = 2 * STAGE <= 160 * 1024 ? 2 : 1;   // double buffer if it fits
+  static_assert(STAGE <= 160 * 1024 - 1024, "one stage must fit in LDS");
   __shared__ __attribute__((aligned(1024))) char rec0[RS::bytes];
-  __shared__ __attribute__((aligned(1024))) char rec1[RS::nbuf == 2 ? RS::bytes : 1024];
-  __shared__ __attribute__((aligned(16))) E vsl0[WPB * 64 * 16];
-  __shared__ __attribute__((aligned(16))) E vsl1[RS::nbuf == 2 ? WPB * 64 * 16 : 8];
+  __shared__ __attribute__((aligned(1024))) char rec1[NBUF == 2 ? RS::bytes : 1024];
+  __shared__ __attribute__((aligned(16))) E vsl0[CW * VSL];
+  __shared__ __attribute__((aligned(16))) E vsl1[NBUF == 2 ? CW * VSL : 8];
 
   const int w = wave_id(), l = lane_id(), col = l & 15, g = l >> 4;
   const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
   const int u = (slot / a.wg_per_unit) * 8 + xcd;
   if (u >= a.n_units) return;
   const int n = u / a.H, h = u % a.H;
-  const int v0 = ((slot % a.wg_per_unit) * WPB + w) * 16;
+  const int vwg = (slot % a.wg_per_unit) * (CW * VC);  // first value column of the workgroup
   const int H = a.H, DV = a.dv;
+  const bool copier = w == CW;
 
   long long tstart, ntok, chunk0;
   if (a.seq_tok0) {
@@ -609,148 +637,241 @@ __global__ __launch_bounds__(64 * WPB) void chunk_scan_kernel(ScanKArgs a) {
     chunk0 = (long long)n * a.nct;
   }
   const int nchunks = (int)((ntok + kChunk - 1) / kChunk);
-
-  const size_t sbase = ((size_t)n * H + h) * DV * DK + (size_t)(v0 + col) * DK;
-  f32x4 st[CT];
-  if (a.S0) {
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) st[ct] = *reinterpret_cast<const f32x4 *>(a.S0 + sbase + 16 * ct + 4 * g);
-  } else {
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) st[ct] = zero4();
-  }
-
   const E *V = reinterpret_cast<const E *>(a.v);
   E *O = reinterpret_cast<E *>(a.o);
   const size_t tok_stride = (size_t)H * DV;
-  const size_t vcol = (size_t)h * DV + v0 + col;
 
-  // this wave's share of chunk ci's record -> LDS (1 KB per instruction).
-  // The copies are issued as inline asm so the compiler does not order the
-  // LDS reads of the other buffer behind them; completion is enforced by the
-  // explicit s_waitcnt + barrier before a buffer is read.
-  auto copy_record = [&](int ci, char *dst) {
+  // ----------------------------------------------------------- copy wave
+  // Value slices land as [compute wave][16-byte column group][token][elements];
+  // rows past the end of the sequence repeat its last token (they never reach
+  // a valid output: their Tb rows and columns are zero).
+  constexpr int VE = 16 / (int)sizeof(E);        // elements per 16-byte group
+  constexpr int VG = VC / VE;                    // 16-byte groups per value row
+  auto copy_chunk = [&](int ci, char *rec, E *vsl) {
     const char *src = a.ws_records + ((size_t)(chunk0 + ci) * H + h) * RS::bytes + l * 16;
-    const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)dst;
-    for (int q = w; q < RS::bytes / 1024; q += WPB) lds_dma16(src + q * 1024, lds + q * 1024);
-  };
-  // this wave's 64 x 16 slice of V for chunk ci -> LDS, laid out as
-  // [16-byte column group][token][elements]; rows past the end of the sequence
-  // repeat its last token (they are zeroed when used)
-  constexpr int VG = 16 * (int)sizeof(E) / 16;  // 16-byte column groups per row
-  constexpr int VE = 16 / (int)sizeof(E);       // elements per group
-  auto copy_v = [&](int ci, E *dst) {
+    const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)rec;
+    for (int q = 0; q < RS::bytes / 1024; ++q) lds_dma16(src + q * 1024, lds + q * 1024);
     const long long t0 = tstart + (long long)kChunk * ci;
     const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
-    const E *src = V + (size_t)(t0 + min(l, L - 1)) * tok_stride + (size_t)h * DV + v0;
-    const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) E *)dst;
+    const E *vsrc = V + (size_t)(t0 + min(l, L - 1)) * tok_stride + (size_t)h * DV + vwg;
+    const uint32_t vl = (uint32_t)(size_t)(__attribute__((address_space(3))) E *)vsl;
 #pragma unroll
-    for (int q = 0; q < VG; ++q) lds_dma16(src + q * VE, lds + q * 64 * 16);
+    for (int cw = 0; cw < CW; ++cw)
+#pragma unroll
+      for (int q = 0; q < VG; ++q)
+        lds_dma16(vsrc + cw * VC + q * VE, vl + (uint32_t)((cw * VSL + q * 64 * VE) * sizeof(E)));
   };
-  auto compute = [&](int ci, const char *recb, const E *vs) {
-    const long long t0 = tstart + (long long)kChunk * ci;
-    const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
+  if (copier) {
+    if (NBUF == 2) {
+      if (nchunks > 0) copy_chunk(0, rec0, vsl0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // chunk 0 ready
+      for (int ci = 0; ci < nchunks; ++ci) {
+        // buffer (ci+1)%2 held chunk ci-1, which every compute wave finished
+        // before the barrier that ended the previous step
+        if (ci + 1 < nchunks) {
+          if (ci & 1) copy_chunk(ci + 1, rec0, vsl0);
+          else copy_chunk(ci + 1, rec1, vsl1);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // chunk ci done by the compute waves, chunk ci+1 ready
+      }
+    } else {
+      for (int ci = 0; ci < nchunks; ++ci) {
+        __syncthreads();  // buffer free
+        copy_chunk(ci, rec0, vsl0);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();  // buffer ready
+      }
+    }
+    return;
+  }
+
+  // -------------------------------------------------------- compute waves
+  const int v0 = vwg + w * VC;
+  const size_t sbase = ((size_t)n * H + h) * DV * DK + (size_t)(v0 + col) * DK;
+  f32x4 st[CT][NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      st[ct][nt] = a.S0 ? *reinterpret_cast<const f32x4 *>(a.S0 + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g)
+                        : zero4();
+
+  // One chunk.  LDS operand reads are issued in the order the products use
+  // them; the scheduler is held to a pattern that keeps reads ahead of the
+  // matrix cores while bounding the registers the fragments take.
+  auto compute = [&](const char *recb, const E *vs, f32x4 (*ov)[NT]) {
+    typedef BOps<E, DK> BK;
+    typedef BOps<E, 64> BT;
     const E *Kh = reinterpret_cast<const E *>(recb + RS::kh);
     const E *Qh = reinterpret_cast<const E *>(recb + RS::qh);
     const E *KtT = reinterpret_cast<const E *>(recb + RS::ktt);
     const E *Tb = reinterpret_cast<const E *>(recb + RS::tb);
     const E *Aq = reinterpret_cast<const E *>(recb + RS::aqk);
     const float *P63 = reinterpret_cast<const float *>(recb + RS::p63);
+    vs += w * VSL;
 
-    // X_top = Kbnd S^T, X_bot = Qbnd S^T
-    BOps<E, DK> sb;
-    sb.build(st);
-    f32x4 xt[4], xb[4];
+    // X_top = Kbnd S^T, X_bot = s Qbnd S^T
+    BK sb[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 col_tiles[CT];
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) col_tiles[ct] = st[ct][nt];
+      sb[nt].build(col_tiles);
+    }
+    f32x4 xt[4][NT], xb[4][NT];
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      xt[I] = sb.template mma<DK>(Kh + I * TILE_K, zero4());
-      xb[I] = sb.template mma<DK>(Qh + I * TILE_K, zero4());
+      const typename BK::template A<DK> fk = BK::template load<DK>(Kh + I * TILE_K);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) xt[I][nt] = sb[nt].mma(fk, zero4());
+      const typename BK::template A<DK> fq = BK::template load<DK>(Qh + I * TILE_K);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) xb[I][nt] = sb[nt].mma(fq, zero4());
     }
     // Ebar = V - X_top ; E = Tb Ebar (row block I needs columns < 16(I+1))
-    f32x4 eb[4];
+    BT ebo[NT];
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 eb[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * g + r;
-        const float x = to_f(vs[((col / VE) * 64 + i) * VE + col % VE]);
-        eb[I][r] = (i < L ? x : 0.f) - xt[I][r];
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * nt + col;
+          eb[I][r] = to_f(vs[((c / VE) * 64 + 16 * I + 4 * g + r) * VE + c % VE]) - xt[I][nt][r];
+        }
+      ebo[nt].build(eb);
+    }
+    f32x4 e[4][NT];
+    {
+      const typename BT::template A<16> f0 = BT::template load<16>(Tb + 0 * TILE_T);
+      const typename BT::template A<32> f1 = BT::template load<32>(Tb + 1 * TILE_T);
+      const typename BT::template A<48> f2 = BT::template load<48>(Tb + 2 * TILE_T);
+      const typename BT::template A<64> f3 = BT::template load<64>(Tb + 3 * TILE_T);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        e[0][nt] = ebo[nt].mma(f0, zero4());
+        e[1][nt] = ebo[nt].mma(f1, zero4());
+        e[2][nt] = ebo[nt].mma(f2, zero4());
+        e[3][nt] = ebo[nt].mma(f3, zero4());
       }
-    BOps<E, 64> ebo;
-    ebo.build(eb);
-    f32x4 e[4];
-    e[0] = ebo.template mma<16>(Tb + 0 * TILE_T, zero4());
-    e[1] = ebo.template mma<32>(Tb + 1 * TILE_T, zero4());
-    e[2] = ebo.template mma<48>(Tb + 2 * TILE_T, zero4());
-    e[3] = ebo.template mma<64>(Tb + 3 * TILE_T, zero4());
-    // O = s X_bot + A E
-    BOps<E, 64> eo;
-    eo.build(e);
-    f32x4 ov[4];
+    }
+    // O = s Qbnd S^T + A E
+    BT eo[NT];
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
+    for (int nt = 0; nt < NT; ++nt) {
+      f32x4 et[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ov[I][r] = a.scale * xb[I][r];
-    ov[0] = eo.template mma<16>(Aq + 0 * TILE_T, ov[0]);
-    ov[1] = eo.template mma<32>(Aq + 1 * TILE_T, ov[1]);
-    ov[2] = eo.template mma<48>(Aq + 2 * TILE_T, ov[2]);
-    ov[3] = eo.template mma<64>(Aq + 3 * TILE_T, ov[3]);
+      for (int I = 0; I < 4; ++I) et[I] = e[I][nt];
+      eo[nt].build(et);
+    }
+    {
+      const typename BT::template A<16> f0 = BT::template load<16>(Aq + 0 * TILE_T);
+      const typename BT::template A<32> f1 = BT::template load<32>(Aq + 1 * TILE_T);
+      const typename BT::template A<48> f2 = BT::template load<48>(Aq + 2 * TILE_T);
+      const typename BT::template A<64> f3 = BT::template load<64>(Aq + 3 * TILE_T);
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * I + 4 * g + r;
-        if (i < L) O[(size_t)(t0 + i) * tok_stride + vcol] = from_f<E>(ov[I][r]);
+      for (int nt = 0; nt < NT; ++nt) {
+        ov[0][nt] = eo[nt].mma(f0, xb[0][nt]);
+        ov[1][nt] = eo[nt].mma(f1, xb[1][nt]);
+        ov[2][nt] = eo[nt].mma(f2, xb[2][nt]);
+        ov[3][nt] = eo[nt].mma(f3, xb[3][nt]);
       }
+    }
     // S^T = D_{0:63} S^T + Kend^T E
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const f32x4 p = *reinterpret_cast<const f32x4 *>(P63 + 16 * ct + 4 * g);
+      const typename BT::template A<64> fkt = BT::template load<64>(KtT + ct * TILE_T);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st[ct][r] *= p[r];
-      st[ct] = eo.template mma<64>(KtT + ct * TILE_T, st[ct]);
+      for (int nt = 0; nt < NT; ++nt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[ct][nt][r] *= p[r];
+        st[ct][nt] = eo[nt].mma(fkt, st[ct][nt]);
+      }
     }
   };
 
-  E *vs0 = vsl0 + w * 64 * 16, *vs1 = vsl1 + w * 64 * 16;
-  if (RS::nbuf == 2) {
-    if (nchunks > 0) {
-      copy_record(0, rec0);
-      copy_v(0, vs0);
+  // outputs of chunk ci, stored after the next barrier so their latency
+  // overlaps the following chunk.  The buffer descriptor covers exactly the
+  // chunk's valid rows, so rows past the end of the sequence are dropped by
+  // the hardware.  The whole offset goes in the VGPR operand: the range check
+  // of a raw buffer access does not include soffset.
+  auto store_o = [&](int ci, f32x4 (*ov)[NT]) {
+    const long long t0 = tstart + (long long)kChunk * ci;
+    const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        O + (size_t)t0 * tok_stride, 0, (int)((size_t)L * tok_stride * sizeof(E)), 0x00020000);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int o_lane = (int)(((size_t)(4 * g) * tok_stride + (size_t)h * DV + v0 + 16 * nt + col) * sizeof(E));
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row_off = (int)((size_t)(16 * I + r) * tok_stride * sizeof(E));
+          // copy the lane value out of the vector first: a bit cast applied to
+          // a vector-element subscript reads element 0 with this compiler
+          const float x = ov[I][nt][r];
+          if constexpr (sizeof(E) == 2)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f<E>(x)), rs,
+                                                  o_lane + row_off, 0, 0);
+          else
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), rs, o_lane + row_off, 0, 0);
+        }
     }
+  };
+
+  f32x4 ov[4][NT];
+  if (NBUF == 2) {
+    __syncthreads();  // chunk 0 ready
     for (int ci = 0; ci < nchunks; ci += 2) {
-      // chunk ci from buffer 0; prefetch ci+1 into buffer 1
-      __builtin_amdgcn_s_waitcnt(0);
+      if (ci > 0) store_o(ci - 1, ov);
+      compute(rec0, vsl0, ov);
       __syncthreads();
-      if (ci + 1 < nchunks) {
-        copy_record(ci + 1, rec1);
-        copy_v(ci + 1, vs1);
-      }
-      compute(ci, rec0, vs0);
       if (ci + 1 >= nchunks) break;
-      // chunk ci+1 from buffer 1; prefetch ci+2 into buffer 0
-      __builtin_amdgcn_s_waitcnt(0);
+      store_o(ci, ov);
+      compute(rec1, vsl1, ov);
       __syncthreads();
-      if (ci + 2 < nchunks) {
-        copy_record(ci + 2, rec0);
-        copy_v(ci + 2, vs0);
-      }
-      compute(ci + 1, rec1, vs1);
     }
   } else {
     for (int ci = 0; ci < nchunks; ++ci) {
-      __syncthreads();  // every wave is done reading the previous record
-      copy_record(ci, rec0);
-      copy_v(ci, vs0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      compute(ci, rec0, vs0);
+      __syncthreads();  // buffer free
+      if (ci > 0) store_o(ci - 1, ov);
+      __syncthreads();  // buffer ready
+      compute(rec0, vsl0, ov);
     }
   }
+  if (nchunks > 0) store_o(nchunks - 1, ov);
 
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct)
-    *reinterpret_cast<f32x4 *>(a.S_final + sbase + 16 * ct + 4 * g) = st[ct];
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
+}
+
+// LDS held by one stage (record + value slices) of a scan configuration.
+template <int DK, typename E> constexpr bool scan_stage_fits(int nt, int cw) {
+  return RecordShape<DK, E>::bytes + cw * 64 * 16 * nt * (int)sizeof(E) <= 160 * 1024 - 1024;
+}
+
+template <int DK, typename E, int NT>
+void launch_scan(int cw, dim3 grid, dim3 block, hipStream_t stream, const ScanKArgs &sa) {
+  if constexpr (scan_stage_fits<DK, E>(NT, 4))
+    if (cw == 4) {
+      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, NT, 4>), grid, block, 0, stream, sa);
+      return;
+    }
+  if constexpr (scan_stage_fits<DK, E>(NT, 2))
+    if (cw == 2) {
+      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, NT, 2>), grid, block, 0, stream, sa);
+      return;
+    }
+  hipLaunchKernelGGL((chunk_scan_kernel<DK, E, NT, 1>), grid, block, 0, stream, sa);
 }
 
 // ================================================================ dispatch
@@ -809,21 +930,28 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     sa.seq_chunk0 = packed ? tables + P.seq_chunk0 : nullptr;
     sa.scale = a.scale;
     sa.n_units = P.n_seq * a.H;
-    // waves per workgroup: each wave owns 16 value columns of one unit
-    int wpb = a.dv >= 32 ? 2 : 1;
-    if (const char *env = std::getenv("KDA_SCAN_WAVES")) {
+    // compute waves per workgroup (CW) and 16-column tiles per wave (NT).
+    // Two tiles per wave halve the LDS reads per column but double each
+    // wave's serial chain of products; one tile and two compute waves per
+    // workgroup measured fastest at d_v = 128.
+    int nt = 1, cw = a.dv >= 32 ? 2 : 1;
+    if (const char *env = std::getenv("KDA_SCAN_NT")) {
       const int x = std::atoi(env);
-      if ((x == 1 || x == 2 || x == 4) && 16 * x <= a.dv) wpb = x;
+      if ((x == 1 || x == 2) && 16 * x <= a.dv) nt = x;
     }
-    sa.wg_per_unit = a.dv / (16 * wpb);
+    if (const char *env = std::getenv("KDA_SCAN_CW")) {
+      const int x = std::atoi(env);
+      if (x == 1 || x == 2 || x == 4) cw = x;
+    }
+    while (cw > 1 && (16 * nt * cw > a.dv || !scan_stage_fits<DK, E>(nt, cw))) cw /= 2;
+    sa.wg_per_unit = a.dv / (16 * nt * cw);
     const long long slots = ((long long)sa.n_units + 7) / 8 * 8 * sa.wg_per_unit;
     const dim3 grid((unsigned)slots);
-    if (wpb == 4)
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, 4>), grid, dim3(256), 0, stream, sa);
-    else if (wpb == 2)
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, 2>), grid, dim3(128), 0, stream, sa);
+    const dim3 block(64 * (cw + 1));
+    if (nt == 2)
+      launch_scan<DK, E, 2>(cw, grid, block, stream, sa);
     else
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, 1>), grid, dim3(64), 0, stream, sa);
+      launch_scan<DK, E, 1>(cw, grid, block, stream, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
