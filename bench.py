@@ -29,6 +29,25 @@ BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 METRIC = "KDA chunked prefill tokens/s at H=16,d=128; decode tok/s; % of roofline"
 NSETS = 4
 
+# HBM traffic per call from two rocprofv3 passes (TCC FETCH_SIZE, then
+# WRITE_SIZE), calibrated against a plain device copy of known size: FETCH_SIZE
+# reads half the bytes moved (x2.0), WRITE_SIZE reads them exactly (x1.0).
+# Each figure belongs to the kernel source with the given sha256 prefix and is
+# reported as null once that source has changed.
+MEASURED_TRAFFIC = {
+    "prefill": ("kda_prefill.hip", "1c6ecb8efd247916", 479_982_592),
+    "decode": ("kda_decode.hip", "4e709b6268b783a8", 1_089_388_544),
+}
+
+
+def measured_traffic(key):
+    import hashlib
+    fname, sha, nbytes = MEASURED_TRAFFIC[key]
+    path = os.path.join(ROOT, "linear_attention_kda_amd", "csrc", fname)
+    with open(path, "rb") as f:
+        cur = hashlib.sha256(f.read()).hexdigest()
+    return nbytes if cur.startswith(sha) else None
+
 
 def prefill_bytes(B, T, H, dk, dv, esize=2, s0=False):
     """Compulsory HBM bytes of one prefill call: q, k, v, o at their dtype,
@@ -121,25 +140,48 @@ def bench_decode(args, torch, kda, inputs):
             "steps": steps, "tokens_per_s": N * steps / (total_ms * 1e-3), "us_per_step": step_us,
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "bytes_per_step": nbytes}}
+                         "traffic": measured_traffic("decode"), "bytes_per_step": nbytes}}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inputs, torch):
-    """The fp64 oracle on the prefill workload (all 64 (sequence, head) units,
-    2048 tokens each), timed on this host's cores."""
+    """The fp64 oracle on the prefill workload, timed on this host's cores:
+    all 64 (sequence, head) units x 2048 tokens with OpenMP over units, and one
+    unit-slice (4 units) on a single thread."""
     import oracle
     inp = inputs.workload("prefill", seed=0, device="cpu")
     args = [oracle._to_f64(inp[n]) for n in ("q", "k", "v", "alpha", "beta")]
     threads = oracle.default_threads()
     orc = oracle.get()
-    t0 = time.perf_counter()
-    orc.fwd(*args, n_threads=threads)
-    dt = time.perf_counter() - t0
     w = inputs.WORKLOADS["prefill"]
     tokens = w["B"] * w["T"]
+    reps, t_all = 3, []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        orc.fwd(*args, n_threads=threads)
+        t_all.append(time.perf_counter() - t0)
+    dt = min(t_all)
+    # single thread on sequence 0, heads 0..3 (4 of 64 units), scaled per unit
+    one = [a[:1, :, :4].copy() for a in args]
+    t0 = time.perf_counter()
+    orc.fwd(*one, n_threads=1)
+    dt1 = (time.perf_counter() - t0) * (w["B"] * w["H"] / 4)
     return {"value": round(tokens / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"whole prefill workload (B=4 x T=2048 tokens, 16 heads, d=128) in fp64; "
-                      f"{dt:.2f} s wall on {threads} threads of {os.cpu_count()} host CPUs"}
+            "sample": f"whole prefill workload (B=4 x T=2048 tokens, 16 heads, d=128) in fp64, "
+                      f"best of {reps}: {dt:.3f} s on {threads} threads ({os.cpu_count()} visible "
+                      f"CPUs, {_cpu_model()}); one thread on 4 of the 64 units, scaled: "
+                      f"{tokens / dt1:.1f} tokens/s",
+            "single_thread_value": round(tokens / dt1, 1)}
 
 
 def main():
@@ -184,7 +226,8 @@ def main():
                                "chunk 64, S0=0", "B": pf["B"], "T": pf["T"], "H": pf["H"],
                    "d_k": pf["dk"], "d_v": pf["dv"], "chunk": 64, "input_sets": NSETS},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("prefill"),
                      "kernel": "kda_chunk_fwd call (chunk_prep_kernel + chunk_scan_kernel)",
                      "algorithmic_bytes": nbytes,
                      "call_us_mean": round(pf["call_ms_mean"] * 1e3, 2),
