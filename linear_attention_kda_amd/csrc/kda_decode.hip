@@ -11,10 +11,13 @@
 //     o_r = scale * S[r,:] . q = scale * (s~ . q + e_r (k . q))
 //
 // The state is HBM-resident fp32 and dominates the traffic (one read and one
-// write per step), so the kernel is laid out for bandwidth: a lane owns 16
-// contiguous channels of one row (four 16-byte loads), LPR = d_k/16 lanes
-// cover a row, and the two dot products are reduced across those lanes with
-// cross-lane swizzles.  One workgroup per (sequence, head).
+// write per step), so the kernel is laid out for bandwidth: every wave-wide
+// state access is one contiguous KiB (lane l takes bytes 16l..16l+15), a lane
+// owns 4 channels of one row, LPR = d_k/4 lanes cover a row, and the two dot
+// products are summed across those lanes with cross-lane swizzles.  State
+// loads and stores carry the nontemporal hint: each state byte is touched
+// once per step, and keeping it out of the caches measured faster.  One
+// workgroup per (sequence, head).
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -30,27 +33,20 @@ struct DecodeKArgs {
 };
 
 template <typename E>
-__device__ __forceinline__ void load16(const E *p, float *out);
+__device__ __forceinline__ void load4(const E *p, float *out);
 
 template <>
-__device__ __forceinline__ void load16<bf16>(const bf16 *p, float *out) {
-  const bf16x8 a = *reinterpret_cast<const bf16x8 *>(p);
-  const bf16x8 b = *reinterpret_cast<const bf16x8 *>(p + 8);
+__device__ __forceinline__ void load4<bf16>(const bf16 *p, float *out) {
+  const bf16x4 a = *reinterpret_cast<const bf16x4 *>(p);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    out[i] = (float)a[i];
-    out[8 + i] = (float)b[i];
-  }
+  for (int i = 0; i < 4; ++i) out[i] = (float)a[i];
 }
 
 template <>
-__device__ __forceinline__ void load16<float>(const float *p, float *out) {
+__device__ __forceinline__ void load4<float>(const float *p, float *out) {
+  const f32x4 x = *reinterpret_cast<const f32x4 *>(p);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const f32x4 x = reinterpret_cast<const f32x4 *>(p)[i];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) out[4 * i + j] = x[j];
-  }
+  for (int i = 0; i < 4; ++i) out[i] = x[i];
 }
 
 template <int LPR>
@@ -62,64 +58,65 @@ __device__ __forceinline__ float group_sum(float x) {
 
 template <int DK, int DV, typename E>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
-  constexpr int LPR = DK / 16;        // lanes per state row
-  constexpr int RPW = 64 / LPR;       // rows per wave per pass
-  constexpr int RPB = 4 * RPW;        // rows per workgroup per pass
-  constexpr int PASSES = (DV + RPB - 1) / RPB;
+  constexpr int LPR = DK / 4;                 // lanes per state row
+  constexpr int RPA = 64 / LPR;               // rows per wave-wide KiB access
+  constexpr int NACC = DV * DK / 256;         // KiB accesses per unit (>= 1)
+  constexpr int NW = kThreads / 64;
+  constexpr int NI = (NACC + NW - 1) / NW;    // accesses per wave
 
-  const size_t u = blockIdx.x;        // (sequence, head) unit
+  const size_t u = blockIdx.x;                // (sequence, head) unit
   const int w = wave_id(), l = lane_id();
-  const int sub = l % LPR, rloc = l / LPR;
-  const int c0 = 16 * sub;
+  const int sub = l % LPR, rsub = l / LPR;
+  const int c0 = 4 * sub;
 
-  float kk[16], qq[16], al[16];
-  load16<E>(reinterpret_cast<const E *>(a.k) + u * DK + c0, kk);
-  load16<E>(reinterpret_cast<const E *>(a.q) + u * DK + c0, qq);
-  load16<float>(a.alpha + u * DK + c0, al);
-  float kq = 0.f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) kq += kk[i] * qq[i];
-  kq = group_sum<LPR>(kq);
+  float kk[4], qq[4], al[4];
+  load4<E>(reinterpret_cast<const E *>(a.k) + u * DK + c0, kk);
+  load4<E>(reinterpret_cast<const E *>(a.q) + u * DK + c0, qq);
+  load4<float>(a.alpha + u * DK + c0, al);
   const float beta = a.beta[u];
   const E *vrow = reinterpret_cast<const E *>(a.v) + u * DV;
   E *orow = reinterpret_cast<E *>(a.o) + u * DV;
   float *S = a.S + u * DV * DK;
 
-  f32x4 s[PASSES][4];
-  // issue every load of this lane's rows first
+  // issue every state load of this lane first (accesses past the unit only
+  // exist when the unit is smaller than one KiB per wave; they are skipped)
+  f32x4 s[NI];
+  float vv[NI];
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int r = p * RPB + w * RPW + rloc;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      s[p][i] = r < DV ? reinterpret_cast<const f32x4 *>(S + (size_t)r * DK + c0)[i] : zero4();
+  for (int i = 0; i < NI; ++i) {
+    const int acc = w * NI + i;
+    const int r = acc * RPA + rsub;
+    if (acc < NACC) {
+      s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)r * DK + c0));
+      vv[i] = (float)vrow[r];
+    } else {
+      s[i] = zero4();
+      vv[i] = 0.f;
+    }
   }
+  float kq = 0.f;
 #pragma unroll
-  for (int p = 0; p < PASSES; ++p) {
-    const int r = p * RPB + w * RPW + rloc;
-    // rows past DV only occur for tiny d_v with wide rows; their lanes idle
-    float st[16];
+  for (int j = 0; j < 4; ++j) kq += kk[j] * qq[j];
+  kq = group_sum<LPR>(kq);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < NI; ++i) {
+    const int acc = w * NI + i;
+    const int r = acc * RPA + rsub;
+    float st[4], d1 = 0.f, d2 = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) st[4 * i + j] = s[p][i][j] * al[4 * i + j];
-    float d1 = 0.f, d2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      d1 += st[i] * kk[i];
-      d2 += st[i] * qq[i];
+    for (int j = 0; j < 4; ++j) {
+      st[j] = s[i][j] * al[j];
+      d1 += st[j] * kk[j];
+      d2 += st[j] * qq[j];
     }
     d1 = group_sum<LPR>(d1);
     d2 = group_sum<LPR>(d2);
-    if (r < DV) {
-      const float e = beta * ((float)vrow[r] - d1);
-      f32x4 outv[4];
+    if (acc < NACC) {
+      const float e = beta * (vv[i] - d1);
+      f32x4 outv;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) outv[i][j] = st[4 * i + j] + e * kk[4 * i + j];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) reinterpret_cast<f32x4 *>(S + (size_t)r * DK + c0)[i] = outv[i];
+      for (int j = 0; j < 4; ++j) outv[j] = st[j] + e * kk[j];
+      __builtin_nontemporal_store(outv, reinterpret_cast<f32x4 *>(S + (size_t)r * DK + c0));
       if (sub == 0) orow[r] = (E)(a.scale * (d2 + e * kq));
     }
   }
