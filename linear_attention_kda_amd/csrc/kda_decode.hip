@@ -56,15 +56,26 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Work split: a unit's state is NACC wave-wide KiB accesses.  A workgroup of
+// four waves takes APW = min(NACC, 8) of them (two per wave), so a d = 128
+// unit spreads over 8 workgroups; fewer accesses in flight per wave and more
+// workgroups measured closer to the copy bandwidth of the part.
+template <int DK, int DV> struct DecodeShape {
+  static constexpr int NACC = DV * DK / 256;
+  static constexpr int APW = NACC < 8 ? NACC : 8;
+  static constexpr int SPLIT = NACC / APW;        // workgroups per unit
+  static constexpr int NI = (APW + 3) / 4;        // accesses per wave
+};
+
 template <int DK, int DV, typename E>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
+  typedef DecodeShape<DK, DV> SH;
   constexpr int LPR = DK / 4;                 // lanes per state row
   constexpr int RPA = 64 / LPR;               // rows per wave-wide KiB access
-  constexpr int NACC = DV * DK / 256;         // KiB accesses per unit (>= 1)
-  constexpr int NW = kThreads / 64;
-  constexpr int NI = (NACC + NW - 1) / NW;    // accesses per wave
+  constexpr int NI = SH::NI;                  // accesses per wave
 
-  const size_t u = blockIdx.x;                // (sequence, head) unit
+  const size_t u = blockIdx.x / SH::SPLIT;    // (sequence, head) unit
+  const int part = blockIdx.x % SH::SPLIT;    // which APW KiB of the unit
   const int w = wave_id(), l = lane_id();
   const int sub = l % LPR, rsub = l / LPR;
   const int c0 = 4 * sub;
@@ -78,15 +89,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   E *orow = reinterpret_cast<E *>(a.o) + u * DV;
   float *S = a.S + u * DV * DK;
 
-  // issue every state load of this lane first (accesses past the unit only
-  // exist when the unit is smaller than one KiB per wave; they are skipped)
+  // issue every state load of this lane first (waves past the workgroup's
+  // share only exist when a unit is smaller than four KiB; they skip)
   f32x4 s[NI];
   float vv[NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int acc = w * NI + i;
+    const int acc = part * SH::APW + w * NI + i;
     const int r = acc * RPA + rsub;
-    if (acc < NACC) {
+    if (w * NI + i < SH::APW) {
       s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)r * DK + c0));
       vv[i] = (float)vrow[r];
     } else {
@@ -100,7 +111,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   kq = group_sum<LPR>(kq);
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int acc = w * NI + i;
+    const int acc = part * SH::APW + w * NI + i;
     const int r = acc * RPA + rsub;
     float st[4], d1 = 0.f, d2 = 0.f;
 #pragma unroll
@@ -111,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     }
     d1 = group_sum<LPR>(d1);
     d2 = group_sum<LPR>(d2);
-    if (acc < NACC) {
+    if (w * NI + i < SH::APW) {
       const float e = beta * (vv[i] - d1);
       f32x4 outv;
 #pragma unroll
@@ -124,14 +135,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 
 template <int DK, typename E>
 hipError_t run_decode_dv(const DecodeArgs &a, const DecodeKArgs &ka, hipStream_t s) {
-  const dim3 grid((unsigned)((size_t)a.N * a.H));
+  const size_t units = (size_t)a.N * a.H;
+  if (units * DecodeShape<DK, 128>::SPLIT > 0x7fffffffull) return hipErrorInvalidConfiguration;
+#define KDA_DECODE_LAUNCH(DV) \
+  hipLaunchKernelGGL((decode_kernel<DK, DV, E>), dim3((unsigned)(units * DecodeShape<DK, DV>::SPLIT)), \
+                     dim3(kThreads), 0, s, ka)
   switch (a.dv) {
-    case 16: hipLaunchKernelGGL((decode_kernel<DK, 16, E>), grid, dim3(kThreads), 0, s, ka); break;
-    case 32: hipLaunchKernelGGL((decode_kernel<DK, 32, E>), grid, dim3(kThreads), 0, s, ka); break;
-    case 64: hipLaunchKernelGGL((decode_kernel<DK, 64, E>), grid, dim3(kThreads), 0, s, ka); break;
-    case 128: hipLaunchKernelGGL((decode_kernel<DK, 128, E>), grid, dim3(kThreads), 0, s, ka); break;
+    case 16: KDA_DECODE_LAUNCH(16); break;
+    case 32: KDA_DECODE_LAUNCH(32); break;
+    case 64: KDA_DECODE_LAUNCH(64); break;
+    case 128: KDA_DECODE_LAUNCH(128); break;
     default: return hipErrorInvalidValue;
   }
+#undef KDA_DECODE_LAUNCH
   return hipGetLastError();
 }
 
