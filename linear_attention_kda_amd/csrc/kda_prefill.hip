@@ -157,15 +157,6 @@ __device__ __forceinline__ int frag_index(int i, int c) {
   return (((i >> 4) * F::NU + c / F::W) * 64 + (i & 15) + 16 * g) * F::KS + pos;
 }
 
-// Copy a 64 x 64 tile from padded LDS rows (stride ld) to fragment order.
-template <typename E>
-__device__ __forceinline__ void lds_to_global_frag64(E *dst, const E *src, int ld) {
-  for (int idx = threadIdx.x; idx < 64 * 64; idx += kThreads) {
-    const int i = idx >> 6, c = idx & 63;
-    dst[frag_index<E, 64>(i, c)] = src[i * ld + c];
-  }
-}
-
 // ======================================================= kernel 1: chunk prep
 struct PrepKArgs {
   const void *q, *k;
@@ -177,15 +168,139 @@ struct PrepKArgs {
   ChunkRecordLayout lay;
 };
 
-template <int DK, typename E> struct PrepSmem {
-  static constexpr int PAD = sizeof(E) == 2 ? 8 : 4;
-  static constexpr int LD = DK + PAD;    // rows of the 64 x d_k operand tiles
-  static constexpr int LDT = 64 + PAD;   // rows of 64-wide E tiles
-  static constexpr int LDR = 68;         // rows of fp32 64x64 tiles
-  static constexpr size_t a_bytes = (size_t)4 * 64 * LD * sizeof(E);
-  static constexpr size_t b_bytes = (size_t)2 * 64 * LDR * sizeof(float) + (size_t)64 * LDT * sizeof(E);
-  static constexpr size_t bytes = a_bytes > b_bytes ? a_bytes : b_bytes;
+// LDS image of a fragment-ordered operand (FragShape<E, K>, ROWS rows), slot
+// by slot in record order.  Within each 16-row group the rows are XOR-swizzled
+// by (g + 4 (slab & 1)) & 7, so that both a wave writing four channels of one
+// row per lane and a wave reading one 16-byte slot per lane spread over all
+// LDS banks.
+template <typename E, int K, int ROWS> struct LdsFrag {
+  typedef FragShape<E, K> F;
+  static constexpr int SLOT = F::KS * (int)sizeof(E);  // bytes per lane slot (16 or 8)
+  static constexpr int NSLOT = ROWS / 16 * F::NU * 64;
+  static constexpr int BYTES = NSLOT * SLOT;
+  __device__ __forceinline__ static int slot_off(int tile, int slab, int row16, int g) {
+    const int sw = (g + 4 * (slab & 1)) & 7;
+    return (((tile * F::NU + slab) * 4 + g) * 16 + (row16 ^ sw)) * SLOT;
+  }
+  // byte offset of element (row, col); col % 4 == 0 starts 4 contiguous elements
+  __device__ __forceinline__ static int elem_off(int row, int col) {
+    const int ci = col % F::W;
+    int g, pos;
+    if constexpr (F::wide) {
+      g = (ci & 15) >> 2;
+      pos = (ci >> 4) * 4 + (ci & 3);
+    } else {
+      g = ci >> 2;
+      pos = ci & 3;
+    }
+    return slot_off(row >> 4, col / F::W, row & 15, g) + pos * (int)sizeof(E);
+  }
+  // LDS byte offset of record slot s = (tile NU + slab) 64 + row16 + 16 g
+  __device__ __forceinline__ static int rec_slot(int s) {
+    const int ts = s >> 6, L = s & 63;
+    return slot_off(ts / F::NU, ts % F::NU, L & 15, L >> 4);
+  }
 };
+
+template <int BYTES> struct VecOf;
+template <> struct VecOf<16> { typedef f32x4 type; };
+template <> struct VecOf<8> { typedef __attribute__((__vector_size__(8))) float type; };
+
+// LDS image -> record (global), one slot per thread per step, coalesced.
+template <typename LF>
+__device__ __forceinline__ void copy_out(char *dst, const char *lds) {
+  typedef typename VecOf<LF::SLOT>::type V;
+  for (int s = threadIdx.x; s < LF::NSLOT; s += kThreads)
+    *reinterpret_cast<V *>(dst + (size_t)s * LF::SLOT) = *reinterpret_cast<const V *>(lds + LF::rec_slot(s));
+}
+
+// Column of element e (0 .. KS-1) of the slot (slab, g) of FragShape<E, K>;
+// the inverse of the position rule in frag_index.
+template <typename E, int K>
+__device__ __forceinline__ int slot_col(int slab, int g, int e) {
+  typedef FragShape<E, K> F;
+  if constexpr (F::wide) return slab * F::W + (e >> 2) * 16 + 4 * g + (e & 3);
+  else return slab * F::W + 4 * g + e;
+}
+
+// One record slot (KS elements of E) packed from fp32.
+template <typename E, int KS> struct SlotVec;
+template <> struct SlotVec<bf16, 8> {
+  typedef bf16x8 type;
+  __device__ __forceinline__ static type pack(const float *x) {
+    type v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
+    return v;
+  }
+};
+template <> struct SlotVec<float, 4> {
+  typedef f32x4 type;
+  __device__ __forceinline__ static type pack(const float *x) { return f32x4{x[0], x[1], x[2], x[3]}; }
+};
+
+// A 64 x 64 fp32 tile in LDS (row stride LDR), masked to j <= i and scaled per
+// column by colscale (or not), to the record in fragment order, slot by slot.
+template <typename E, int LDR>
+__device__ __forceinline__ void tile64_out(E *dst, const float *src, const float *colscale) {
+  typedef FragShape<E, 64> F;
+  typedef SlotVec<E, F::KS> SV;
+  for (int s = threadIdx.x; s < 4 * F::NU * 64; s += kThreads) {
+    const int ts = s >> 6, L = s & 63;
+    const int i = 16 * (ts / F::NU) + (L & 15), slab = ts % F::NU, g = L >> 4;
+    float x[F::KS];
+#pragma unroll
+    for (int e = 0; e < F::KS; ++e) {
+      const int j = slot_col<E, 64>(slab, g, e);
+      x[e] = j <= i ? src[i * LDR + j] * (colscale ? colscale[j] : 1.f) : 0.f;
+    }
+    *reinterpret_cast<typename SV::type *>(dst + (size_t)s * F::KS) = SV::pack(x);
+  }
+}
+
+// Four elements of E from / to fp32.
+template <typename E> struct Four;
+template <> struct Four<bf16> {
+  typedef bf16x4 vec;
+  __device__ __forceinline__ static void load(const bf16 *p, float *x) {
+    const bf16x4 v = *reinterpret_cast<const bf16x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = (float)v[j];
+  }
+  __device__ __forceinline__ static vec pack(const float *x) {
+    vec v;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (bf16)x[j];
+    return v;
+  }
+};
+template <> struct Four<float> {
+  typedef f32x4 vec;
+  __device__ __forceinline__ static void load(const float *p, float *x) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = v[j];
+  }
+  __device__ __forceinline__ static vec pack(const float *x) { return f32x4{x[0], x[1], x[2], x[3]}; }
+};
+
+// acc += A_slot * B_slot over one slab (slots read from LDS at byte offsets).
+template <typename E, int K>
+__device__ __forceinline__ f32x4 slot_mma(const char *pa, const char *pb, f32x4 acc) {
+  typedef FragShape<E, K> F;
+  if constexpr (sizeof(E) == 4) {
+    const f32x4 x = *reinterpret_cast<const f32x4 *>(pa), y = *reinterpret_cast<const f32x4 *>(pb);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(x[s], y[s], acc, 0, 0, 0);
+  } else if constexpr (F::wide) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8 *>(pa),
+                                                  *reinterpret_cast<const bf16x8 *>(pb), acc, 0, 0, 0);
+  } else {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(*reinterpret_cast<const bf16x4 *>(pa),
+                                                    *reinterpret_cast<const bf16x4 *>(pb), acc, 0, 0, 0);
+  }
+  return acc;
+}
 
 // Off-diagonal block (I, J), I > J, of T = (I + R)^{-1}:
 //   T_IJ = -T_II * sum_{K=J}^{I-1} R_IK T_KJ      (16x16 fp32 blocks, one wave)
@@ -209,61 +324,43 @@ __device__ __forceinline__ void inverse_offdiag_block(int I, int J, const float 
   for (int r = 0; r < 4; ++r) sT[(16 * I + 4 * g + r) * LDR + 16 * J + col] = -t[r];
 }
 
-// One 16x16 tile of A^kk or A^qk over d_k on the matrix cores, with the B rows
-// optionally scaled per key channel by f (fp32, LDS) on the way in.
-template <typename M, int K, typename E>
-__device__ __forceinline__ f32x4 mma_rows_scaled(const E *a_row, const E *bt_row, const float *f, f32x4 acc) {
-  const int g = lane_id() >> 4;
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += M::KS) {
-    typename M::frag b = M::load(bt_row + k0 + g * M::KPL);
-    if (f) {
-#pragma unroll
-      for (int e = 0; e < M::KPL; ++e) {
-        if constexpr (M::KPL == 1) b = b * f[k0 + g];
-        else b[e] = (E)((float)b[e] * f[k0 + g * M::KPL + e]);
-      }
-    }
-    acc = M::mma(M::load(a_row + k0 + g * M::KPL), b, acc);
-  }
-  return acc;
+// pair p in 0..9 -> (I, J) of the lower block triangle, row-major
+__device__ __forceinline__ void tile_ij(int p, int &I, int &J) {
+  I = p >= 6 ? 3 : (p >= 3 ? 2 : (p >= 1 ? 1 : 0));
+  J = p - I * (I + 1) / 2;
 }
 
-// tile t in 0..9 -> (I, J) of the lower block triangle, row-major
-__device__ __forceinline__ void tile_ij(int t, int &I, int &J) {
-  I = t >= 6 ? 3 : (t >= 3 ? 2 : (t >= 1 ? 1 : 0));
-  J = t - I * (I + 1) / 2;
-}
-
-// Chunk prep.  The chunk is cut into four blocks of 16 tokens.  Per key
-// channel: a_i = in-block inclusive prefix product of the gates, s_j = in-block
-// exclusive suffix product, tau_b = whole-block product.  Then for j <= i
-//   D_{j+1:i} = a_i / a_j                                    (same block)
-//   D_{j+1:i} = s_j * prod_{J<b<I} tau_b * a_i               (block J < block I)
-// The second form has no division and no factor above 1, so off-diagonal
-// blocks are safe for any gates.  The first form is used on a diagonal block
-// while its tau >= 2^-100 on every channel; otherwise that block is formed
-// exactly with running products.
+// Chunk prep: one workgroup per (chunk, head); wave b owns the 16-token block
+// b, lane (cg, th) owns channels 4cg..4cg+3 for TPL consecutive tokens.
+//
+// Fast path.  With a_i = D_{0:i} (per channel, products of the gates from the
+// chunk start to token i inclusive) every decay between tokens of the chunk
+// factors as D_{j+1:i} = a_i / a_j, so
+//   R^T = (k / a) (k a)^T,  A^T = (k / a) (s q a)^T   (then masked, R scaled by beta_i)
+//   Kbnd = k a,  s Qbnd = s q a,  Kend_j = k_j D_{j+1:63} = (k_j / a_j) D_{0:63}
+// are plain products on the matrix cores.  Every a_j >= D_{0:63}, so while
+// D_{0:63} >= 2^-100 on every channel no factor exceeds 2^100 and nothing
+// over- or underflows in fp32 or bf16.
+// Exact path (a chunk with some D_{0:63} below 2^-100, e.g. a gate of 0):
+// no division at all.  Kbnd and Qbnd as above, Kend from suffix products, and
+// R and A summed channel by channel with running products of the gates.
 template <int DK, typename E>
-__global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrepKArgs a) {
-  typedef PrepSmem<DK, E> SM;
-  constexpr int LD = SM::LD, LDT = SM::LDT, LDR = SM::LDR;
-  typedef typename MmaFor<E, DK>::type M;
-  constexpr int NTASK = 4 * DK;                               // (channel, block) pairs
-  constexpr int TPT = (NTASK + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) char smem[SM::bytes];
-  __shared__ __attribute__((aligned(16))) float sTau[4 * DK];  // tau_b per channel
-  __shared__ __attribute__((aligned(16))) float sF[3 * DK];    // tau_1, tau_2, tau_1*tau_2
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrepKArgs a) {
+  typedef LdsFrag<E, DK, 64> LK;   // Kbnd, Qbnd, k / a: rows = tokens, K = d_k
+  typedef LdsFrag<E, 64, DK> LT;   // Kend^T: rows = channels, K = tokens
+  typedef Four<E> F4;
+  constexpr int CG = DK / 4;       // channel groups of four per token
+  constexpr int TH = 64 / CG;      // lanes per channel group (token sub-ranges of a block)
+  constexpr int TPL = 16 / TH;     // tokens per lane
+  constexpr int LDR = 68;          // row stride of the fp32 64x64 tiles
+  constexpr int RT_BYTES = 64 * LDR * 4;
+  constexpr int SA_BYTES = LT::BYTES > RT_BYTES ? LT::BYTES : RT_BYTES;
+  constexpr int P1 = 3 * LK::BYTES;                 // Kbnd | Qbnd | k / a
+  constexpr int P2 = 2 * RT_BYTES + SA_BYTES;       // R | T | Kend^T staging or A (exact)
+  constexpr int ARENA = P1 > P2 ? P1 : P2;
+  static_assert(ARENA >= 4 * DK * 4, "the gate totals live at the start of the arena");
+  __shared__ __attribute__((aligned(16))) char arena[ARENA];
   __shared__ float sBeta[kChunk];
-  __shared__ int sFlag[4];
-
-  E *sKr = reinterpret_cast<E *>(smem);   // k_i a_i           (left operand)
-  E *sQr = sKr + 64 * LD;                 // q_i a_i           (left operand)
-  E *sKl = sQr + 64 * LD;                 // k_j s_j           (right, off-diagonal)
-  E *sKd = sKl + 64 * LD;                 // k_j / a_j         (right, diagonal)
-  float *sR = reinterpret_cast<float *>(smem);
-  float *sT = sR + 64 * LDR;
-  E *sOut = reinterpret_cast<E *>(sT + 64 * LDR);
 
   const int h = blockIdx.y;
   const long long c = blockIdx.x;
@@ -273,175 +370,317 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrepKArgs a) {
 
   char *rec = a.ws_records + ((size_t)c * a.H + h) * a.lay.bytes;
   const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+  const int cg = l % CG, th = l / CG, c0 = 4 * cg;
   const E *q = reinterpret_cast<const E *>(a.q);
   const E *k = reinterpret_cast<const E *>(a.k);
   const size_t hs = (size_t)a.H * DK;  // token stride of q, k, alpha
-  const size_t base = (size_t)t0 * hs + (size_t)h * DK;
-  E *gKh = reinterpret_cast<E *>(rec + a.lay.kh);
-  E *gQh = reinterpret_cast<E *>(rec + a.lay.qh);
-  E *gKtT = reinterpret_cast<E *>(rec + a.lay.ktt);
+  const size_t base = (size_t)t0 * hs + (size_t)h * DK + c0;
+  char *sKh = arena, *sQh = arena + LK::BYTES, *sKd = arena + 2 * LK::BYTES;
+  float *sR = reinterpret_cast<float *>(arena);
+  float *sT = reinterpret_cast<float *>(arena + RT_BYTES);
+  char *sX = arena + 2 * RT_BYTES;     // Kend^T staging (fast) or A in fp32 (exact)
+  // whole-block gate products; read before the barrier that precedes the
+  // first write of the operand images, which reuse this space
+  float *sTau = reinterpret_cast<float *>(arena);
 
   if (tid < kChunk) sBeta[tid] = tid < L ? a.beta[(size_t)(t0 + tid) * a.H + h] : 0.f;
-  if (tid < 4) sFlag[tid] = 0;
 
-  // ---- per (channel, block): load, in-block prefix / suffix products.
-  // Padded tokens (index >= L) have q = k = 0 and alpha = 1.
-  float kv[TPT][16], qv[TPT][16], pa[TPT][16], ps[TPT][16];
+  // ---- loads and in-block prefix products.  Padded tokens (index >= L)
+  // take q = k = 0 and alpha = 1; their loads read a valid token instead.
+  const int tb0 = 16 * w + TPL * th;   // first token of this lane
+  // q and k stay packed in their own type until used (register budget)
+  typename F4::vec kraw[TPL], qraw[TPL];
+  float pa[TPL][4];
 #pragma unroll
-  for (int m = 0; m < TPT; ++m) {
-    const int p = tid + kThreads * m;
-    if (p < NTASK) {
-      const int ch = p % DK, b = p / DK;
-      float av[16];
+  for (int u = 0; u < TPL; ++u) {
+    const int tok = tb0 + u;
+    const bool live = tok < L;
+    const size_t off = base + (size_t)min(tok, L - 1) * hs;
+    float al[4];
+    Four<float>::load(a.alpha + off, al);
+    kraw[u] = *reinterpret_cast<const typename F4::vec *>(k + off);
+    qraw[u] = *reinterpret_cast<const typename F4::vec *>(q + off);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        // branch-free: load a valid token, then substitute the padding values
-        const int tok = 16 * b + i;
-        const bool live = tok < L;
-        const size_t off = base + (size_t)min(tok, L - 1) * hs + ch;
-        const float al = a.alpha[off], kx = to_f(k[off]), qx = to_f(q[off]);
-        av[i] = live ? al : 1.f;
-        kv[m][i] = live ? kx : 0.f;
-        qv[m][i] = live ? qx : 0.f;
-      }
-      float run = 1.f;
+    for (int j = 0; j < 4; ++j) pa[u][j] = live ? al[j] : 1.f;
+  }
+  // k (or q) of token u, channel j, zero for padded tokens
+  auto kval = [&](int u, int j) {
+    const float x = (float)kraw[u][j];
+    return tb0 + u < L ? x : 0.f;
+  };
+  auto qval = [&](int u, int j) {
+    const float x = (float)qraw[u][j];
+    return tb0 + u < L ? x : 0.f;
+  };
+  float tot[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        run *= av[i];
-        pa[m][i] = run;
-      }
-      run = 1.f;
+  for (int j = 0; j < 4; ++j) {
+    float run = 1.f;
 #pragma unroll
-      for (int j = 15; j >= 0; --j) {
-        ps[m][j] = run;
-        run *= av[j];
-      }
+    for (int u = 0; u < TPL; ++u) {
+      run *= pa[u][j];
+      pa[u][j] = run;
+    }
+    tot[j] = run;
+  }
+  // exclusive product over the lanes of earlier sub-ranges of the block
+  // (lanes cg + CG th' for th' < th); Hillis-Steele scan with stride CG
+  float incl[4], excl[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) incl[j] = tot[j];
+#pragma unroll
+  for (int d = 1; d < TH; d <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float y = __shfl(incl[j], l - d * CG);
+      if (th >= d) incl[j] *= y;
     }
   }
-  __syncthreads();  // sFlag initialised
 #pragma unroll
-  for (int m = 0; m < TPT; ++m) {
-    const int p = tid + kThreads * m;
-    if (p < NTASK) {
-      const int ch = p % DK, b = p / DK;
-      const float tau = pa[m][15];
-      sTau[b * DK + ch] = tau;
-      if (!(tau >= 0x1p-100f)) sFlag[b] = 1;
+  for (int j = 0; j < 4; ++j) {
+    const float y = __shfl(incl[j], l - CG);
+    excl[j] = th >= 1 ? y : 1.f;
+  }
+#pragma unroll
+  for (int u = 0; u < TPL; ++u)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) pa[u][j] *= excl[j];
+  if (th == TH - 1) *reinterpret_cast<f32x4 *>(sTau + w * DK + c0) = f32x4{incl[0], incl[1], incl[2], incl[3]};
+  __syncthreads();
+
+  // ---- chunk prefix a = (blocks before) * (in-block prefix); D_{0:63}
+  float fb[4], gb[4], p63[4];
+  {
+    f32x4 tau[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) tau[b] = *reinterpret_cast<const f32x4 *>(sTau + b * DK + c0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float before = 1.f, after = 1.f;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b < w) before *= tau[b][j];
+        if (b > w) after *= tau[b][j];
+      }
+      fb[j] = before;
+      gb[j] = after;
+      p63[j] = tau[0][j] * tau[1][j] * tau[2][j] * tau[3][j];
+    }
+  }
+  int weak = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) weak |= !(p63[j] >= 0x1p-100f);
+  const bool exact = __syncthreads_or(weak) != 0;   // uniform over the workgroup
+
+  // ---- Kbnd, s Qbnd (both paths) and k / a (fast path) into LDS
+  typename F4::vec ktt[TPL];   // Kend rows of this lane's tokens, packed (written later)
+#pragma unroll
+  for (int u = 0; u < TPL; ++u) {
+    const int tok = tb0 + u;
+    float kh[4], qh[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float av = pa[u][j] * fb[j];
+      kh[j] = kval(u, j) * av;
+      qh[j] = qval(u, j) * av * a.scale;
+      pa[u][j] = av;
+    }
+    *reinterpret_cast<typename F4::vec *>(sKh + LK::elem_off(tok, c0)) = F4::pack(kh);
+    *reinterpret_cast<typename F4::vec *>(sQh + LK::elem_off(tok, c0)) = F4::pack(qh);
+  }
+  if (!exact) {
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      const int tok = tb0 + u;
+      float kd[4], kt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kd[j] = kval(u, j) * __builtin_amdgcn_rcpf(pa[u][j]);
+        kt[j] = kd[j] * p63[j];
+      }
+      *reinterpret_cast<typename F4::vec *>(sKd + LK::elem_off(tok, c0)) = F4::pack(kd);
+      ktt[u] = F4::pack(kt);
+    }
+  } else {
+    // D_{j+1:63} without division: in-lane exclusive suffix, times the later
+    // sub-ranges of the block, times the later blocks.  The gates are read
+    // again (this path is rare).
+    float sfx[TPL][4], run[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) run[j] = 1.f;
+#pragma unroll
+    for (int u = TPL - 1; u >= 0; --u) {
+      const int tok = tb0 + u;
+      float al[4];
+      Four<float>::load(a.alpha + base + (size_t)min(tok, L - 1) * hs, al);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sfx[u][j] = run[j];
+        run[j] *= tok < L ? al[j] : 1.f;
+      }
+    }
+    float later[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) later[j] = 1.f;
+    for (int d = 1; d < TH; ++d) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y = __shfl(run[j], l + d * CG);
+        if (th + d < TH) later[j] *= y;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      float kt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kt[j] = kval(u, j) * sfx[u][j] * later[j] * gb[j];
+      ktt[u] = F4::pack(kt);
     }
   }
   __syncthreads();
 
-  // ---- operands: LDS tiles for A^kk / A^qk, record tiles for the scan
+  // ---- fast path: R^T and A^T tiles on the matrix cores.  Pair (I, J),
+  // I >= J: D[j][i] over j in block J (rows), i in block I (columns).
+  constexpr int NP = 3;  // pairs per wave: w, w + 4, w + 8 (< 10)
+  f32x4 rt[NP], at[NP];
+  if (!exact) {
 #pragma unroll
-  for (int m = 0; m < TPT; ++m) {
-    const int p = tid + kThreads * m;
-    if (p < NTASK) {
-      const int ch = p % DK, b = p / DK;
-      const float t0_ = sTau[ch], t1_ = sTau[DK + ch], t2_ = sTau[2 * DK + ch], t3_ = sTau[3 * DK + ch];
-      // D_{0:16b-1} (blocks before b) and D_{16b+16:63} (blocks after b)
-      const float fb = b == 0 ? 1.f : (b == 1 ? t0_ : (b == 2 ? t0_ * t1_ : t0_ * t1_ * t2_));
-      const float gb = b == 3 ? 1.f : (b == 2 ? t3_ : (b == 1 ? t2_ * t3_ : t1_ * t2_ * t3_));
-      if (b == 0) {
-        reinterpret_cast<float *>(rec + a.lay.p63)[ch] = t0_ * t1_ * t2_ * t3_;
-        sF[ch] = t1_;
-        sF[DK + ch] = t2_;
-        sF[2 * DK + ch] = t1_ * t2_;
-      }
+    for (int s = 0; s < NP; ++s) {
+      const int p = w + 4 * s;
+      rt[s] = at[s] = zero4();
+      if (p < 10) {
+        int I, J;
+        tile_ij(p, I, J);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = 16 * b + i;
-        const float kr = kv[m][i] * pa[m][i], qr = qv[m][i] * pa[m][i];
-        sKr[row * LD + ch] = from_f<E>(kr);
-        sQr[row * LD + ch] = from_f<E>(qr);
-        sKl[row * LD + ch] = from_f<E>(kv[m][i] * ps[m][i]);
-        sKd[row * LD + ch] = from_f<E>(kv[m][i] * __builtin_amdgcn_rcpf(pa[m][i]));
-        gKh[frag_index<E, DK>(row, ch)] = from_f<E>(kr * fb);                  // k_i D_{0:i}
-        gQh[frag_index<E, DK>(row, ch)] = from_f<E>(qr * fb * a.scale);        // s q_i D_{0:i}
-        gKtT[frag_index<E, 64>(ch, row)] = from_f<E>(kv[m][i] * ps[m][i] * gb);  // k_j D_{j+1:63}
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- A^kk (tiles 0..9) and A^qk (tiles 10..19), lower block triangle
-  f32x4 acc[5];
-#pragma unroll
-  for (int s = 0; s < 5; ++s) {
-    const int t = w + 4 * s, kind = t / 10;
-    int I, J;
-    tile_ij(t % 10, I, J);
-    const E *arow = (kind == 0 ? sKr : sQr) + (16 * I + (l & 15)) * LD;
-    const E *brow = (I == J ? sKd : sKl) + (16 * J + (l & 15)) * LD;
-    const float *f = I - J == 2 ? sF + (J == 0 ? 0 : DK) : (I - J == 3 ? sF + 2 * DK : nullptr);
-    acc[s] = mma_rows_scaled<M, DK>(arow, brow, f, zero4());
-  }
-  __syncthreads();  // the operand area is reused from here on
-
-#pragma unroll
-  for (int s = 0; s < 5; ++s) {
-    const int t = w + 4 * s, kind = t / 10;
-    int I, J;
-    tile_ij(t % 10, I, J);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 16 * I + 4 * (l >> 4) + r, j = 16 * J + (l & 15);
-      if (kind == 0)
-        sR[i * LDR + j] = j < i ? sBeta[i] * acc[s][r] : 0.f;
-      else
-        sOut[i * LDT + j] = from_f<E>(j <= i ? a.scale * acc[s][r] : 0.f);
-    }
-  }
-  // zero the blocks of A above the diagonal
-  for (int idx = tid; idx < 6 * 256; idx += kThreads) {
-    const int u = idx >> 8, e = idx & 255;
-    const int I = u < 3 ? 0 : (u < 5 ? 1 : 2);
-    const int J = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
-    sOut[(16 * I + (e >> 4)) * LDT + 16 * J + (e & 15)] = from_f<E>(0.f);
-  }
-  __syncthreads();
-
-  // ---- exact diagonal blocks where the in-block decay left fp32's range:
-  // thread (j, channel group) runs D_{j+1:i} as a product over i.
-  for (int b = 0; b < 4; ++b) {
-    if (!sFlag[b]) continue;  // uniform: read after a barrier
-    constexpr int CPG = DK / 16;
-    const int j = tid >> 4, cg = tid & 15, s0 = 16 * b;
-    float racc[16], aacc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) racc[i] = aacc[i] = 0.f;
-    for (int cc = 0; cc < CPG; ++cc) {
-      const int ch = cg * CPG + cc;
-      const float kj = s0 + j < L ? to_f(k[base + (size_t)(s0 + j) * hs + ch]) : 0.f;
-      float rho = 1.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        if (i >= j && s0 + i < L) {
-          const size_t off = base + (size_t)(s0 + i) * hs + ch;
-          if (i > j) rho *= a.alpha[off];
-          const float wgt = kj * rho;
-          if (i > j) racc[i] += to_f(k[off]) * wgt;
-          aacc[i] += to_f(q[off]) * wgt;
+        for (int u = 0; u < LK::F::NU; ++u) {
+          const char *ad = sKd + LK::slot_off(J, u, l & 15, l >> 4);
+          rt[s] = slot_mma<E, DK>(ad, sKh + LK::slot_off(I, u, l & 15, l >> 4), rt[s]);
+          at[s] = slot_mma<E, DK>(ad, sQh + LK::slot_off(I, u, l & 15, l >> 4), at[s]);
         }
       }
     }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) {
-        racc[i] += __shfl_xor(racc[i], m);
-        aacc[i] += __shfl_xor(aacc[i], m);
-      }
-    }
-    if (cg == 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sR[(s0 + i) * LDR + s0 + j] = i > j ? sBeta[s0 + i] * racc[i] : 0.f;
-        sOut[(s0 + i) * LDT + s0 + j] = from_f<E>(i >= j ? a.scale * aacc[i] : 0.f);
-      }
-    }
-    __syncthreads();
   }
-  lds_to_global_frag64(reinterpret_cast<E *>(rec + a.lay.aqk), sOut, LDT);
+  copy_out<LK>(rec + a.lay.kh, sKh);
+  copy_out<LK>(rec + a.lay.qh, sQh);
+  __syncthreads();  // phase-1 images are dead from here on
+
+  E *gA = reinterpret_cast<E *>(rec + a.lay.aqk);
+  if (!exact) {
+    // R (scaled by beta_i, j < i) to LDS for the solve; A (j <= i) straight to
+    // the record: lane (i, g) holds A[i][16J + 4g .. +3], four consecutive
+    // elements of one record slot.
+#pragma unroll
+    for (int s = 0; s < NP; ++s) {
+      const int p = w + 4 * s;
+      if (p < 10) {
+        int I, J;
+        tile_ij(p, I, J);
+        const int i = 16 * I + (l & 15), jb = 16 * J + 4 * (l >> 4);
+        float rv[4], av[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          rv[r] = jb + r < i ? sBeta[i] * rt[s][r] : 0.f;
+          av[r] = jb + r <= i ? at[s][r] : 0.f;
+        }
+        *reinterpret_cast<f32x4 *>(sR + i * LDR + jb) = f32x4{rv[0], rv[1], rv[2], rv[3]};
+        *reinterpret_cast<typename F4::vec *>(gA + frag_index<E, 64>(i, jb)) = F4::pack(av);
+      }
+    }
+    // blocks above the diagonal of A are zero
+    for (int idx = tid; idx < 6 * 64; idx += kThreads) {
+      const int u = idx >> 6, ln = idx & 63;
+      const int I = u < 3 ? 0 : (u < 5 ? 1 : 2);
+      const int J = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
+      const float z[4] = {0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<typename F4::vec *>(gA + frag_index<E, 64>(16 * I + (ln & 15), 16 * J + 4 * (ln >> 4))) =
+          F4::pack(z);
+    }
+    // Kend^T into its LDS image (copied out after the next barrier): four
+    // consecutive tokens of one channel are contiguous there
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (TPL >= 4) {
+#pragma unroll
+        for (int u = 0; u < TPL; u += 4) {
+          typename F4::vec v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const E x = ktt[u + e][j];
+            v[e] = x;
+          }
+          *reinterpret_cast<typename F4::vec *>(sX + LT::elem_off(c0 + j, tb0 + u)) = v;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+          const E x = ktt[u][j];
+          *reinterpret_cast<E *>(sX + LT::elem_off(c0 + j, tb0 + u)) = x;
+        }
+      }
+    }
+  } else {
+    // R and A channel by channel: thread (j, quarter) runs D_{j+1:i} over i
+    // for its quarter of the channels; the four quarters are summed across
+    // neighbouring lanes.
+    constexpr int CQ = DK / 4;
+    float *sA = reinterpret_cast<float *>(sX);
+    const int j = tid >> 2, qd = tid & 3;
+    const size_t cb = (size_t)t0 * hs + (size_t)h * DK + qd * CQ;
+    float kj[CQ], rho[CQ];
+#pragma unroll
+    for (int cc = 0; cc < CQ; cc += 4) {
+      F4::load(k + cb + (size_t)min(j, L - 1) * hs + cc, kj + cc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kj[cc + e] = j < L ? kj[cc + e] : 0.f;
+        rho[cc + e] = 1.f;
+      }
+    }
+    for (int i = 0; i < kChunk; ++i) {
+      const bool live = i < L;
+      const size_t off = cb + (size_t)min(i, L - 1) * hs;
+      float racc = 0.f, aacc = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < CQ; cc += 4) {
+        float al[4], kx[4], qx[4];
+        Four<float>::load(a.alpha + off + cc, al);
+        F4::load(k + off + cc, kx);
+        F4::load(q + off + cc, qx);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (i > j) rho[cc + e] *= live ? al[e] : 1.f;
+          const float wgt = i >= j ? kj[cc + e] * rho[cc + e] : 0.f;
+          racc += (live ? kx[e] : 0.f) * wgt;
+          aacc += (live ? qx[e] : 0.f) * wgt;
+        }
+      }
+      racc += __shfl_xor(racc, 1);
+      aacc += __shfl_xor(aacc, 1);
+      racc += __shfl_xor(racc, 2);
+      aacc += __shfl_xor(aacc, 2);
+      if (qd == 0) {
+        sR[i * LDR + j] = i > j ? sBeta[i] * racc : 0.f;
+        sA[i * LDR + j] = i >= j ? a.scale * aacc : 0.f;
+      }
+    }
+    // Kend^T straight to the record (scattered; this path is rare)
+    E *gT = reinterpret_cast<E *>(rec + a.lay.ktt);
+#pragma unroll
+    for (int u = 0; u < TPL; ++u)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const E x = ktt[u][jj];
+        gT[frag_index<E, 64>(c0 + jj, tb0 + u)] = x;
+      }
+  }
+  __syncthreads();
+
+  if (!exact) {
+    copy_out<LT>(rec + a.lay.ktt, sX);
+  } else {
+    tile64_out<E, LDR>(gA, reinterpret_cast<const float *>(sX), nullptr);
+  }
+  if (w == 0 && th == 0) *reinterpret_cast<f32x4 *>(rec + a.lay.p63 + 4 * c0) = f32x4{p63[0], p63[1], p63[2], p63[3]};
 
   // ---- T = (I + R)^{-1}: diagonal 16x16 blocks by forward substitution.
   if (w == 0) {
@@ -465,13 +704,8 @@ __global__ __launch_bounds__(kThreads) void chunk_prep_kernel(PrepKArgs a) {
   if (w == 0) inverse_offdiag_block<LDR>(3, 0, sR, sT);     // (3,0)
   __syncthreads();
 
-  // ---- Tb = T Diag(beta), zero above the diagonal
-  for (int idx = tid; idx < 64 * 64; idx += kThreads) {
-    const int i = idx >> 6, j = idx & 63;
-    sOut[i * LDT + j] = from_f<E>(j <= i ? sT[i * LDR + j] * sBeta[j] : 0.f);
-  }
-  __syncthreads();
-  lds_to_global_frag64(reinterpret_cast<E *>(rec + a.lay.tb), sOut, LDT);
+  // ---- Tb = T Diag(beta), zero above the diagonal, into the record
+  tile64_out<E, LDR>(reinterpret_cast<E *>(rec + a.lay.tb), sT, sBeta);
 }
 
 // ======================================================= kernel 2: chunk scan
