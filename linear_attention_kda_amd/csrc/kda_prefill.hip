@@ -813,6 +813,14 @@ __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt[3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).  Vector memory loads
+// retire in issue order, so this waits for all but the N latest.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Compile-time copy of ChunkRecordLayout for the scan's LDS image of a record.
 template <int DK, typename E> struct RecordShape {
   static constexpr int es = sizeof(E);
@@ -832,8 +840,8 @@ template <int DK, typename E> struct RecordShape {
 // conflict-free 16-byte reads, shared by the NT column tiles) and its B
 // operand from the wave's own accumulators.  Workgroups of one unit get ids
 // congruent mod 8, which the dispatcher sends to one XCD.
-template <int DK, typename E, int NT, int CW>
-__global__ __launch_bounds__(64 * (CW + 1)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int DK, typename E, int NT, int CW, int NCP>
+__global__ __launch_bounds__(64 * (CW + NCP)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunk_scan_kernel(ScanKArgs a) {
   typedef RecordShape<DK, E> RS;
   constexpr int CT = DK / 16;
@@ -843,13 +851,15 @@ void chunk_scan_kernel(ScanKArgs a) {
   constexpr int TILE_K = FK::NU * 64 * FK::KS;   // elements per 16-row tile, K = d_k
   constexpr int TILE_T = FT::NU * 64 * FT::KS;   // elements per 16-row tile, K = 64
   constexpr int VSL = 64 * VC;                   // value-slice elements per compute wave
-  constexpr int STAGE = RS::bytes + CW * VSL * (int)sizeof(E);
-  constexpr int NBUF = 2 * STAGE <= 160 * 1024 ? 2 : 1;   // double buffer if it fits
-  static_assert(STAGE <= 160 * 1024 - 1024, "one stage must fit in LDS");
+  constexpr int VBYTES = CW * VSL * (int)sizeof(E);
+  // records double-buffered, value tiles in a ring of three (they come from
+  // HBM, so they are requested two chunks ahead) if that fits
+  constexpr int NBUF = 2 * RS::bytes + 3 * VBYTES <= 159 * 1024 ? 2 : 1;
+  static_assert(RS::bytes + VBYTES <= 159 * 1024, "one stage must fit in LDS");
+  constexpr int NV = NBUF == 2 ? 3 : 1;
   __shared__ __attribute__((aligned(1024))) char rec0[RS::bytes];
   __shared__ __attribute__((aligned(1024))) char rec1[NBUF == 2 ? RS::bytes : 1024];
-  __shared__ __attribute__((aligned(16))) E vsl0[CW * VSL];
-  __shared__ __attribute__((aligned(16))) E vsl1[NBUF == 2 ? CW * VSL : 8];
+  __shared__ __attribute__((aligned(16))) E vring[NV][CW * VSL];
 
   const int w = wave_id(), l = lane_id(), col = l & 15, g = l >> 4;
   const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
@@ -858,7 +868,9 @@ void chunk_scan_kernel(ScanKArgs a) {
   const int n = u / a.H, h = u % a.H;
   const int vwg = (slot % a.wg_per_unit) * (CW * VC);  // first value column of the workgroup
   const int H = a.H, DV = a.dv;
-  const bool copier = w == CW;
+  const bool copier = w >= CW;
+  const int cpi = w - CW;                  // index among the copy waves
+  const bool vcopier = w == CW + NCP - 1;  // the copy wave that also moves the value tiles
 
   long long tstart, ntok, chunk0;
   if (a.seq_tok0) {
@@ -876,44 +888,73 @@ void chunk_scan_kernel(ScanKArgs a) {
   const size_t tok_stride = (size_t)H * DV;
 
   // ----------------------------------------------------------- copy wave
-  // Value slices land as [compute wave][16-byte column group][token][elements];
-  // rows past the end of the sequence repeat its last token (they never reach
-  // a valid output: their Tb rows and columns are zero).
+  // The workgroup's value columns land as [token][WC elements] (RB bytes per
+  // row).  Each copy covers 64/LPRW whole rows, LPRW lanes per row, so one
+  // instruction touches one line segment per row instead of one line per
+  // lane.  Rows past the end of the sequence repeat its last token (they never
+  // reach a valid output: their Tb rows and columns are zero).
   constexpr int VE = 16 / (int)sizeof(E);        // elements per 16-byte group
-  constexpr int VG = VC / VE;                    // 16-byte groups per value row
-  auto copy_chunk = [&](int ci, char *rec, E *vsl) {
+  constexpr int WC = CW * VC;                    // value columns of the workgroup
+  constexpr int RB = WC * (int)sizeof(E);        // bytes per staged row
+  constexpr int LPRW = RB / 16;                  // lanes per row
+  constexpr int RPI = 64 / LPRW;                 // rows per copy
+  static_assert(RB % 16 == 0 && LPRW <= 64, "value rows are whole 16-byte groups");
+  constexpr int NVD = 64 / RPI;                  // value copies per chunk
+  auto copy_rec = [&](int ci, char *rec) {
     const char *src = a.ws_records + ((size_t)(chunk0 + ci) * H + h) * RS::bytes + l * 16;
     const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)rec;
-    for (int q = 0; q < RS::bytes / 1024; ++q) lds_dma16(src + q * 1024, lds + q * 1024);
+    // copy wave cpi takes KiB blocks cpi*QPW .. cpi*QPW + QPW - 1, clamped to
+    // the last block (a clamped block is copied twice with the same bytes),
+    // so the loop unrolls with no branch per copy
+    constexpr int NQ = RS::bytes / 1024, QPW = (NQ + NCP - 1) / NCP;
+#pragma unroll
+    for (int qq = 0; qq < QPW; ++qq) {
+      const int q = min(cpi * QPW + qq, NQ - 1);
+      lds_dma16(src + q * 1024, lds + q * 1024);
+    }
+  };
+  auto copy_v = [&](int ci, E *vsl) {
     const long long t0 = tstart + (long long)kChunk * ci;
     const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
-    const E *vsrc = V + (size_t)(t0 + min(l, L - 1)) * tok_stride + (size_t)h * DV + vwg;
     const uint32_t vl = (uint32_t)(size_t)(__attribute__((address_space(3))) E *)vsl;
+    const int vr = l / LPRW, vc = (l % LPRW) * VE;
 #pragma unroll
-    for (int cw = 0; cw < CW; ++cw)
-#pragma unroll
-      for (int q = 0; q < VG; ++q)
-        lds_dma16(vsrc + cw * VC + q * VE, vl + (uint32_t)((cw * VSL + q * 64 * VE) * sizeof(E)));
+    for (int j = 0; j < 64 / RPI; ++j) {
+      const E *vsrc = V + (size_t)(t0 + min(j * RPI + vr, L - 1)) * tok_stride + (size_t)h * DV + vwg + vc;
+      lds_dma16(vsrc, vl + j * 1024);
+    }
   };
   if (copier) {
     if (NBUF == 2) {
-      if (nchunks > 0) copy_chunk(0, rec0, vsl0);
-      __builtin_amdgcn_s_waitcnt(0);
+      if (nchunks > 0) {
+        copy_rec(0, rec0);
+        if (vcopier) copy_v(0, vring[0]);
+      }
+      if (vcopier && nchunks > 1) {
+        copy_v(1, vring[1]);
+        wait_vmcnt<NVD>();             // chunk 0 in; chunk 1's values may still fly
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
       __syncthreads();  // chunk 0 ready
       for (int ci = 0; ci < nchunks; ++ci) {
-        // buffer (ci+1)%2 held chunk ci-1, which every compute wave finished
-        // before the barrier that ended the previous step
-        if (ci + 1 < nchunks) {
-          if (ci & 1) copy_chunk(ci + 1, rec0, vsl0);
-          else copy_chunk(ci + 1, rec1, vsl1);
+        // record buffer (ci+1)%2 and value slot (ci+2)%3 held chunk ci-1, which
+        // every compute wave finished before the barrier that ended the
+        // previous step
+        if (ci + 1 < nchunks) copy_rec(ci + 1, (ci & 1) ? rec0 : rec1);
+        if (vcopier && ci + 2 < nchunks) {
+          copy_v(ci + 2, vring[(ci + 2) % 3]);
+          wait_vmcnt<NVD>();           // all but chunk ci+2's values
+        } else {
+          __builtin_amdgcn_s_waitcnt(0);
         }
-        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // chunk ci done by the compute waves, chunk ci+1 ready
       }
     } else {
       for (int ci = 0; ci < nchunks; ++ci) {
         __syncthreads();  // buffer free
-        copy_chunk(ci, rec0, vsl0);
+        copy_rec(ci, rec0);
+        if (vcopier) copy_v(ci, vring[0]);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();  // buffer ready
       }
@@ -944,7 +985,7 @@ void chunk_scan_kernel(ScanKArgs a) {
     const E *Tb = reinterpret_cast<const E *>(recb + RS::tb);
     const E *Aq = reinterpret_cast<const E *>(recb + RS::aqk);
     const float *P63 = reinterpret_cast<const float *>(recb + RS::p63);
-    vs += w * VSL;
+    vs += w * VC;
 
     // X_top = Kbnd S^T, X_bot = s Qbnd S^T
     BK sb[NT];
@@ -975,7 +1016,7 @@ void chunk_scan_kernel(ScanKArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int c = 16 * nt + col;
-          eb[I][r] = to_f(vs[((c / VE) * 64 + 16 * I + 4 * g + r) * VE + c % VE]) - xt[I][nt][r];
+          eb[I][r] = to_f(vs[(16 * I + 4 * g + r) * WC + c]) - xt[I][nt][r];
         }
       ebo[nt].build(eb);
     }
@@ -1064,11 +1105,11 @@ void chunk_scan_kernel(ScanKArgs a) {
     __syncthreads();  // chunk 0 ready
     for (int ci = 0; ci < nchunks; ci += 2) {
       if (ci > 0) store_o(ci - 1, ov);
-      compute(rec0, vsl0, ov);
+      compute(rec0, vring[ci % NV], ov);
       __syncthreads();
       if (ci + 1 >= nchunks) break;
       store_o(ci, ov);
-      compute(rec1, vsl1, ov);
+      compute(rec1, vring[(ci + 1) % NV], ov);
       __syncthreads();
     }
   } else {
@@ -1076,7 +1117,7 @@ void chunk_scan_kernel(ScanKArgs a) {
       __syncthreads();  // buffer free
       if (ci > 0) store_o(ci - 1, ov);
       __syncthreads();  // buffer ready
-      compute(rec0, vsl0, ov);
+      compute(rec0, vring[ci % NV], ov);
     }
   }
   if (nchunks > 0) store_o(nchunks - 1, ov);
@@ -1093,19 +1134,14 @@ template <int DK, typename E> constexpr bool scan_stage_fits(int nt, int cw) {
   return RecordShape<DK, E>::bytes + cw * 64 * 16 * nt * (int)sizeof(E) <= 160 * 1024 - 1024;
 }
 
-template <int DK, typename E, int NT>
-void launch_scan(int cw, dim3 grid, dim3 block, hipStream_t stream, const ScanKArgs &sa) {
-  if constexpr (scan_stage_fits<DK, E>(NT, 4))
-    if (cw == 4) {
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, NT, 4>), grid, block, 0, stream, sa);
-      return;
-    }
+template <int DK, typename E, int NT, int NCP>
+void launch_scan(int cw, dim3 grid, hipStream_t stream, const ScanKArgs &sa) {
   if constexpr (scan_stage_fits<DK, E>(NT, 2))
     if (cw == 2) {
-      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, NT, 2>), grid, block, 0, stream, sa);
+      hipLaunchKernelGGL((chunk_scan_kernel<DK, E, NT, 2, NCP>), grid, dim3(64 * (2 + NCP)), 0, stream, sa);
       return;
     }
-  hipLaunchKernelGGL((chunk_scan_kernel<DK, E, NT, 1>), grid, block, 0, stream, sa);
+  hipLaunchKernelGGL((chunk_scan_kernel<DK, E, NT, 1, NCP>), grid, dim3(64 * (1 + NCP)), 0, stream, sa);
 }
 
 // ================================================================ dispatch
@@ -1168,24 +1204,31 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     // Two tiles per wave halve the LDS reads per column but double each
     // wave's serial chain of products; one tile and two compute waves per
     // workgroup measured fastest at d_v = 128.
-    int nt = 1, cw = a.dv >= 32 ? 2 : 1;
+    int nt = 1, cw = a.dv >= 32 ? 2 : 1, ncp = 3;
     if (const char *env = std::getenv("KDA_SCAN_NT")) {
       const int x = std::atoi(env);
       if ((x == 1 || x == 2) && 16 * x <= a.dv) nt = x;
     }
     if (const char *env = std::getenv("KDA_SCAN_CW")) {
       const int x = std::atoi(env);
-      if (x == 1 || x == 2 || x == 4) cw = x;
+      if (x == 1 || x == 2) cw = x;
+    }
+    if (const char *env = std::getenv("KDA_SCAN_CP")) {
+      const int x = std::atoi(env);
+      if (x == 1 || x == 3) ncp = x;
     }
     while (cw > 1 && (16 * nt * cw > a.dv || !scan_stage_fits<DK, E>(nt, cw))) cw /= 2;
     sa.wg_per_unit = a.dv / (16 * nt * cw);
     const long long slots = ((long long)sa.n_units + 7) / 8 * 8 * sa.wg_per_unit;
     const dim3 grid((unsigned)slots);
-    const dim3 block(64 * (cw + 1));
-    if (nt == 2)
-      launch_scan<DK, E, 2>(cw, grid, block, stream, sa);
+    if (nt == 2 && ncp == 3)
+      launch_scan<DK, E, 2, 3>(cw, grid, stream, sa);
+    else if (nt == 2)
+      launch_scan<DK, E, 2, 1>(cw, grid, stream, sa);
+    else if (ncp == 3)
+      launch_scan<DK, E, 1, 3>(cw, grid, stream, sa);
     else
-      launch_scan<DK, E, 1>(cw, grid, block, stream, sa);
+      launch_scan<DK, E, 1, 1>(cw, grid, stream, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
