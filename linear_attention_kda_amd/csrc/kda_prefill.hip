@@ -827,6 +827,15 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The same with the nontemporal hint, for data read exactly once.
+__device__ __forceinline__ void lds_dma16_nt(const void *src, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
+}
+
 // Compile-time copy of ChunkRecordLayout for the scan's LDS image of a record.
 template <int DK, typename E> struct RecordShape {
   static constexpr int es = sizeof(E);
@@ -927,7 +936,7 @@ void chunk_scan_kernel(ScanKArgs a) {
 #pragma unroll
     for (int j = 0; j < 64 / RPI; ++j) {
       const E *vsrc = V + (size_t)(t0 + min(j * RPI + vr, L - 1)) * tok_stride + (size_t)h * DV + vwg + vc;
-      lds_dma16(vsrc, vl + j * 1024);
+      lds_dma16_nt(vsrc, vl + j * 1024);
     }
   };
   if (copier) {
@@ -1097,11 +1106,12 @@ void chunk_scan_kernel(ScanKArgs a) {
           // copy the lane value out of the vector first: a bit cast applied to
           // a vector-element subscript reads element 0 with this compiler
           const float x = ov[I][nt][r];
+          // cache policy 2 = nontemporal: every output byte is written once
           if constexpr (sizeof(E) == 2)
             __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f<E>(x)), rs,
-                                                  o_lane + row_off, 0, 0);
+                                                  o_lane + row_off, 0, 2);
           else
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), rs, o_lane + row_off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), rs, o_lane + row_off, 0, 2);
         }
     }
   };
