@@ -770,13 +770,18 @@ template <int K> struct BOps<bf16, K> {
   template <int KU>
   __device__ __forceinline__ f32x4 mma(const A<KU> &a, f32x4 acc) const {
 #pragma unroll
-    for (int u = 0; u < (KU + F::W - 1) / F::W; ++u) {
-      if constexpr (F::wide)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.x[u], f[u], acc, 0, 0, 0);
-      else
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.x[u], f[u], acc, 0, 0, 0);
-    }
+    for (int u = 0; u < (KU + F::W - 1) / F::W; ++u) acc = mma1(a.x[u], u, acc);
     return acc;
+  }
+  // one slab: the A fragment of slab u of the tile at `a`, and its product
+  __device__ __forceinline__ static frag load1(const bf16 *a, int u) {
+    return *reinterpret_cast<const frag *>(a + (u * 64 + lane_id()) * F::KS);
+  }
+  __device__ __forceinline__ f32x4 mma1(const frag &a, int u, f32x4 acc) const {
+    if constexpr (F::wide)
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, f[u], acc, 0, 0, 0);
+    else
+      return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, f[u], acc, 0, 0, 0);
   }
 };
 
@@ -801,9 +806,16 @@ template <int K> struct BOps<float, K> {
   template <int KU>
   __device__ __forceinline__ f32x4 mma(const A<KU> &a, f32x4 acc) const {
 #pragma unroll
-    for (int u = 0; u < (KU + 15) / 16; ++u)
+    for (int u = 0; u < (KU + 15) / 16; ++u) acc = mma1(a.x[u], u, acc);
+    return acc;
+  }
+  typedef f32x4 frag;
+  __device__ __forceinline__ static frag load1(const float *a, int u) {
+    return *reinterpret_cast<const f32x4 *>(a + (u * 64 + lane_id()) * 4);
+  }
+  __device__ __forceinline__ f32x4 mma1(const frag &a, int u, f32x4 acc) const {
 #pragma unroll
-      for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x[u][s], f[u][s], acc, 0, 0, 0);
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], f[u][s], acc, 0, 0, 0);
     return acc;
   }
 };
@@ -988,12 +1000,14 @@ void chunk_scan_kernel(ScanKArgs a) {
       st[ct][nt] = a.S0 ? *reinterpret_cast<const f32x4 *>(a.S0 + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g)
                         : zero4();
 
-  // One chunk.  LDS operand reads are issued in the order the products use
-  // them; the scheduler is held to a pattern that keeps reads ahead of the
-  // matrix cores while bounding the registers the fragments take.
+  // One chunk.  Every product loop runs slab-major (the k slab outer, the
+  // 16-row tiles inner), so consecutive matrix-core products are independent
+  // and none waits for the previous one's result; the LDS operand reads of
+  // later phases are issued early, in the order they are used.
   auto compute = [&](const char *recb, const E *vs, f32x4 (*ov)[NT]) {
     typedef BOps<E, DK> BK;
     typedef BOps<E, 64> BT;
+    constexpr int UK = FK::NU, UT = FT::NU;          // slabs over d_k, over 64 tokens
     const E *Kh = reinterpret_cast<const E *>(recb + RS::kh);
     const E *Qh = reinterpret_cast<const E *>(recb + RS::qh);
     const E *KtT = reinterpret_cast<const E *>(recb + RS::ktt);
@@ -1001,8 +1015,10 @@ void chunk_scan_kernel(ScanKArgs a) {
     const E *Aq = reinterpret_cast<const E *>(recb + RS::aqk);
     const float *P63 = reinterpret_cast<const float *>(recb + RS::p63);
     vs += w * VC;
+    // row tile I of Tb and A only needs slabs holding columns < 16 (I + 1)
+    auto need = [](int I, int u) { return u * FT::W < 16 * (I + 1); };
 
-    // X_top = Kbnd S^T, X_bot = s Qbnd S^T
+    // B operands from the state; X_top = Kbnd S^T, X_bot = s Qbnd S^T
     BK sb[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1013,15 +1029,53 @@ void chunk_scan_kernel(ScanKArgs a) {
     }
     f32x4 xt[4][NT], xb[4][NT];
 #pragma unroll
-    for (int I = 0; I < 4; ++I) {
-      const typename BK::template A<DK> fk = BK::template load<DK>(Kh + I * TILE_K);
+    for (int I = 0; I < 4; ++I)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) xt[I][nt] = sb[nt].mma(fk, zero4());
-      const typename BK::template A<DK> fq = BK::template load<DK>(Qh + I * TILE_K);
+      for (int nt = 0; nt < NT; ++nt) xt[I][nt] = xb[I][nt] = zero4();
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) xb[I][nt] = sb[nt].mma(fq, zero4());
+    for (int u = 0; u < UK; ++u) {
+      typename BK::frag fk[4], fq[4];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        fk[I] = BK::load1(Kh + I * TILE_K, u);
+        fq[I] = BK::load1(Qh + I * TILE_K, u);
+      }
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          xt[I][nt] = sb[nt].mma1(fk[I], u, xt[I][nt]);
+          xb[I][nt] = sb[nt].mma1(fq[I], u, xb[I][nt]);
+        }
     }
-    // Ebar = V - X_top ; E = Tb Ebar (row block I needs columns < 16(I+1))
+    // operands of the later phases
+    typename BT::frag ftb[4][UT], faq[4][UT], fkt[CT][UT];
+    float vv[NT][4][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vv[nt][I][r] = to_f(vs[(16 * I + 4 * g + r) * WC + 16 * nt + col]);
+#pragma unroll
+    for (int u = 0; u < UT; ++u)
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+        if (need(I, u)) ftb[I][u] = BT::load1(Tb + I * TILE_T, u);
+#pragma unroll
+    for (int u = 0; u < UT; ++u)
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+        if (need(I, u)) faq[I][u] = BT::load1(Aq + I * TILE_T, u);
+#pragma unroll
+    for (int u = 0; u < UT; ++u)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) fkt[ct][u] = BT::load1(KtT + ct * TILE_T, u);
+    f32x4 p[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) p[ct] = *reinterpret_cast<const f32x4 *>(P63 + 16 * ct + 4 * g);
+
+    // Ebar = V - X_top ; E = Tb Ebar
     BT ebo[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1029,27 +1083,22 @@ void chunk_scan_kernel(ScanKArgs a) {
 #pragma unroll
       for (int I = 0; I < 4; ++I)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = 16 * nt + col;
-          eb[I][r] = to_f(vs[(16 * I + 4 * g + r) * WC + c]) - xt[I][nt][r];
-        }
+        for (int r = 0; r < 4; ++r) eb[I][r] = vv[nt][I][r] - xt[I][nt][r];
       ebo[nt].build(eb);
     }
     f32x4 e[4][NT];
-    {
-      const typename BT::template A<16> f0 = BT::template load<16>(Tb + 0 * TILE_T);
-      const typename BT::template A<32> f1 = BT::template load<32>(Tb + 1 * TILE_T);
-      const typename BT::template A<48> f2 = BT::template load<48>(Tb + 2 * TILE_T);
-      const typename BT::template A<64> f3 = BT::template load<64>(Tb + 3 * TILE_T);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        e[0][nt] = ebo[nt].mma(f0, zero4());
-        e[1][nt] = ebo[nt].mma(f1, zero4());
-        e[2][nt] = ebo[nt].mma(f2, zero4());
-        e[3][nt] = ebo[nt].mma(f3, zero4());
-      }
-    }
-    // O = s Qbnd S^T + A E
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) e[I][nt] = zero4();
+#pragma unroll
+    for (int u = 0; u < UT; ++u)
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+        if (need(I, u))
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) e[I][nt] = ebo[nt].mma1(ftb[I][u], u, e[I][nt]);
+    // O = s Qbnd S^T + A E ;  S^T = D_{0:63} S^T + Kend^T E
     BT eo[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1058,30 +1107,27 @@ void chunk_scan_kernel(ScanKArgs a) {
       for (int I = 0; I < 4; ++I) et[I] = e[I][nt];
       eo[nt].build(et);
     }
-    {
-      const typename BT::template A<16> f0 = BT::template load<16>(Aq + 0 * TILE_T);
-      const typename BT::template A<32> f1 = BT::template load<32>(Aq + 1 * TILE_T);
-      const typename BT::template A<48> f2 = BT::template load<48>(Aq + 2 * TILE_T);
-      const typename BT::template A<64> f3 = BT::template load<64>(Aq + 3 * TILE_T);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        ov[0][nt] = eo[nt].mma(f0, xb[0][nt]);
-        ov[1][nt] = eo[nt].mma(f1, xb[1][nt]);
-        ov[2][nt] = eo[nt].mma(f2, xb[2][nt]);
-        ov[3][nt] = eo[nt].mma(f3, xb[3][nt]);
-      }
-    }
-    // S^T = D_{0:63} S^T + Kend^T E
+    for (int I = 0; I < 4; ++I)
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) {
-      const f32x4 p = *reinterpret_cast<const f32x4 *>(P63 + 16 * ct + 4 * g);
-      const typename BT::template A<64> fkt = BT::template load<64>(KtT + ct * TILE_T);
+      for (int nt = 0; nt < NT; ++nt) ov[I][nt] = xb[I][nt];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st[ct][nt][r] *= p[r];
-        st[ct][nt] = eo[nt].mma(fkt, st[ct][nt]);
-      }
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[ct][nt][r] *= p[ct][r];
+#pragma unroll
+    for (int u = 0; u < UT; ++u) {
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+        if (need(I, u))
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) ov[I][nt] = eo[nt].mma1(faq[I][u], u, ov[I][nt]);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) st[ct][nt] = eo[nt].mma1(fkt[ct][u], u, st[ct][nt]);
     }
   };
 
