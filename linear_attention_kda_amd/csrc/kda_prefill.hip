@@ -879,14 +879,19 @@ void chunk_scan_kernel(ScanKArgs a) {
   constexpr int TILE_T = FT::NU * 64 * FT::KS;   // elements per 16-row tile, K = 64
   constexpr int VSL = 64 * VC;                   // value-slice elements per compute wave
   constexpr int VBYTES = CW * VSL * (int)sizeof(E);
+  // outputs of a chunk, staged as rows for the copy waves to store: WC
+  // columns per row, rows padded by 16 bytes
+  constexpr int OROW = CW * VC * (int)sizeof(E) + 16;
   // records double-buffered, value tiles in a ring of three (they come from
-  // HBM, so they are requested two chunks ahead) if that fits
-  constexpr int NBUF = 2 * RS::bytes + 3 * VBYTES <= 159 * 1024 ? 2 : 1;
+  // HBM, so they are requested two chunks ahead) and two output stages, if
+  // that fits
+  constexpr int NBUF = 2 * RS::bytes + 3 * VBYTES + 2 * 64 * OROW <= 159 * 1024 ? 2 : 1;
   static_assert(RS::bytes + VBYTES <= 159 * 1024, "one stage must fit in LDS");
   constexpr int NV = NBUF == 2 ? 3 : 1;
   __shared__ __attribute__((aligned(1024))) char rec0[RS::bytes];
   __shared__ __attribute__((aligned(1024))) char rec1[NBUF == 2 ? RS::bytes : 1024];
   __shared__ __attribute__((aligned(16))) E vring[NV][CW * VSL];
+  __shared__ __attribute__((aligned(16))) char otile[2][NBUF == 2 ? 64 * OROW : 16];
 
   const int w = wave_id(), l = lane_id(), col = l & 15, g = l >> 4;
   const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
@@ -951,6 +956,26 @@ void chunk_scan_kernel(ScanKArgs a) {
       lds_dma16_nt(vsrc, vl + j * 1024);
     }
   };
+  // chunk ci's outputs from an LDS stage to o: 16-byte row segments; the
+  // buffer descriptor covers exactly the chunk's valid rows, so rows past the
+  // end of the sequence are dropped by the hardware (the whole offset goes in
+  // the VGPR operand: the range check of a raw buffer access does not include
+  // soffset); nontemporal, every output byte is written once
+  auto store_tile = [&](int ci, const char *ot) {
+    const long long t0 = tstart + (long long)kChunk * ci;
+    const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        O + (size_t)t0 * tok_stride, 0, (int)((size_t)L * tok_stride * sizeof(E)), 0x00020000);
+    constexpr int SEG = RB / 16;
+#pragma unroll
+    for (int k = 0; k < SEG; ++k) {
+      const int idx = l + 64 * k, row = idx / SEG, sg = idx % SEG;
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(ot + row * OROW + sg * 16);
+      const int off = (int)(((size_t)row * tok_stride + (size_t)h * DV + vwg) * sizeof(E)) + sg * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((__vector_size__(16))) unsigned int, v),
+                                             rs, off, 0, 2);
+    }
+  };
   if (copier) {
     if (NBUF == 2) {
       if (nchunks > 0) {
@@ -969,6 +994,8 @@ void chunk_scan_kernel(ScanKArgs a) {
         // every compute wave finished before the barrier that ended the
         // previous step
         if (ci + 1 < nchunks) copy_rec(ci + 1, (ci & 1) ? rec0 : rec1);
+        // the compute waves staged chunk ci-1's outputs before the last barrier
+        if (cpi == 0 && ci > 0) store_tile(ci - 1, otile[(ci - 1) & 1]);
         if (vcopier && ci + 2 < nchunks) {
           copy_v(ci + 2, vring[(ci + 2) % 3]);
           wait_vmcnt<NVD>();           // all but chunk ci+2's values
@@ -977,6 +1004,7 @@ void chunk_scan_kernel(ScanKArgs a) {
         }
         __syncthreads();  // chunk ci done by the compute waves, chunk ci+1 ready
       }
+      if (cpi == 0 && nchunks > 0) store_tile(nchunks - 1, otile[(nchunks - 1) & 1]);
     } else {
       for (int ci = 0; ci < nchunks; ++ci) {
         __syncthreads();  // buffer free
@@ -1162,16 +1190,30 @@ void chunk_scan_kernel(ScanKArgs a) {
     }
   };
 
+  // this wave's outputs into the LDS stage (rows 16I + 4g + r, its columns)
+  auto stage_o = [&](char *ot, f32x4 (*ov)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float x = ov[I][nt][r];
+          *reinterpret_cast<E *>(ot + (16 * I + 4 * g + r) * OROW + (w * VC + 16 * nt + col) * (int)sizeof(E)) =
+              from_f<E>(x);
+        }
+  };
+
   f32x4 ov[4][NT];
   if (NBUF == 2) {
     __syncthreads();  // chunk 0 ready
     for (int ci = 0; ci < nchunks; ci += 2) {
-      if (ci > 0) store_o(ci - 1, ov);
       compute(rec0, vring[ci % NV], ov);
+      stage_o(otile[ci & 1], ov);
       __syncthreads();
       if (ci + 1 >= nchunks) break;
-      store_o(ci, ov);
       compute(rec1, vring[(ci + 1) % NV], ov);
+      stage_o(otile[(ci + 1) & 1], ov);
       __syncthreads();
     }
   } else {
@@ -1181,8 +1223,8 @@ void chunk_scan_kernel(ScanKArgs a) {
       __syncthreads();  // buffer ready
       compute(rec0, vring[ci % NV], ov);
     }
+    if (nchunks > 0) store_o(nchunks - 1, ov);
   }
-  if (nchunks > 0) store_o(nchunks - 1, ov);
 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
