@@ -207,10 +207,12 @@ template <> struct VecOf<16> { typedef f32x4 type; };
 template <> struct VecOf<8> { typedef __attribute__((__vector_size__(8))) float type; };
 
 // LDS image -> record (global), one slot per thread per step, coalesced.
+// Threads t0 .. t0 + nthr - 1 of the workgroup take part.
 template <typename LF>
-__device__ __forceinline__ void copy_out(char *dst, const char *lds) {
+__device__ __forceinline__ void copy_out(char *dst, const char *lds, int t0 = 0, int nthr = kThreads) {
   typedef typename VecOf<LF::SLOT>::type V;
-  for (int s = threadIdx.x; s < LF::NSLOT; s += kThreads)
+  if ((int)threadIdx.x < t0) return;
+  for (int s = threadIdx.x - t0; s < LF::NSLOT; s += nthr)
     *reinterpret_cast<V *>(dst + (size_t)s * LF::SLOT) = *reinterpret_cast<const V *>(lds + LF::rec_slot(s));
 }
 
@@ -239,13 +241,16 @@ template <> struct SlotVec<float, 4> {
   __device__ __forceinline__ static type pack(const float *x) { return f32x4{x[0], x[1], x[2], x[3]}; }
 };
 
-// A 64 x 64 fp32 tile in LDS (row stride LDR), masked to j <= i and scaled per
-// column by colscale (or not), to the record in fragment order, slot by slot.
+// Row tiles I0 .. I1-1 of a 64 x 64 fp32 tile in LDS (row stride LDR), masked
+// to j <= i and scaled per column by colscale (or not), to the record in
+// fragment order, slot by slot, by threads t0 .. t0 + nthr - 1.
 template <typename E, int LDR>
-__device__ __forceinline__ void tile64_out(E *dst, const float *src, const float *colscale) {
+__device__ __forceinline__ void tile64_out(E *dst, const float *src, const float *colscale, int I0 = 0, int I1 = 4,
+                                           int t0 = 0, int nthr = kThreads) {
   typedef FragShape<E, 64> F;
   typedef SlotVec<E, F::KS> SV;
-  for (int s = threadIdx.x; s < 4 * F::NU * 64; s += kThreads) {
+  if ((int)threadIdx.x < t0) return;
+  for (int s = I0 * F::NU * 64 + threadIdx.x - t0; s < I1 * F::NU * 64; s += nthr) {
     const int ts = s >> 6, L = s & 63;
     const int i = 16 * (ts / F::NU) + (L & 15), slab = ts % F::NU, g = L >> 4;
     float x[F::KS];
@@ -681,14 +686,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   __syncthreads();
 
-  if (!exact) {
-    copy_out<LT>(rec + a.lay.ktt, sX);
-  } else {
-    tile64_out<E, LDR>(gA, reinterpret_cast<const float *>(sX), nullptr);
-  }
   if (w == 0 && th == 0) *reinterpret_cast<f32x4 *>(rec + a.lay.p63 + 4 * c0) = f32x4{p63[0], p63[1], p63[2], p63[3]};
 
-  // ---- T = (I + R)^{-1}: diagonal 16x16 blocks by forward substitution.
+  // ---- T = (I + R)^{-1}.  Wave 0 inverts the four diagonal 16x16 blocks by
+  // forward substitution while waves 1-3 copy Kend^T (or A) out; then three
+  // levels of off-diagonal blocks, T_IJ = -T_II sum_K R_IK T_KJ, and the
+  // waves a level leaves idle write the row tiles of Tb = T Diag(beta) whose
+  // blocks are final.
+  E *gTb = reinterpret_cast<E *>(rec + a.lay.tb);
   if (w == 0) {
     const int b = l >> 4, jc = l & 15;
     float X[16];
@@ -701,17 +706,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
 #pragma unroll
     for (int m = 0; m < 16; ++m) sT[(16 * b + m) * LDR + 16 * b + jc] = X[m];
+  } else if (!exact) {
+    copy_out<LT>(rec + a.lay.ktt, sX, 64, kThreads - 64);
+  } else {
+    tile64_out<E, LDR>(gA, reinterpret_cast<const float *>(sX), nullptr, 0, 4, 64, kThreads - 64);
   }
   __syncthreads();
   if (w < 3) inverse_offdiag_block<LDR>(w + 1, w, sR, sT);  // (1,0) (2,1) (3,2)
+  else tile64_out<E, LDR>(gTb, sT, sBeta, 0, 1, 192, 64);     // row tile 0 is final
   __syncthreads();
   if (w < 2) inverse_offdiag_block<LDR>(w + 2, w, sR, sT);  // (2,0) (3,1)
+  else tile64_out<E, LDR>(gTb, sT, sBeta, 1, 2, 128, 128);    // row tile 1
   __syncthreads();
   if (w == 0) inverse_offdiag_block<LDR>(3, 0, sR, sT);     // (3,0)
+  else tile64_out<E, LDR>(gTb, sT, sBeta, 2, 3, 64, 192);     // row tile 2
   __syncthreads();
-
-  // ---- Tb = T Diag(beta), zero above the diagonal, into the record
-  tile64_out<E, LDR>(reinterpret_cast<E *>(rec + a.lay.tb), sT, sBeta);
+  tile64_out<E, LDR>(gTb, sT, sBeta, 3, 4);                   // row tile 3
 }
 
 // ======================================================= kernel 2: chunk scan
