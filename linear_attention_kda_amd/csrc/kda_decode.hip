@@ -30,6 +30,7 @@ struct DecodeKArgs {
   float *S;
   void *o;
   float scale;
+  size_t units;  // sequences x heads
 };
 
 template <typename E>
@@ -74,8 +75,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   constexpr int RPA = 64 / LPR;               // rows per wave-wide KiB access
   constexpr int NI = SH::NI;                  // accesses per wave
 
-  const size_t u = blockIdx.x / SH::SPLIT;    // (sequence, head) unit
-  const int part = blockIdx.x % SH::SPLIT;    // which APW KiB of the unit
+  // the SPLIT workgroups of a unit get ids congruent mod 8, which the
+  // dispatcher sends to one XCD, so k, q and alpha leave HBM once per unit
+  const size_t bid = blockIdx.x, slot = bid >> 3;
+  const size_t u = (slot / SH::SPLIT) * 8 + (bid & 7);   // (sequence, head) unit
+  const int part = (int)(slot % SH::SPLIT);              // which APW KiB of the unit
+  if (u >= a.units) return;
   const int w = wave_id(), l = lane_id();
   const int sub = l % LPR, rsub = l / LPR;
   const int c0 = 4 * sub;
@@ -136,9 +141,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 template <int DK, typename E>
 hipError_t run_decode_dv(const DecodeArgs &a, const DecodeKArgs &ka, hipStream_t s) {
   const size_t units = (size_t)a.N * a.H;
-  if (units * DecodeShape<DK, 128>::SPLIT > 0x7fffffffull) return hipErrorInvalidConfiguration;
+  if ((units + 7) / 8 * 8 * DecodeShape<DK, 128>::SPLIT > 0x7fffffffull) return hipErrorInvalidConfiguration;
 #define KDA_DECODE_LAUNCH(DV) \
-  hipLaunchKernelGGL((decode_kernel<DK, DV, E>), dim3((unsigned)(units * DecodeShape<DK, DV>::SPLIT)), \
+  hipLaunchKernelGGL((decode_kernel<DK, DV, E>), dim3((unsigned)((units + 7) / 8 * 8 * DecodeShape<DK, DV>::SPLIT)), \
                      dim3(kThreads), 0, s, ka)
   switch (a.dv) {
     case 16: KDA_DECODE_LAUNCH(16); break;
@@ -153,7 +158,7 @@ hipError_t run_decode_dv(const DecodeArgs &a, const DecodeKArgs &ka, hipStream_t
 
 template <typename E>
 hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
-  DecodeKArgs ka{a.q, a.k, a.v, a.alpha, a.beta, a.S, a.o, a.scale};
+  DecodeKArgs ka{a.q, a.k, a.v, a.alpha, a.beta, a.S, a.o, a.scale, (size_t)a.N * a.H};
   switch (a.dk) {
     case 16: return run_decode_dv<16, E>(a, ka, s);
     case 32: return run_decode_dv<32, E>(a, ka, s);
