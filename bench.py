@@ -35,8 +35,8 @@ NSETS = 4
 # Each figure belongs to the kernel source with the given sha256 prefix and is
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
-    "prefill": ("kda_prefill.hip", "1c6ecb8efd247916", 479_982_592),
-    "decode": ("kda_decode.hip", "4e709b6268b783a8", 1_089_388_544),
+    "prefill": ("kda_prefill.hip", "fe9c646be16a16b5", 480_342_425),
+    "decode": ("kda_decode.hip", "621875230307cbcf", 1_086_896_844),
 }
 
 
