@@ -49,11 +49,13 @@ def measured_traffic(key):
     return nbytes if cur.startswith(sha) else None
 
 
-def prefill_bytes(B, T, H, dk, dv, esize=2, s0=False):
+def prefill_bytes(B, T, H, dk, dv, esize=2, s0=False, gate_form="channel"):
     """Compulsory HBM bytes of one prefill call: q, k, v, o at their dtype,
-    alpha fp32 per key channel, beta fp32, S_final (and S0) fp32."""
+    alpha fp32 (per key channel, or one per token and head, or none), beta
+    fp32, S_final (and S0) fp32."""
     tok = B * T * H
-    return (tok * (2 * dk + 2 * dv) * esize + tok * dk * 4 + tok * 4
+    alpha = {"channel": tok * dk * 4, "scalar": tok * 4, "none": 0}[gate_form]
+    return (tok * (2 * dk + 2 * dv) * esize + alpha + tok * 4
             + (2 if s0 else 1) * B * H * dv * dk * 4)
 
 
@@ -68,16 +70,21 @@ def decode_bytes(N, H, dk, dv, esize=2):
     return units * (2 * dv * dk * 4 + (2 * dk + 2 * dv) * esize + dk * 4 + 4)
 
 
-def bench_prefill(args, torch, kda, inputs):
+def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None):
     w = inputs.WORKLOADS["prefill"]
     B, T, H, dk, dv = w["B"], w["T"], w["H"], w["dk"], w["dv"]
+    steps = steps or args.steps
     dev = torch.device("cuda:0")
     sets = []
     # one workspace, as a caller running layer after layer would hold
     ws = torch.empty(kda.chunk_fwd_workspace_size(B, T, H, dk, dv, -1, kda.KDA_BF16),
                      dtype=torch.uint8, device=dev)
     for s in range(NSETS):
-        inp = inputs.workload("prefill", seed=s, device=dev)
+        if gate_form == "channel":
+            inp = inputs.workload("prefill", seed=s, device=dev)
+        else:
+            inp = inputs.dense(B, T, H, dk, dv, w["dtype"], w["gate"], seed=s, device=dev,
+                               gate_form=gate_form)
         o = torch.empty_like(inp["v"])
         S = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
         sets.append((inp, ws, o, S))
@@ -85,7 +92,7 @@ def bench_prefill(args, torch, kda, inputs):
 
     def step(i):
         inp, ws, o, S = sets[i % NSETS]
-        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], out=o,
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], gate=gate_form, out=o,
                       S_final=S, workspace=ws)
 
     for i in range(args.warmup):
@@ -93,10 +100,10 @@ def bench_prefill(args, torch, kda, inputs):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
+          for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         ev[i][0].record(stream)
         step(i)
         ev[i][1].record(stream)
@@ -104,7 +111,7 @@ def bench_prefill(args, torch, kda, inputs):
     wall = time.perf_counter() - t0
     call_ms = sorted(a.elapsed_time(b) for a, b in ev)
     mean_ms = sum(call_ms) / len(call_ms)
-    return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=wall, ms_per_step=wall * 1e3 / args.steps,
+    return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=wall, ms_per_step=wall * 1e3 / steps,
                 call_ms_mean=mean_ms, call_ms_median=call_ms[len(call_ms) // 2],
                 call_ms_min=call_ms[0], tokens=B * T)
 
@@ -191,6 +198,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-gate-forms", action="store_true",
+                    help="skip the scalar-gate prefill line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
@@ -236,6 +245,17 @@ def main():
     }
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, kda, inputs)
+    if not args.no_gate_forms:
+        # the same workload with one gate per (token, head) (Gated DeltaNet form)
+        sg = bench_prefill(args, torch, kda, inputs, gate_form="scalar", steps=max(20, args.steps // 4))
+        sb = prefill_bytes(sg["B"], sg["T"], sg["H"], sg["dk"], sg["dv"], gate_form="scalar")
+        ach = sb / (sg["call_ms_mean"] * 1e-3) / 1e9
+        result["prefill_scalar_gate"] = {
+            "workload": "prefill B=4 H=16 T=2048 d=128 bf16, one fp32 gate per (token, head)",
+            "tokens_per_s": round(sg["tokens"] / (sg["ms_per_step"] * 1e-3), 1),
+            "call_us_mean": round(sg["call_ms_mean"] * 1e3, 2),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": sb}}
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)

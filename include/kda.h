@@ -58,10 +58,24 @@ typedef enum {
   KDA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the query result */
   KDA_ERR_VARLEN_REQUIRES_B1 = 7,  /* cu_seqlens given with B != 1           */
   KDA_ERR_ALIAS = 8,               /* o overlaps an input                    */
-  KDA_ERR_HIP = 9                  /* the HIP runtime reported an error      */
+  KDA_ERR_HIP = 9,                 /* the HIP runtime reported an error      */
+  KDA_ERR_UNSUPPORTED_GATE = 10    /* gate is not a kda_gate value           */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * How the forget gate is given.  Page "Kimi Delta Attention (KDA)": section
+ * "KDA: a separate gate for each key channel" gives one gate per key channel;
+ * section "Gated DeltaNet: ..." gives one scalar gate per token that scales
+ * the whole state; section "DeltaNet: ..." has no gate.  The scalar form is
+ * the per-channel form with the same value on every channel, and no gate is
+ * the per-channel form with every value 1.
+ *   KDA_GATE_CHANNEL  alpha [..., d_k] fp32, one value per key channel
+ *   KDA_GATE_SCALAR   alpha [...]      fp32, one value per token and head
+ *   KDA_GATE_NONE     no forgetting; alpha is not read and may be NULL
+ */
+typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_SCALAR = 1, KDA_GATE_NONE = 2 } kda_gate;
 
 /* Text for a status code (static storage; never NULL). */
 const char *kda_status_string(kda_status s);
@@ -108,6 +122,21 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          hipStream_t stream);
 
 /*
+ * kda_chunk_fwd with the gate given as `gate` (see kda_gate): alpha is
+ * [B, T, H, d_k] for KDA_GATE_CHANNEL (then this is kda_chunk_fwd),
+ * [B, T, H] for KDA_GATE_SCALAR, and unused (may be NULL) for KDA_GATE_NONE.
+ * Everything else as for kda_chunk_fwd; an unknown gate returns
+ * KDA_ERR_UNSUPPORTED_GATE.
+ */
+kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v,
+                               const float *alpha, kda_gate gate, const float *beta,
+                               const float *S0, const int32_t *cu_seqlens, int N,
+                               int B, int T, int H, int d_k, int d_v, float scale,
+                               kda_dtype dtype, void *o, float *S_final,
+                               void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * One decode step for N independent sequences (page "Kimi Delta Attention
  * (KDA)", section "Two schedules for one recurrence", the fused recurrent
  * schedule): every (n, h) state takes one token and is updated in place.
@@ -122,6 +151,17 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
                            const float *alpha, const float *beta, float *S,
                            int N, int H, int d_k, int d_v, float scale,
                            kda_dtype dtype, void *o, hipStream_t stream);
+
+/*
+ * kda_decode_step with the gate given as `gate`: alpha is [N, H, d_k] for
+ * KDA_GATE_CHANNEL, [N, H] for KDA_GATE_SCALAR, unused (may be NULL) for
+ * KDA_GATE_NONE.  An unknown gate returns KDA_ERR_UNSUPPORTED_GATE.
+ */
+kda_status kda_decode_step_gated(const void *q, const void *k, const void *v,
+                                 const float *alpha, kda_gate gate,
+                                 const float *beta, float *S, int N, int H,
+                                 int d_k, int d_v, float scale, kda_dtype dtype,
+                                 void *o, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -17,9 +17,16 @@ LIB_PATH = os.path.join(PKG_DIR, "libkda.so")
 KDA_F32 = 0
 KDA_BF16 = 1
 
+# forget-gate forms (kda_gate): one gate per key channel, one per token and
+# head shared by all channels, or none
+KDA_GATE_CHANNEL = 0
+KDA_GATE_SCALAR = 1
+KDA_GATE_NONE = 2
+GATES = {"channel": KDA_GATE_CHANNEL, "scalar": KDA_GATE_SCALAR, "none": KDA_GATE_NONE}
+
 # names exported by include/kda.h
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
-            "kda_decode_step")
+            "kda_chunk_fwd_gated", "kda_decode_step", "kda_decode_step_gated")
 
 
 class KdaError(RuntimeError):
@@ -44,8 +51,13 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = i32
     lib.kda_chunk_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                   f32, i32, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_gated.restype = i32
+    lib.kda_chunk_fwd_gated.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                        f32, i32, vp, vp, vp, sz, vp]
     lib.kda_decode_step.restype = i32
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.kda_decode_step_gated.restype = i32
+    lib.kda_decode_step_gated.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
     return lib
 
 
@@ -85,26 +97,42 @@ def _dtype_code(t) -> int:
     raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
 
 
+def _gate_code(gate, alpha, q):
+    """kda_gate code: given by name, else read from alpha's shape."""
+    if gate is None:
+        if alpha is None:
+            return KDA_GATE_NONE
+        return KDA_GATE_SCALAR if alpha.dim() == q.dim() - 1 else KDA_GATE_CHANNEL
+    if gate not in GATES:
+        raise ValueError(f"gate must be one of {sorted(GATES)}, got {gate!r}")
+    return GATES[gate]
+
+
 def _stream(device):
     import torch
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, out=None,
+def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gate=None, out=None,
               S_final=None, workspace=None):
     """Chunked prefill.  Returns (o, S_final).
 
-    Dense batch: q, k, alpha [B, T, H, d_k]; v [B, T, H, d_v]; beta [B, T, H].
+    Dense batch: q, k [B, T, H, d_k]; v [B, T, H, d_v]; beta [B, T, H].
+    alpha: [B, T, H, d_k] (gate "channel"), [B, T, H] (gate "scalar"), or
+    None (gate "none"); ``gate`` defaults to what alpha's shape says.
     Packed batch: pass ``cu_seqlens`` (int32, device, N+1 offsets) and tensors
     with a packed token axis, [T, H, d] or [1, T, H, d].
     S0: [N, H, d_v, d_k] fp32 or None.  ``S_final`` may be ``S0`` (in place).
     """
     import torch
     dt = _dtype_code(q)
+    gc = _gate_code(gate, alpha, q)
+    if gc == KDA_GATE_NONE:
+        alpha = None
     q, k, v, alpha, beta = map(_prep, (q, k, v, alpha, beta))
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must share one dtype")
-    if alpha.dtype != torch.float32 or beta.dtype != torch.float32:
+    if (alpha is not None and alpha.dtype != torch.float32) or beta.dtype != torch.float32:
         raise TypeError("alpha and beta must be float32")
     d_k, d_v, H = q.shape[-1], v.shape[-1], q.shape[-2]
     if cu_seqlens is not None:
@@ -118,8 +146,12 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, out
             raise ValueError("dense q must be [B, T, H, d_k]")
         B, T = q.shape[0], q.shape[1]
         N = B
-    if k.shape != q.shape or alpha.shape != q.shape:
-        raise ValueError("k and alpha must have the shape of q")
+    if k.shape != q.shape:
+        raise ValueError("k must have the shape of q")
+    if gc == KDA_GATE_CHANNEL and alpha.shape != q.shape:
+        raise ValueError("per-channel alpha must have the shape of q")
+    if gc == KDA_GATE_SCALAR and alpha.numel() != B * T * H:
+        raise ValueError("scalar alpha must have one value per token and head")
     if v.numel() != B * T * H * d_v or beta.numel() != B * T * H:
         raise ValueError("v / beta sizes do not match q")
     if S0 is not None:
@@ -136,20 +168,24 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, out
     ws_need = chunk_fwd_workspace_size(B, T, H, d_k, d_v, N if cu_seqlens is not None else -1, dt)
     if workspace is None or workspace.numel() < ws_need:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
-    st = lib.kda_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S0),
-                           _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
-                           float(scale) if scale else 0.0, dt, _ptr(out), _ptr(S_final),
-                           _ptr(workspace), workspace.numel(), _stream(dev))
+    st = lib.kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), _ptr(S0),
+                                 _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
+                                 float(scale) if scale else 0.0, dt, _ptr(out), _ptr(S_final),
+                                 _ptr(workspace), workspace.numel(), _stream(dev))
     if st != 0:
-        raise KdaError("kda_chunk_fwd", st)
+        raise KdaError("kda_chunk_fwd_gated", st)
     return out, S_final
 
 
-def decode_step(q, k, v, alpha, beta, S, scale=None, *, out=None):
-    """One token for N sequences: q, k, alpha [N, H, d_k]; v [N, H, d_v];
-    beta [N, H]; S [N, H, d_v, d_k] fp32, updated in place.  Returns o."""
+def decode_step(q, k, v, alpha, beta, S, scale=None, *, gate=None, out=None):
+    """One token for N sequences: q, k [N, H, d_k]; v [N, H, d_v]; beta [N, H];
+    alpha [N, H, d_k] (gate "channel"), [N, H] ("scalar") or None ("none");
+    S [N, H, d_v, d_k] fp32, updated in place.  Returns o."""
     import torch
     dt = _dtype_code(q)
+    gc = _gate_code(gate, alpha, q)
+    if gc == KDA_GATE_NONE:
+        alpha = None
     if not S.is_contiguous() or S.dtype != torch.float32 or S.data_ptr() % 16:
         raise ValueError("S must be a contiguous, 16-byte aligned float32 tensor (updated in place)")
     q, k, v, alpha, beta = map(_prep, (q, k, v, alpha, beta))
@@ -157,11 +193,15 @@ def decode_step(q, k, v, alpha, beta, S, scale=None, *, out=None):
     d_v = v.shape[-1]
     if S.shape != (N, H, d_v, d_k):
         raise ValueError("S must be [N, H, d_v, d_k]")
+    if gc == KDA_GATE_CHANNEL and alpha.shape != q.shape:
+        raise ValueError("per-channel alpha must be [N, H, d_k]")
+    if gc == KDA_GATE_SCALAR and alpha.numel() != N * H:
+        raise ValueError("scalar alpha must be [N, H]")
     if out is None:
         out = torch.empty((N, H, d_v), dtype=v.dtype, device=q.device)
-    st = lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(S), N, H,
-                             d_k, d_v, float(scale) if scale else 0.0, dt, _ptr(out),
-                             _stream(q.device))
+    st = lib.kda_decode_step_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), _ptr(S),
+                                   N, H, d_k, d_v, float(scale) if scale else 0.0, dt, _ptr(out),
+                                   _stream(q.device))
     if st != 0:
-        raise KdaError("kda_decode_step", st)
+        raise KdaError("kda_decode_step_gated", st)
     return out

@@ -45,6 +45,7 @@ const char *kda_status_string(kda_status s) {
     case KDA_ERR_VARLEN_REQUIRES_B1: return "cu_seqlens requires B == 1";
     case KDA_ERR_ALIAS: return "the output overlaps an input";
     case KDA_ERR_HIP: return "the HIP runtime reported an error";
+    case KDA_ERR_UNSUPPORTED_GATE: return "gate must be KDA_GATE_CHANNEL, KDA_GATE_SCALAR or KDA_GATE_NONE";
   }
   return "unknown status";
 }
@@ -65,6 +66,15 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
                          const float *S0, const int32_t *cu_seqlens, int N, int B, int T, int H, int d_k,
                          int d_v, float scale, kda_dtype dtype, void *o, float *S_final, void *workspace,
                          size_t workspace_bytes, hipStream_t stream) {
+  return kda_chunk_fwd_gated(q, k, v, alpha, KDA_GATE_CHANNEL, beta, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale,
+                             dtype, o, S_final, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                               const float *beta, const float *S0, const int32_t *cu_seqlens, int N, int B, int T,
+                               int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o, float *S_final,
+                               void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_SCALAR && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED_GATE;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
   if (B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
@@ -78,9 +88,12 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
   const size_t es = dtype == KDA_BF16 ? 2 : 4;
   const size_t ntok = (size_t)B * T;
   const size_t qk_bytes = ntok * H * d_k * es, v_bytes = ntok * H * d_v * es;
-  const size_t a_bytes = ntok * H * d_k * sizeof(float), b_bytes = ntok * H * sizeof(float);
+  const size_t a_bytes = gate == KDA_GATE_CHANNEL ? ntok * H * d_k * sizeof(float)
+                         : gate == KDA_GATE_SCALAR ? ntok * H * sizeof(float) : 0;
+  const size_t b_bytes = ntok * H * sizeof(float);
   const size_t s_bytes = (size_t)N * H * d_v * d_k * sizeof(float);
-  if (ntok > 0 && (!q || !k || !v || !alpha || !beta || !o)) return KDA_ERR_NULL_ARG;
+  if (gate == KDA_GATE_NONE) alpha = nullptr;
+  if (ntok > 0 && (!q || !k || !v || (a_bytes && !alpha) || !beta || !o)) return KDA_ERR_NULL_ARG;
   if (s_bytes > 0 && !S_final) return KDA_ERR_NULL_ARG;
   if (ntok > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
   const void *ptrs[] = {q, k, v, alpha, beta, S0, cu_seqlens, o, S_final, workspace};
@@ -93,7 +106,7 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
   if (ntok > 0) {
     const Range ro = range_of(o, ntok * H * d_v * es);
     const Range ins[] = {range_of(q, qk_bytes), range_of(k, qk_bytes), range_of(v, v_bytes),
-                         range_of(alpha, a_bytes), range_of(beta, b_bytes),
+                         range_of(alpha, alpha ? a_bytes : 0), range_of(beta, b_bytes),
                          range_of(S0, S0 ? s_bytes : 0), range_of(S_final, s_bytes),
                          range_of(workspace, plan.total)};
     for (const Range &r : ins)
@@ -106,6 +119,7 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
   a.k = k;
   a.v = v;
   a.alpha = alpha;
+  a.gate = (int)gate;
   a.beta = beta;
   a.S0 = S0;
   a.cu_seqlens = cu_seqlens;
@@ -126,20 +140,30 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v, const floa
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *alpha, const float *beta,
                            float *S, int N, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
                            hipStream_t stream) {
+  return kda_decode_step_gated(q, k, v, alpha, KDA_GATE_CHANNEL, beta, S, N, H, d_k, d_v, scale, dtype, o, stream);
+}
+
+kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                                 const float *beta, float *S, int N, int H, int d_k, int d_v, float scale,
+                                 kda_dtype dtype, void *o, hipStream_t stream) {
+  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_SCALAR && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED_GATE;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
   if (N < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
   const size_t units = (size_t)N * H;
   if (units == 0) return KDA_OK;
-  if (!q || !k || !v || !alpha || !beta || !S || !o) return KDA_ERR_NULL_ARG;
+  if (gate == KDA_GATE_NONE) alpha = nullptr;
+  if (!q || !k || !v || (gate != KDA_GATE_NONE && !alpha) || !beta || !S || !o) return KDA_ERR_NULL_ARG;
   const void *ptrs[] = {q, k, v, alpha, beta, S, o};
   for (const void *p : ptrs)
-    if (!aligned16(p)) return KDA_ERR_MISALIGNED;
+    if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+  const size_t a_bytes = gate == KDA_GATE_CHANNEL ? units * d_k * sizeof(float)
+                         : gate == KDA_GATE_SCALAR ? units * sizeof(float) : 0;
   if (units > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
   const size_t es = dtype == KDA_BF16 ? 2 : 4;
   const Range ro = range_of(o, units * d_v * es);
   const Range ins[] = {range_of(q, units * d_k * es), range_of(k, units * d_k * es),
-                       range_of(v, units * d_v * es), range_of(alpha, units * d_k * sizeof(float)),
+                       range_of(v, units * d_v * es), range_of(alpha, alpha ? a_bytes : 0),
                        range_of(beta, units * sizeof(float)), range_of(S, units * d_v * d_k * sizeof(float))};
   for (const Range &r : ins)
     if (overlaps(ro, r)) return KDA_ERR_ALIAS;
@@ -149,6 +173,7 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
   a.k = k;
   a.v = v;
   a.alpha = alpha;
+  a.gate = (int)gate;
   a.beta = beta;
   a.S = S;
   a.o = o;

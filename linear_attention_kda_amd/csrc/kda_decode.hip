@@ -27,6 +27,7 @@ namespace {
 struct DecodeKArgs {
   const void *q, *k, *v;
   const float *alpha, *beta;
+  int gate;  // kGateChannel: alpha [N, H, d_k]; kGateScalar: alpha [N, H]; kGateNone: unused
   float *S;
   void *o;
   float scale;
@@ -88,7 +89,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   float kk[4], qq[4], al[4];
   load4<E>(reinterpret_cast<const E *>(a.k) + u * DK + c0, kk);
   load4<E>(reinterpret_cast<const E *>(a.q) + u * DK + c0, qq);
-  load4<float>(a.alpha + u * DK + c0, al);
+  if (a.gate == kGateChannel) {
+    load4<float>(a.alpha + u * DK + c0, al);
+  } else {
+    const float x = a.gate == kGateScalar ? a.alpha[u] : 1.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) al[j] = x;
+  }
   const float beta = a.beta[u];
   const E *vrow = reinterpret_cast<const E *>(a.v) + u * DV;
   E *orow = reinterpret_cast<E *>(a.o) + u * DV;
@@ -158,7 +165,7 @@ hipError_t run_decode_dv(const DecodeArgs &a, const DecodeKArgs &ka, hipStream_t
 
 template <typename E>
 hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
-  DecodeKArgs ka{a.q, a.k, a.v, a.alpha, a.beta, a.S, a.o, a.scale, (size_t)a.N * a.H};
+  DecodeKArgs ka{a.q, a.k, a.v, a.alpha, a.beta, a.gate, a.S, a.o, a.scale, (size_t)a.N * a.H};
   switch (a.dk) {
     case 16: return run_decode_dv<16, E>(a, ka, s);
     case 32: return run_decode_dv<32, E>(a, ka, s);

@@ -73,9 +73,13 @@ inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
   return P;
 }
 
+// gate kinds (kda_gate): 0 per key channel, 1 one per token and head, 2 none
+constexpr int kGateChannel = 0, kGateScalar = 1, kGateNone = 2;
+
 struct PrefillArgs {
   const void *q, *k, *v;
   const float *alpha, *beta, *S0;
+  int gate;
   const int32_t *cu_seqlens;  // device, or null for a dense batch
   void *o;
   float *S_final;
@@ -91,6 +95,7 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 struct DecodeArgs {
   const void *q, *k, *v;
   const float *alpha, *beta;
+  int gate;
   float *S;
   void *o;
   int N, H, dk, dv;

@@ -161,6 +161,7 @@ __device__ __forceinline__ int frag_index(int i, int c) {
 struct PrepKArgs {
   const void *q, *k;
   const float *alpha, *beta;
+  int gate;  // kGateChannel: alpha [.., H, d_k]; kGateScalar: alpha [.., H]; kGateNone: unused
   ChunkSource src;
   int H;
   float scale;
@@ -349,7 +350,7 @@ __device__ __forceinline__ void tile_ij(int p, int &I, int &J) {
 // Exact path (a chunk with some D_{0:63} below 2^-100, e.g. a gate of 0):
 // no division at all.  Kbnd and Qbnd as above, Kend from suffix products, and
 // R and A summed channel by channel with running products of the gates.
-template <int DK, typename E>
+template <int DK, typename E, int GATE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrepKArgs a) {
   typedef LdsFrag<E, DK, 64> LK;   // Kbnd, Qbnd, k / a: rows = tokens, K = d_k
   typedef LdsFrag<E, 64, DK> LT;   // Kend^T: rows = channels, K = tokens
@@ -380,6 +381,22 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const E *k = reinterpret_cast<const E *>(a.k);
   const size_t hs = (size_t)a.H * DK;  // token stride of q, k, alpha
   const size_t base = (size_t)t0 * hs + (size_t)h * DK + c0;
+  // gates of channels ch0 .. ch0+3 of token t0 + tk (tk a valid chunk index):
+  // per channel, one shared value, or none (see kda_gate)
+  auto gate4 = [&](int tk, int ch0, float *al, bool nontemporal) {
+    const size_t tok = (size_t)t0 + tk;
+    if constexpr (GATE == kGateChannel) {
+      const f32x4 *p = reinterpret_cast<const f32x4 *>(a.alpha + tok * hs + (size_t)h * DK + ch0);
+      const f32x4 x = nontemporal ? __builtin_nontemporal_load(p) : *p;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) al[j] = x[j];
+    } else {
+      float x = 1.f;
+      if constexpr (GATE == kGateScalar) x = a.alpha[tok * a.H + h];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) al[j] = x;
+    }
+  };
   char *sKh = arena, *sQh = arena + LK::BYTES, *sKd = arena + 2 * LK::BYTES;
   float *sR = reinterpret_cast<float *>(arena);
   float *sT = reinterpret_cast<float *>(arena + RT_BYTES);
@@ -404,11 +421,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const bool live = tok < L;
     const size_t off = base + (size_t)min(tok, L - 1) * hs;
     float al[4];
-    {
-      const f32x4 av = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.alpha + off));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = av[j];
-    }
+    gate4(min(tok, L - 1), c0, al, true);
     kraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(k + off));
     qraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(q + off));
 #pragma unroll
@@ -523,7 +536,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     for (int u = TPL - 1; u >= 0; --u) {
       const int tok = tb0 + u;
       float al[4];
-      Four<float>::load(a.alpha + base + (size_t)min(tok, L - 1) * hs, al);
+      gate4(min(tok, L - 1), c0, al, false);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         sfx[u][j] = run[j];
@@ -654,7 +667,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
       for (int cc = 0; cc < CQ; cc += 4) {
         float al[4], kx[4], qx[4];
-        Four<float>::load(a.alpha + off + cc, al);
+        gate4(min(i, L - 1), qd * CQ + cc, al, false);
         F4::load(k + off + cc, kx);
         F4::load(q + off + cc, qx);
 #pragma unroll
@@ -1281,6 +1294,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.q = a.q;
     pa.k = a.k;
     pa.alpha = a.alpha;
+    pa.gate = a.gate;
     pa.beta = a.beta;
     pa.src.T = a.T;
     pa.src.nct = nct;
@@ -1292,8 +1306,13 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.scale = a.scale;
     pa.ws_records = records;
     pa.lay = lay;
-    hipLaunchKernelGGL((chunk_prep_kernel<DK, E>), dim3((unsigned)P.max_chunks, a.H), dim3(kThreads), 0, stream,
-                       pa);
+    const dim3 pg((unsigned)P.max_chunks, a.H);
+    if (a.gate == kGateScalar)
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar>), pg, dim3(kThreads), 0, stream, pa);
+    else if (a.gate == kGateNone)
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone>), pg, dim3(kThreads), 0, stream, pa);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel>), pg, dim3(kThreads), 0, stream, pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -53,19 +53,35 @@ def _gate(shape, gen, device, gate: str, alpha_lo: float = 0.9) -> torch.Tensor:
     return torch.exp(-torch.nn.functional.softplus(g))
 
 
+def _gate_shape(lead, dk, gate_form):
+    """alpha's shape for a gate form: one value per key channel, one per token
+    and head, or none at all."""
+    if gate_form == "channel":
+        return (*lead, dk)
+    if gate_form == "scalar":
+        return tuple(lead)
+    if gate_form == "none":
+        return None
+    raise ValueError(gate_form)
+
+
 def dense(B, T, H, dk, dv, dtype=torch.bfloat16, gate="softplus", alpha_lo=0.9,
-          s0_std=None, seed=0, device="cpu"):
-    """A dense [B, T, H, .] batch.  Returns a dict of tensors on `device`."""
+          s0_std=None, seed=0, device="cpu", gate_form="channel"):
+    """A dense [B, T, H, .] batch.  Returns a dict of tensors on `device`.
+    gate_form "scalar" draws one gate per (token, head), "none" returns
+    alpha = None; the draws of the other tensors do not change."""
     gen = torch.Generator(device=device).manual_seed(seed)
     q = torch.empty((B, T, H, dk), device=device).normal_(generator=gen)
     k = _unit(torch.empty((B, T, H, dk), device=device).normal_(generator=gen))
     v = torch.empty((B, T, H, dv), device=device).normal_(generator=gen)
-    alpha = _gate((B, T, H, dk), gen, device, gate, alpha_lo)
+    shape = _gate_shape((B, T, H), dk, gate_form)
+    alpha = _gate(shape, gen, device, gate, alpha_lo) if shape is not None else None
     beta = torch.sigmoid(torch.empty((B, T, H), device=device).normal_(generator=gen))
     S0 = None
     if s0_std is not None:
         S0 = torch.empty((B, H, dv, dk), device=device).normal_(0.0, s0_std, generator=gen)
-    return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), alpha=alpha.contiguous(),
+    return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype),
+                alpha=alpha.contiguous() if alpha is not None else None,
                 beta=beta.contiguous(), S0=S0)
 
 
@@ -76,8 +92,9 @@ def packed_lengths(n_seq, mu, sigma, lo, hi, seed=0, device="cpu"):
 
 
 def packed(lengths, H, dk, dv, dtype=torch.bfloat16, gate="softplus", s0_std=0.02,
-           stress=False, gen=None, seed=0, device="cpu"):
-    """A packed batch of sequences with the given lengths (list or tensor)."""
+           stress=False, gen=None, seed=0, device="cpu", gate_form="channel"):
+    """A packed batch of sequences with the given lengths (list or tensor).
+    gate_form as for dense(); the stress mix applies to per-channel gates."""
     if gen is None:
         gen = torch.Generator(device=device).manual_seed(seed)
     lengths = torch.as_tensor(lengths, dtype=torch.int64).cpu()
@@ -88,16 +105,18 @@ def packed(lengths, H, dk, dv, dtype=torch.bfloat16, gate="softplus", s0_std=0.0
     q = torch.empty((T, H, dk), device=device).normal_(generator=gen)
     k = _unit(torch.empty((T, H, dk), device=device).normal_(generator=gen))
     v = torch.empty((T, H, dv), device=device).normal_(generator=gen)
-    alpha = _gate((T, H, dk), gen, device, gate)
+    shape = _gate_shape((T, H), dk, gate_form)
+    alpha = _gate(shape, gen, device, gate) if shape is not None else None
     beta = torch.sigmoid(torch.empty((T, H), device=device).normal_(generator=gen))
-    if stress:
+    if stress and alpha is not None and gate_form == "channel":
         q4 = H // 4
         alpha[:, :q4] = torch.empty((T, q4, dk), device=device).uniform_(0.999, 1.0, generator=gen)
         beta[:, q4:2 * q4] = 1.0
     S0 = None
     if s0_std is not None:
         S0 = torch.empty((N, H, dv, dk), device=device).normal_(0.0, s0_std, generator=gen)
-    return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), alpha=alpha.contiguous(),
+    return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype),
+                alpha=alpha.contiguous() if alpha is not None else None,
                 beta=beta.contiguous(), S0=S0,
                 cu_seqlens=cu.to(torch.int32).to(device), lengths=lengths)
 

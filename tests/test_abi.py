@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(kda):
 
 
 def test_status_strings(kda):
-    for s in range(10):
+    for s in range(11):
         assert kda.status_string(s) and kda.status_string(s) != "unknown status"
     assert kda.status_string(99) == "unknown status"
 
@@ -99,3 +99,42 @@ def test_decode_validation(kda):
     assert call(S=None) == 1
     assert call(beta=P(0x50008)) == 5
     assert call(o=P(0x60000)) == 8                   # o aliases S
+
+
+def _fwd_gated(kda, gate, **kw):
+    P = lambda a: ctypes.c_void_p(a)
+    args = dict(q=P(0x10000), k=P(0x20000), v=P(0x30000), alpha=P(0x40000), beta=P(0x50000),
+                S0=None, cu=None, N=2, B=2, T=8, H=2, dk=16, dv=16, scale=0.0, dt=kda.KDA_BF16,
+                o=P(0x60000), S_final=P(0x70000), ws=P(0x80000), ws_bytes=1 << 30, stream=None)
+    args.update(kw)
+    return kda.lib.kda_chunk_fwd_gated(args["q"], args["k"], args["v"], args["alpha"], gate, args["beta"],
+                                       args["S0"], args["cu"], args["N"], args["B"], args["T"], args["H"],
+                                       args["dk"], args["dv"], args["scale"], args["dt"], args["o"],
+                                       args["S_final"], args["ws"], args["ws_bytes"], args["stream"])
+
+
+def test_gated_validation(kda):
+    P = ctypes.c_void_p
+    assert _fwd_gated(kda, 3) == 10                           # unknown gate
+    assert _fwd_gated(kda, -1) == 10
+    assert _fwd_gated(kda, kda.KDA_GATE_SCALAR, alpha=None) == 1   # scalar gates need alpha
+    assert _fwd_gated(kda, kda.KDA_GATE_CHANNEL, alpha=None) == 1
+    assert _fwd_gated(kda, kda.KDA_GATE_SCALAR, alpha=P(0x40004)) == 5
+    # no gate: alpha is not read, so NULL or a misaligned value are both fine;
+    # the call then fails later on the deliberately bad shape
+    assert _fwd_gated(kda, kda.KDA_GATE_NONE, alpha=None, H=0) == 2
+    assert _fwd_gated(kda, kda.KDA_GATE_NONE, alpha=P(0x40004), dk=48) == 3
+    # a scalar alpha covers B*T*H floats, a per-channel one B*T*H*d_k: o placed
+    # inside the per-channel extent aliases only that form
+    assert _fwd_gated(kda, kda.KDA_GATE_CHANNEL, o=P(0x40000 + 256)) == 8
+    # decode
+    good = dict(q=P(0x10000), k=P(0x20000), v=P(0x30000), beta=P(0x50000), S=P(0x60000), o=P(0x90000))
+
+    def dec(gate, alpha, **kw):
+        a = dict(good, **kw)
+        return kda.lib.kda_decode_step_gated(a["q"], a["k"], a["v"], alpha, gate, a["beta"], a["S"], 2, 2,
+                                             16, 16, 0.0, kda.KDA_F32, a["o"], None)
+    assert dec(7, P(0x40000)) == 10
+    assert dec(kda.KDA_GATE_SCALAR, None) == 1
+    assert dec(kda.KDA_GATE_CHANNEL, P(0x40008)) == 5
+    assert dec(kda.KDA_GATE_NONE, None, o=P(0x60000)) == 8   # o aliases S, alpha unused
