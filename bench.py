@@ -116,6 +116,54 @@ def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None):
                 call_ms_min=call_ms[0], tokens=B * T)
 
 
+def decode_tokens_bytes(N, H, dk, dv, Tk, esize=2):
+    """One multi-token launch: the state is read and written once, each of the
+    Tk tokens brings its q, k, v, alpha, beta and writes its output row."""
+    units = N * H
+    return units * (2 * dv * dk * 4 + Tk * ((2 * dk + 2 * dv) * esize + dk * 4 + 4))
+
+
+def bench_decode_tokens(args, torch, kda, inputs, Tk=4):
+    """Draft verification: Tk tokens per sequence per launch over the decode
+    workload's state, the same 1024 tokens per sequence as the decode line."""
+    w = inputs.WORKLOADS["decode"]
+    N, H, dk, dv = w["N"], w["H"], w["dk"], w["dv"]
+    launches = max(1, args.decode_steps // Tk)
+    dev = torch.device("cuda:0")
+    S = inputs.decode_state(N, H, dk, dv, w["s0_std"], seed=0, device=dev)
+    blocks = []                      # 32 distinct input blocks (1.3 GiB), cycled
+    for b in range(min(32, launches)):
+        toks = [inputs.decode_token(N, H, dk, dv, w["dtype"], w["alpha_lo"], step=b * Tk + t, device=dev)
+                for t in range(Tk)]
+        blocks.append({key: torch.stack([t[key] for t in toks], 1).contiguous() for key in toks[0]})
+    o = torch.empty((N, Tk, H, dv), dtype=w["dtype"], device=dev)
+    S_w = S.clone()
+    for b in range(min(4, launches)):
+        t = blocks[b % len(blocks)]
+        kda.decode_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S_w, S_out=S_w, out=o)
+    del S_w
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for b in range(launches):
+        t = blocks[b % len(blocks)]
+        kda.decode_tokens(t["q"], t["k"], t["v"], t["alpha"], t["beta"], S, S_out=S, out=o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    launch_us = total_ms * 1e3 / launches
+    nbytes = decode_tokens_bytes(N, H, dk, dv, Tk)
+    achieved = nbytes / (launch_us * 1e-6) / 1e9
+    return {"workload": f"decode_tokens N={N} H={H} d_k=d_v={dk} bf16, Tk={Tk} tokens per launch, "
+                        f"fp32 state {N * H * dv * dk * 4 >> 20} MiB updated in place",
+            "launches": launches, "tokens_per_s": N * Tk * launches / (total_ms * 1e-3),
+            "us_per_launch": launch_us,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "bytes_per_launch": nbytes}}
+
+
 def bench_decode(args, torch, kda, inputs):
     w = inputs.WORKLOADS["decode"]
     N, H, dk, dv, steps = w["N"], w["H"], w["dk"], w["dv"], args.decode_steps
@@ -245,6 +293,7 @@ def main():
     }
     if not args.no_decode:
         result["decode"] = bench_decode(args, torch, kda, inputs)
+        result["decode_tokens"] = bench_decode_tokens(args, torch, kda, inputs)
     if not args.no_gate_forms:
         # the same workload with one gate per (token, head) (Gated DeltaNet form)
         sg = bench_prefill(args, torch, kda, inputs, gate_form="scalar", steps=max(20, args.steps // 4))

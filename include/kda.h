@@ -163,6 +163,32 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v,
                                  int d_k, int d_v, float scale, kda_dtype dtype,
                                  void *o, hipStream_t stream);
 
+/*
+ * Several tokens per sequence in one launch, taken in order by the
+ * token-by-token schedule, for verifying a draft of speculative decoding
+ * (page "K3 架构图解", chapter 10: a draft model proposes tokens, the target
+ * model verifies them together, and the recurrent state has to be kept
+ * where a rejected token can be undone).  Each (n, h) state is read from
+ * S_in once, carried through its Tk tokens in registers, and written to
+ * S_out once.  With S_out a different buffer, S_in stays the checkpoint to
+ * roll back to (run again on the accepted prefix); S_out == S_in updates in
+ * place.  Tk = 0 copies S_in to S_out.
+ *
+ *  q, k     [N, Tk, H, d_k]  dtype     v [N, Tk, H, d_v]  dtype
+ *  alpha    [N, Tk, H, d_k] (KDA_GATE_CHANNEL), [N, Tk, H] (KDA_GATE_SCALAR),
+ *           unused (KDA_GATE_NONE)    beta [N, Tk, H]  fp32
+ *  S_in, S_out [N, H, d_v, d_k] fp32: the same buffer or disjoint ones
+ *           (a partial overlap returns KDA_ERR_ALIAS)
+ *  o        [N, Tk, H, d_v]  dtype     must not overlap an input or a state
+ *  scale    <= 0 selects d_k^{-1/2}
+ */
+kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
+                             const float *alpha, kda_gate gate,
+                             const float *beta, const float *S_in,
+                             float *S_out, int N, int Tk, int H, int d_k,
+                             int d_v, float scale, kda_dtype dtype, void *o,
+                             hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,7 +26,7 @@ GATES = {"channel": KDA_GATE_CHANNEL, "scalar": KDA_GATE_SCALAR, "none": KDA_GAT
 
 # names exported by include/kda.h
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
-            "kda_chunk_fwd_gated", "kda_decode_step", "kda_decode_step_gated")
+            "kda_chunk_fwd_gated", "kda_decode_step", "kda_decode_step_gated", "kda_decode_tokens")
 
 
 class KdaError(RuntimeError):
@@ -58,6 +58,9 @@ def _load() -> ctypes.CDLL:
     lib.kda_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.kda_decode_step_gated.restype = i32
     lib.kda_decode_step_gated.argtypes = [vp, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32, f32, i32, vp, vp]
+    lib.kda_decode_tokens.restype = i32
+    lib.kda_decode_tokens.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                      vp, vp]
     return lib
 
 
@@ -205,3 +208,45 @@ def decode_step(q, k, v, alpha, beta, S, scale=None, *, gate=None, out=None):
     if st != 0:
         raise KdaError("kda_decode_step_gated", st)
     return out
+
+
+def decode_tokens(q, k, v, alpha, beta, S_in, S_out=None, scale=None, *, gate=None, out=None):
+    """Tk tokens per sequence in one launch: q, k [N, Tk, H, d_k]; v
+    [N, Tk, H, d_v]; beta [N, Tk, H]; alpha [N, Tk, H, d_k] ("channel"),
+    [N, Tk, H] ("scalar") or None ("none").  The state is read from S_in
+    ([N, H, d_v, d_k] fp32) and the state after the last token is written to
+    S_out: a new tensor by default, so S_in stays the checkpoint; pass
+    S_out=S_in to update in place.  Returns (o [N, Tk, H, d_v], S_out)."""
+    import torch
+    dt = _dtype_code(q)
+    gc = _gate_code(gate, alpha, q)
+    if gc == KDA_GATE_NONE:
+        alpha = None
+    if not S_in.is_contiguous() or S_in.dtype != torch.float32 or S_in.data_ptr() % 16:
+        raise ValueError("S_in must be a contiguous, 16-byte aligned float32 tensor")
+    q, k, v, alpha, beta = map(_prep, (q, k, v, alpha, beta))
+    if q.dim() != 4:
+        raise ValueError("q must be [N, Tk, H, d_k]")
+    N, Tk, H, d_k = q.shape
+    d_v = v.shape[-1]
+    if k.shape != q.shape or v.shape != (N, Tk, H, d_v) or beta.numel() != N * Tk * H:
+        raise ValueError("k, v, beta do not match q")
+    if gc == KDA_GATE_CHANNEL and alpha.shape != q.shape:
+        raise ValueError("per-channel alpha must be [N, Tk, H, d_k]")
+    if gc == KDA_GATE_SCALAR and alpha.numel() != N * Tk * H:
+        raise ValueError("scalar alpha must be [N, Tk, H]")
+    if S_in.shape != (N, H, d_v, d_k):
+        raise ValueError("S_in must be [N, H, d_v, d_k]")
+    if S_out is None:
+        S_out = torch.empty_like(S_in)
+    elif (not S_out.is_contiguous() or S_out.dtype != torch.float32 or S_out.data_ptr() % 16
+          or S_out.shape != S_in.shape):
+        raise ValueError("S_out must be a contiguous, 16-byte aligned float32 tensor shaped like S_in")
+    if out is None:
+        out = torch.empty((N, Tk, H, d_v), dtype=v.dtype, device=q.device)
+    st = lib.kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), _ptr(S_in),
+                               _ptr(S_out), N, Tk, H, d_k, d_v, float(scale) if scale else 0.0, dt,
+                               _ptr(out), _stream(q.device))
+    if st != 0:
+        raise KdaError("kda_decode_tokens", st)
+    return out, S_out

@@ -175,12 +175,66 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, co
   a.alpha = alpha;
   a.gate = (int)gate;
   a.beta = beta;
+  a.S_in = S;
   a.S = S;
+  a.Tk = 1;
   a.o = o;
   a.N = N;
   a.H = H;
   a.dk = d_k;
   a.dv = d_v;
+  a.scale = default_scale(scale, d_k);
+  a.bf16 = dtype == KDA_BF16;
+  return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                             const float *beta, const float *S_in, float *S_out, int N, int Tk, int H, int d_k,
+                             int d_v, float scale, kda_dtype dtype, void *o, hipStream_t stream) {
+  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_SCALAR && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED_GATE;
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
+  if (N < 0 || H <= 0 || Tk < 0) return KDA_ERR_BAD_SHAPE;
+  const size_t units = (size_t)N * H;
+  if (units == 0) return KDA_OK;
+  if (units > (size_t)INT32_MAX || (size_t)Tk * units > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
+  const size_t toks = (size_t)Tk * units;
+  if (gate == KDA_GATE_NONE) alpha = nullptr;
+  if (!S_in || !S_out) return KDA_ERR_NULL_ARG;
+  if (toks > 0 && (!q || !k || !v || (gate != KDA_GATE_NONE && !alpha) || !beta || !o)) return KDA_ERR_NULL_ARG;
+  const void *ptrs[] = {q, k, v, alpha, beta, S_in, S_out, o};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+  const size_t es = dtype == KDA_BF16 ? 2 : 4;
+  const size_t a_bytes = gate == KDA_GATE_CHANNEL ? toks * d_k * sizeof(float)
+                         : gate == KDA_GATE_SCALAR ? toks * sizeof(float) : 0;
+  const size_t s_bytes = units * d_v * d_k * sizeof(float);
+  // the state is updated in place or written to a disjoint buffer
+  if (S_in != S_out && overlaps(range_of(S_in, s_bytes), range_of(S_out, s_bytes))) return KDA_ERR_ALIAS;
+  if (toks > 0) {
+    const Range ro = range_of(o, toks * d_v * es);
+    const Range ins[] = {range_of(q, toks * d_k * es), range_of(k, toks * d_k * es),
+                         range_of(v, toks * d_v * es), range_of(alpha, alpha ? a_bytes : 0),
+                         range_of(beta, toks * sizeof(float)), range_of(S_in, s_bytes), range_of(S_out, s_bytes)};
+    for (const Range &r : ins)
+      if (overlaps(ro, r)) return KDA_ERR_ALIAS;
+  }
+
+  kda::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.gate = (int)gate;
+  a.beta = beta;
+  a.S_in = S_in;
+  a.S = S_out;
+  a.o = o;
+  a.N = N;
+  a.H = H;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.Tk = Tk;
   a.scale = default_scale(scale, d_k);
   a.bf16 = dtype == KDA_BF16;
   return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;

@@ -11,13 +11,18 @@
 //     o_r = scale * S[r,:] . q = scale * (s~ . q + e_r (k . q))
 //
 // The state is HBM-resident fp32 and dominates the traffic (one read and one
-// write per step), so the kernel is laid out for bandwidth: every wave-wide
+// write per launch), so the kernel is laid out for bandwidth: every wave-wide
 // state access is one contiguous KiB (lane l takes bytes 16l..16l+15), a lane
 // owns 4 channels of one row, LPR = d_k/4 lanes cover a row, and the two dot
 // products are summed across those lanes with cross-lane swizzles.  State
 // loads and stores carry the nontemporal hint: each state byte is touched
-// once per step, and keeping it out of the caches measured faster.  One
-// workgroup per (sequence, head).
+// once per launch, and keeping it out of the caches measured faster.
+//
+// One launch may carry Tk tokens of each sequence (checking the tokens a
+// draft model proposed: page "K3 架构图解", chapter 10, the section on
+// speculative decoding):
+// the state rows stay in registers across the tokens and the result may go
+// to a second buffer, so the state before the launch survives for rollback.
 #include "kda_device.h"
 #include "kda_launch.h"
 
@@ -26,12 +31,15 @@ namespace {
 
 struct DecodeKArgs {
   const void *q, *k, *v;
+  // alpha: [.., H, d_k] for kGateChannel, [.., H] for kGateScalar, unused
+  // for kGateNone (the kernel is instantiated per form)
   const float *alpha, *beta;
-  int gate;  // kGateChannel: alpha [N, H, d_k]; kGateScalar: alpha [N, H]; kGateNone: unused
-  float *S;
+  const float *S_in;
+  float *S_out;  // may be S_in
   void *o;
   float scale;
-  size_t units;  // sequences x heads
+  unsigned units;  // sequences x heads (< 2^31)
+  int H, Tk;     // heads; tokens per sequence (inputs are [N, Tk, H, .])
 };
 
 template <typename E>
@@ -51,10 +59,27 @@ __device__ __forceinline__ void load4<float>(const float *p, float *out) {
   for (int i = 0; i < 4; ++i) out[i] = x[i];
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of LPR lanes, every lane receiving its group's
+// sum, in registers: DPP quad permutes for lane distance 1 and 2, the half-row
+// and row mirrors for 4 and 8 (once the smaller groups hold equal sums a
+// mirror reads the other half), and the row swap of gfx950 for 16.
 template <int LPR>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < LPR; m <<= 1) x += __shfl_xor(x, m);
+  static_assert(LPR >= 1 && LPR <= 32, "group of at most 32 lanes");
+  if constexpr (LPR >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (LPR >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 8) x += dpp<0x141>(x);   // row_half_mirror
+  if constexpr (LPR >= 16) x += dpp<0x140>(x);  // row_mirror
+  if constexpr (LPR >= 32) {
+    // rows 2i and 2i+1 trade places between the two results
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
   return x;
 }
 
@@ -69,89 +94,160 @@ template <int DK, int DV> struct DecodeShape {
   static constexpr int NI = (APW + 3) / 4;        // accesses per wave
 };
 
-template <int DK, int DV, typename E>
+// Inputs of one token as this lane needs them: 4 channels of k, q, alpha
+// and the values of its state rows.
+template <int NI> struct TokIn {
+  float kk[4], qq[4], al[4], beta, vv[NI];
+};
+
+// Marks every value of x as used here: the loads that fill it must have
+// completed at this point.
+template <int NI>
+__device__ __forceinline__ void consume(const TokIn<NI> &x) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) asm volatile("" ::"v"(x.kk[j]), "v"(x.qq[j]), "v"(x.al[j]));
+#pragma unroll
+  for (int i = 0; i < NI; ++i) asm volatile("" ::"v"(x.vv[i]));
+  asm volatile("" ::"v"(x.beta));
+}
+
+template <int DK, int DV, typename E, int GATE, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   typedef DecodeShape<DK, DV> SH;
   constexpr int LPR = DK / 4;                 // lanes per state row
   constexpr int RPA = 64 / LPR;               // rows per wave-wide KiB access
   constexpr int NI = SH::NI;                  // accesses per wave
+  constexpr bool FULL = SH::APW % 4 == 0;     // every wave owns NI accesses
 
   // the SPLIT workgroups of a unit get ids congruent mod 8, which the
   // dispatcher sends to one XCD, so k, q and alpha leave HBM once per unit
-  const size_t bid = blockIdx.x, slot = bid >> 3;
-  const size_t u = (slot / SH::SPLIT) * 8 + (bid & 7);   // (sequence, head) unit
-  const int part = (int)(slot % SH::SPLIT);              // which APW KiB of the unit
+  const unsigned bid = blockIdx.x, slot = bid >> 3;
+  const unsigned u = (slot / SH::SPLIT) * 8 + (bid & 7);   // (sequence, head) unit
+  const int part = (int)(slot % SH::SPLIT);                // which APW KiB of the unit
   if (u >= a.units) return;
   const int w = wave_id(), l = lane_id();
   const int sub = l % LPR, rsub = l / LPR;
   const int c0 = 4 * sub;
+  const int Tk = G == 1 ? 1 : a.Tk;  // >= 1; the G = 1 kernel is launched for one token
+  // token t of this unit in the [N, Tk, H, .] inputs (with one token per
+  // launch that is the unit itself)
+  auto tok_index = [&](int t) -> size_t {
+    if constexpr (G == 1) return u;
+    const unsigned n = u / (unsigned)a.H, h = u % (unsigned)a.H;
+    return ((size_t)n * Tk + t) * a.H + h;
+  };
 
-  float kk[4], qq[4], al[4];
-  load4<E>(reinterpret_cast<const E *>(a.k) + u * DK + c0, kk);
-  load4<E>(reinterpret_cast<const E *>(a.q) + u * DK + c0, qq);
-  if (a.gate == kGateChannel) {
-    load4<float>(a.alpha + u * DK + c0, al);
-  } else {
-    const float x = a.gate == kGateScalar ? a.alpha[u] : 1.f;
+  // rows of this lane; when a unit is smaller than four KiB the waves past
+  // its share read a valid row, compute on zeros and store nothing (loads
+  // stay unconditional: a branch around a load costs a full wait)
+  int rows[NI];
+  bool valid[NI];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) al[j] = x;
+  for (int i = 0; i < NI; ++i) {
+    const int acc = w * NI + i;
+    valid[i] = FULL || acc < SH::APW;
+    rows[i] = (part * SH::APW + (valid[i] ? acc : 0)) * RPA + rsub;
   }
-  const float beta = a.beta[u];
-  const E *vrow = reinterpret_cast<const E *>(a.v) + u * DV;
-  E *orow = reinterpret_cast<E *>(a.o) + u * DV;
-  float *S = a.S + u * DV * DK;
 
-  // issue every state load of this lane first (waves past the workgroup's
-  // share only exist when a unit is smaller than four KiB; they skip)
+  // the inputs of G tokens are requested together, so a group costs one
+  // memory latency; indexes past the last token re-read the last token
+  TokIn<NI> x[G];
+  auto load_group = [&](int t0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int t = min(t0 + g, Tk - 1);
+      const size_t ix = tok_index(t);
+      load4<E>(reinterpret_cast<const E *>(a.k) + ix * DK + c0, x[g].kk);
+      load4<E>(reinterpret_cast<const E *>(a.q) + ix * DK + c0, x[g].qq);
+      if constexpr (GATE == kGateChannel) {
+        load4<float>(a.alpha + ix * DK + c0, x[g].al);
+      } else {
+        const float al = GATE == kGateScalar ? a.alpha[ix] : 1.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[g].al[j] = al;
+      }
+      x[g].beta = a.beta[ix];
+      const E *vrow = reinterpret_cast<const E *>(a.v) + ix * DV;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) x[g].vv[i] = (float)vrow[rows[i]];
+    }
+  };
+  // this lane's state rows stay in registers across the tokens: one read and
+  // one write of the state per launch
+  const float *Sin = a.S_in + (size_t)u * DV * DK;
   f32x4 s[NI];
-  float vv[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int acc = part * SH::APW + w * NI + i;
-    const int r = acc * RPA + rsub;
-    if (w * NI + i < SH::APW) {
-      s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(S + (size_t)r * DK + c0));
-      vv[i] = (float)vrow[r];
-    } else {
-      s[i] = zero4();
-      vv[i] = 0.f;
+  for (int i = 0; i < NI; ++i)
+    s[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(Sin + (size_t)rows[i] * DK + c0));
+  if constexpr (!FULL) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (!valid[i]) s[i] = zero4();
+  }
+  // the state requests leave first: they come from HBM, the token inputs
+  // mostly from L2 (measured 1% faster than letting the scheduler pick)
+  __builtin_amdgcn_sched_barrier(0);
+
+  // one call site for the group loads: with two (before the loop and at its
+  // end) the compiler merges them into the loop header behind a full wait
+  for (int t0 = 0; t0 < Tk; t0 += G) {
+    load_group(t0);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int t = t0 + g;
+      if (G > 1 && t >= Tk) break;
+      const TokIn<NI> &y = x[g];
+      E *orow = reinterpret_cast<E *>(a.o) + tok_index(t) * DV;
+      float kq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kq += y.kk[j] * y.qq[j];
+      kq = group_sum<LPR>(kq);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        float st[4], d1 = 0.f, d2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          st[j] = s[i][j] * y.al[j];
+          d1 += st[j] * y.kk[j];
+          d2 += st[j] * y.qq[j];
+        }
+        d1 = group_sum<LPR>(d1);
+        d2 = group_sum<LPR>(d2);
+        const float e = y.beta * (y.vv[i] - d1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[i][j] = st[j] + e * y.kk[j];
+        if (valid[i] && sub == 0) orow[rows[i]] = (E)(a.scale * (d2 + e * kq));
+      }
+    }
+    // the inputs of a partial last group past Tk are never read; without
+    // this the compiler assumes their loads may still be in flight on the
+    // back edge and makes the next group's loads wait for every load
+    if constexpr (G > 1) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) consume(x[g]);
     }
   }
-  float kq = 0.f;
+
+  float *Sout = a.S_out + (size_t)u * DV * DK;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) kq += kk[j] * qq[j];
-  kq = group_sum<LPR>(kq);
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int acc = part * SH::APW + w * NI + i;
-    const int r = acc * RPA + rsub;
-    float st[4], d1 = 0.f, d2 = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      st[j] = s[i][j] * al[j];
-      d1 += st[j] * kk[j];
-      d2 += st[j] * qq[j];
-    }
-    d1 = group_sum<LPR>(d1);
-    d2 = group_sum<LPR>(d2);
-    if (w * NI + i < SH::APW) {
-      const float e = beta * (vv[i] - d1);
-      f32x4 outv;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) outv[j] = st[j] + e * kk[j];
-      __builtin_nontemporal_store(outv, reinterpret_cast<f32x4 *>(S + (size_t)r * DK + c0));
-      if (sub == 0) orow[r] = (E)(a.scale * (d2 + e * kq));
-    }
-  }
+  for (int i = 0; i < NI; ++i)
+    if (valid[i]) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4 *>(Sout + (size_t)rows[i] * DK + c0));
 }
 
-template <int DK, typename E>
+constexpr int kTokGroup = 4;  // tokens whose inputs are requested together
+
+template <int DK, typename E, int GATE>
 hipError_t run_decode_dv(const DecodeArgs &a, const DecodeKArgs &ka, hipStream_t s) {
   const size_t units = (size_t)a.N * a.H;
   if ((units + 7) / 8 * 8 * DecodeShape<DK, 128>::SPLIT > 0x7fffffffull) return hipErrorInvalidConfiguration;
-#define KDA_DECODE_LAUNCH(DV) \
-  hipLaunchKernelGGL((decode_kernel<DK, DV, E>), dim3((unsigned)((units + 7) / 8 * 8 * DecodeShape<DK, DV>::SPLIT)), \
-                     dim3(kThreads), 0, s, ka)
+#define KDA_DECODE_LAUNCH(DV)                                                                         \
+  {                                                                                                   \
+    const dim3 grid((unsigned)((units + 7) / 8 * 8 * DecodeShape<DK, DV>::SPLIT));                    \
+    if (a.Tk == 1)                                                                                    \
+      hipLaunchKernelGGL((decode_kernel<DK, DV, E, GATE, 1>), grid, dim3(kThreads), 0, s, ka);         \
+    else                                                                                              \
+      hipLaunchKernelGGL((decode_kernel<DK, DV, E, GATE, kTokGroup>), grid, dim3(kThreads), 0, s, ka); \
+  }
   switch (a.dv) {
     case 16: KDA_DECODE_LAUNCH(16); break;
     case 32: KDA_DECODE_LAUNCH(32); break;
@@ -163,14 +259,24 @@ hipError_t run_decode_dv(const DecodeArgs &a, const DecodeKArgs &ka, hipStream_t
   return hipGetLastError();
 }
 
+template <int DK, typename E>
+hipError_t run_decode_gate(const DecodeArgs &a, const DecodeKArgs &ka, hipStream_t s) {
+  switch (a.gate) {
+    case kGateChannel: return run_decode_dv<DK, E, kGateChannel>(a, ka, s);
+    case kGateScalar: return run_decode_dv<DK, E, kGateScalar>(a, ka, s);
+    case kGateNone: return run_decode_dv<DK, E, kGateNone>(a, ka, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <typename E>
 hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
-  DecodeKArgs ka{a.q, a.k, a.v, a.alpha, a.beta, a.gate, a.S, a.o, a.scale, (size_t)a.N * a.H};
+  DecodeKArgs ka{a.q, a.k, a.v, a.alpha, a.beta, a.S_in, a.S, a.o, a.scale, (unsigned)((size_t)a.N * a.H), a.H, a.Tk};
   switch (a.dk) {
-    case 16: return run_decode_dv<16, E>(a, ka, s);
-    case 32: return run_decode_dv<32, E>(a, ka, s);
-    case 64: return run_decode_dv<64, E>(a, ka, s);
-    case 128: return run_decode_dv<128, E>(a, ka, s);
+    case 16: return run_decode_gate<16, E>(a, ka, s);
+    case 32: return run_decode_gate<32, E>(a, ka, s);
+    case 64: return run_decode_gate<64, E>(a, ka, s);
+    case 128: return run_decode_gate<128, E>(a, ka, s);
   }
   return hipErrorInvalidValue;
 }
@@ -179,6 +285,11 @@ hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if ((size_t)a.N * a.H == 0) return hipSuccess;
+  if (a.Tk == 0) {  // no token: the state passes through
+    if (a.S == a.S_in) return hipSuccess;
+    return hipMemcpyAsync(a.S, a.S_in, (size_t)a.N * a.H * a.dv * a.dk * sizeof(float), hipMemcpyDeviceToDevice,
+                          stream);
+  }
   return a.bf16 ? run_decode<bf16>(a, stream) : run_decode<float>(a, stream);
 }
 

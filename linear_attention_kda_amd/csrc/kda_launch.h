@@ -96,9 +96,11 @@ struct DecodeArgs {
   const void *q, *k, *v;
   const float *alpha, *beta;
   int gate;
-  float *S;
+  const float *S_in;  // state read
+  float *S;           // state written (may be S_in)
   void *o;
   int N, H, dk, dv;
+  int Tk;             // tokens per sequence (1 for a single step)
   float scale;
   bool bf16;
 };

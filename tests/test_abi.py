@@ -138,3 +138,22 @@ def test_gated_validation(kda):
     assert dec(kda.KDA_GATE_SCALAR, None) == 1
     assert dec(kda.KDA_GATE_CHANNEL, P(0x40008)) == 5
     assert dec(kda.KDA_GATE_NONE, None, o=P(0x60000)) == 8   # o aliases S, alpha unused
+
+
+def test_decode_tokens_validation(kda):
+    P = ctypes.c_void_p
+    good = dict(q=P(0x10000), k=P(0x20000), v=P(0x30000), alpha=P(0x40000), beta=P(0x50000),
+                Si=P(0x100000), So=P(0x200000), o=P(0x90000), N=2, Tk=3, H=2, gate=kda.KDA_GATE_CHANNEL)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return kda.lib.kda_decode_tokens(a["q"], a["k"], a["v"], a["alpha"], a["gate"], a["beta"], a["Si"],
+                                         a["So"], a["N"], a["Tk"], a["H"], 16, 16, 0.0, kda.KDA_F32, a["o"],
+                                         None)
+    assert call(Tk=-1) == 2
+    assert call(gate=5) == 10
+    assert call(Si=None) == 1
+    assert call(So=P(0x100000 + 256)) == 8          # partial overlap of the two states
+    assert call(o=P(0x100000)) == 8                 # o overlaps a state
+    assert call(gate=kda.KDA_GATE_SCALAR, alpha=None) == 1
+    assert call(N=0) == 0
