@@ -54,7 +54,8 @@ def prefill_bytes(B, T, H, dk, dv, esize=2, s0=False, gate_form="channel"):
     alpha fp32 (per key channel, or one per token and head, or none), beta
     fp32, S_final (and S0) fp32."""
     tok = B * T * H
-    alpha = {"channel": tok * dk * 4, "scalar": tok * 4, "none": 0}[gate_form]
+    alpha = {"channel": tok * dk * 4, "scalar": tok * 4, "none": 0,
+             "log_channel": tok * dk * 4, "log_scalar": tok * 4}[gate_form]
     return (tok * (2 * dk + 2 * dv) * esize + alpha + tok * 4
             + (2 if s0 else 1) * B * H * dv * dk * 4)
 
@@ -295,16 +296,20 @@ def main():
         result["decode"] = bench_decode(args, torch, kda, inputs)
         result["decode_tokens"] = bench_decode_tokens(args, torch, kda, inputs)
     if not args.no_gate_forms:
-        # the same workload with one gate per (token, head) (Gated DeltaNet form)
-        sg = bench_prefill(args, torch, kda, inputs, gate_form="scalar", steps=max(20, args.steps // 4))
-        sb = prefill_bytes(sg["B"], sg["T"], sg["H"], sg["dk"], sg["dv"], gate_form="scalar")
-        ach = sb / (sg["call_ms_mean"] * 1e-3) / 1e9
-        result["prefill_scalar_gate"] = {
-            "workload": "prefill B=4 H=16 T=2048 d=128 bf16, one fp32 gate per (token, head)",
-            "tokens_per_s": round(sg["tokens"] / (sg["ms_per_step"] * 1e-3), 1),
-            "call_us_mean": round(sg["call_ms_mean"] * 1e3, 2),
-            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": sb}}
+        # the same workload with the gate in other forms: one gate per (token,
+        # head) (Gated DeltaNet), and per-channel gates given as log(alpha)
+        forms = (("scalar", "prefill_scalar_gate", "one fp32 gate per (token, head)"),
+                 ("log_channel", "prefill_log_gate", "per-channel fp32 gates given as log(alpha)"))
+        for form, key, what in forms:
+            sg = bench_prefill(args, torch, kda, inputs, gate_form=form, steps=max(20, args.steps // 4))
+            sb = prefill_bytes(sg["B"], sg["T"], sg["H"], sg["dk"], sg["dv"], gate_form=form)
+            ach = sb / (sg["call_ms_mean"] * 1e-3) / 1e9
+            result[key] = {
+                "workload": f"prefill B=4 H=16 T=2048 d=128 bf16, {what}",
+                "tokens_per_s": round(sg["tokens"] / (sg["ms_per_step"] * 1e-3), 1),
+                "call_us_mean": round(sg["call_ms_mean"] * 1e3, 2),
+                "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": sb}}
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)

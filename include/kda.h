@@ -71,11 +71,27 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * the whole state; section "DeltaNet: ..." has no gate.  The scalar form is
  * the per-channel form with the same value on every channel, and no gate is
  * the per-channel form with every value 1.
- *   KDA_GATE_CHANNEL  alpha [..., d_k] fp32, one value per key channel
- *   KDA_GATE_SCALAR   alpha [...]      fp32, one value per token and head
- *   KDA_GATE_NONE     no forgetting; alpha is not read and may be NULL
+ *   KDA_GATE_CHANNEL      alpha [..., d_k] fp32, one value per key channel
+ *   KDA_GATE_SCALAR       alpha [...]      fp32, one value per token and head
+ *   KDA_GATE_NONE         no forgetting; alpha is not read and may be NULL
+ *   KDA_GATE_LOG_CHANNEL  as KDA_GATE_CHANNEL, holding log(alpha) <= 0
+ *   KDA_GATE_LOG_SCALAR   as KDA_GATE_SCALAR, holding log(alpha) <= 0
+ * The log forms take the gate as the same page's section "Two schedules of
+ * computation for one recurrence" describes the production pipeline taking
+ * it (decays as logarithms); a model computing alpha = exp(-softplus(x))
+ * passes -softplus(x) and skips the exponential pass over the gates.  The
+ * kernels take exp on load (fp32, hardware exp2 of g log2 e, relative error
+ * about |g| 2^-23; -inf gives a gate of exactly 0) and
+ * then run unchanged.  Gates must lie in [0, 1] (log gates in [-inf, 0]);
+ * values outside are not checked and give unspecified results.
  */
-typedef enum { KDA_GATE_CHANNEL = 0, KDA_GATE_SCALAR = 1, KDA_GATE_NONE = 2 } kda_gate;
+typedef enum {
+  KDA_GATE_CHANNEL = 0,
+  KDA_GATE_SCALAR = 1,
+  KDA_GATE_NONE = 2,
+  KDA_GATE_LOG_CHANNEL = 3,
+  KDA_GATE_LOG_SCALAR = 4
+} kda_gate;
 
 /* Text for a status code (static storage; never NULL). */
 const char *kda_status_string(kda_status s);
@@ -123,8 +139,9 @@ kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
 
 /*
  * kda_chunk_fwd with the gate given as `gate` (see kda_gate): alpha is
- * [B, T, H, d_k] for KDA_GATE_CHANNEL (then this is kda_chunk_fwd),
- * [B, T, H] for KDA_GATE_SCALAR, and unused (may be NULL) for KDA_GATE_NONE.
+ * [B, T, H, d_k] for KDA_GATE_CHANNEL (then this is kda_chunk_fwd) and
+ * KDA_GATE_LOG_CHANNEL, [B, T, H] for KDA_GATE_SCALAR and
+ * KDA_GATE_LOG_SCALAR, and unused (may be NULL) for KDA_GATE_NONE.
  * Everything else as for kda_chunk_fwd; an unknown gate returns
  * KDA_ERR_UNSUPPORTED_GATE.
  */
@@ -154,8 +171,8 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
 
 /*
  * kda_decode_step with the gate given as `gate`: alpha is [N, H, d_k] for
- * KDA_GATE_CHANNEL, [N, H] for KDA_GATE_SCALAR, unused (may be NULL) for
- * KDA_GATE_NONE.  An unknown gate returns KDA_ERR_UNSUPPORTED_GATE.
+ * the per-channel forms, [N, H] for the scalar forms, unused (may be NULL)
+ * for KDA_GATE_NONE.  An unknown gate returns KDA_ERR_UNSUPPORTED_GATE.
  */
 kda_status kda_decode_step_gated(const void *q, const void *k, const void *v,
                                  const float *alpha, kda_gate gate,
@@ -175,8 +192,8 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v,
  * place.  Tk = 0 copies S_in to S_out.
  *
  *  q, k     [N, Tk, H, d_k]  dtype     v [N, Tk, H, d_v]  dtype
- *  alpha    [N, Tk, H, d_k] (KDA_GATE_CHANNEL), [N, Tk, H] (KDA_GATE_SCALAR),
- *           unused (KDA_GATE_NONE)    beta [N, Tk, H]  fp32
+ *  alpha    [N, Tk, H, d_k] (per-channel forms), [N, Tk, H] (scalar
+ *           forms), unused (KDA_GATE_NONE)    beta [N, Tk, H]  fp32
  *  S_in, S_out [N, H, d_v, d_k] fp32: the same buffer or disjoint ones
  *           (a partial overlap returns KDA_ERR_ALIAS)
  *  o        [N, Tk, H, d_v]  dtype     must not overlap an input or a state

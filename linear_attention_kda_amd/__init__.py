@@ -6,7 +6,8 @@ is the thin Python binding over that ABI; torch supplies device memory and
 streams.  The library is loaded on first use of a binding name; if it is
 missing that raises ImportError (there is no fallback).
 """
-_BINDING_NAMES = ("EXPORTED", "GATES", "KDA_BF16", "KDA_F32", "KDA_GATE_CHANNEL", "KDA_GATE_NONE",
+_BINDING_NAMES = ("EXPORTED", "GATES", "KDA_BF16", "KDA_F32", "KDA_GATE_CHANNEL", "KDA_GATE_LOG_CHANNEL",
+                  "KDA_GATE_LOG_SCALAR", "KDA_GATE_NONE",
                   "KDA_GATE_SCALAR", "LIB_PATH", "KdaError", "chunk_fwd", "chunk_fwd_workspace_size",
                   "decode_step", "decode_tokens", "lib", "status_string")
 

@@ -22,7 +22,12 @@ KDA_BF16 = 1
 KDA_GATE_CHANNEL = 0
 KDA_GATE_SCALAR = 1
 KDA_GATE_NONE = 2
-GATES = {"channel": KDA_GATE_CHANNEL, "scalar": KDA_GATE_SCALAR, "none": KDA_GATE_NONE}
+KDA_GATE_LOG_CHANNEL = 3
+KDA_GATE_LOG_SCALAR = 4
+GATES = {"channel": KDA_GATE_CHANNEL, "scalar": KDA_GATE_SCALAR, "none": KDA_GATE_NONE,
+         "log_channel": KDA_GATE_LOG_CHANNEL, "log_scalar": KDA_GATE_LOG_SCALAR}
+_PER_CHANNEL = (KDA_GATE_CHANNEL, KDA_GATE_LOG_CHANNEL)
+_PER_TOKEN = (KDA_GATE_SCALAR, KDA_GATE_LOG_SCALAR)
 
 # names exported by include/kda.h
 EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
@@ -101,7 +106,8 @@ def _dtype_code(t) -> int:
 
 
 def _gate_code(gate, alpha, q):
-    """kda_gate code: given by name, else read from alpha's shape."""
+    """kda_gate code: given by name, else read from alpha's shape (which
+    cannot tell a log gate from a gate: the log forms are named)."""
     if gate is None:
         if alpha is None:
             return KDA_GATE_NONE
@@ -151,9 +157,9 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gat
         N = B
     if k.shape != q.shape:
         raise ValueError("k must have the shape of q")
-    if gc == KDA_GATE_CHANNEL and alpha.shape != q.shape:
+    if gc in _PER_CHANNEL and alpha.shape != q.shape:
         raise ValueError("per-channel alpha must have the shape of q")
-    if gc == KDA_GATE_SCALAR and alpha.numel() != B * T * H:
+    if gc in _PER_TOKEN and alpha.numel() != B * T * H:
         raise ValueError("scalar alpha must have one value per token and head")
     if v.numel() != B * T * H * d_v or beta.numel() != B * T * H:
         raise ValueError("v / beta sizes do not match q")
@@ -196,9 +202,9 @@ def decode_step(q, k, v, alpha, beta, S, scale=None, *, gate=None, out=None):
     d_v = v.shape[-1]
     if S.shape != (N, H, d_v, d_k):
         raise ValueError("S must be [N, H, d_v, d_k]")
-    if gc == KDA_GATE_CHANNEL and alpha.shape != q.shape:
+    if gc in _PER_CHANNEL and alpha.shape != q.shape:
         raise ValueError("per-channel alpha must be [N, H, d_k]")
-    if gc == KDA_GATE_SCALAR and alpha.numel() != N * H:
+    if gc in _PER_TOKEN and alpha.numel() != N * H:
         raise ValueError("scalar alpha must be [N, H]")
     if out is None:
         out = torch.empty((N, H, d_v), dtype=v.dtype, device=q.device)
@@ -231,9 +237,9 @@ def decode_tokens(q, k, v, alpha, beta, S_in, S_out=None, scale=None, *, gate=No
     d_v = v.shape[-1]
     if k.shape != q.shape or v.shape != (N, Tk, H, d_v) or beta.numel() != N * Tk * H:
         raise ValueError("k, v, beta do not match q")
-    if gc == KDA_GATE_CHANNEL and alpha.shape != q.shape:
+    if gc in _PER_CHANNEL and alpha.shape != q.shape:
         raise ValueError("per-channel alpha must be [N, Tk, H, d_k]")
-    if gc == KDA_GATE_SCALAR and alpha.numel() != N * Tk * H:
+    if gc in _PER_TOKEN and alpha.numel() != N * Tk * H:
         raise ValueError("scalar alpha must be [N, Tk, H]")
     if S_in.shape != (N, H, d_v, d_k):
         raise ValueError("S_in must be [N, H, d_v, d_k]")

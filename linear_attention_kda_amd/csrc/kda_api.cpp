@@ -14,6 +14,10 @@
 namespace {
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool valid_gate(kda_gate g) {
+  return g == KDA_GATE_CHANNEL || g == KDA_GATE_SCALAR || g == KDA_GATE_NONE || g == KDA_GATE_LOG_CHANNEL ||
+         g == KDA_GATE_LOG_SCALAR;
+}
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct Range {
@@ -45,7 +49,7 @@ const char *kda_status_string(kda_status s) {
     case KDA_ERR_VARLEN_REQUIRES_B1: return "cu_seqlens requires B == 1";
     case KDA_ERR_ALIAS: return "the output overlaps an input";
     case KDA_ERR_HIP: return "the HIP runtime reported an error";
-    case KDA_ERR_UNSUPPORTED_GATE: return "gate must be KDA_GATE_CHANNEL, KDA_GATE_SCALAR or KDA_GATE_NONE";
+    case KDA_ERR_UNSUPPORTED_GATE: return "gate must be a kda_gate value (channel, scalar, none, log channel, log scalar)";
   }
   return "unknown status";
 }
@@ -74,7 +78,7 @@ kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v, cons
                                const float *beta, const float *S0, const int32_t *cu_seqlens, int N, int B, int T,
                                int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o, float *S_final,
                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_SCALAR && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED_GATE;
+  if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
   if (B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
@@ -88,8 +92,8 @@ kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v, cons
   const size_t es = dtype == KDA_BF16 ? 2 : 4;
   const size_t ntok = (size_t)B * T;
   const size_t qk_bytes = ntok * H * d_k * es, v_bytes = ntok * H * d_v * es;
-  const size_t a_bytes = gate == KDA_GATE_CHANNEL ? ntok * H * d_k * sizeof(float)
-                         : gate == KDA_GATE_SCALAR ? ntok * H * sizeof(float) : 0;
+  const size_t a_bytes = kda::gate_per_channel(gate) ? ntok * H * d_k * sizeof(float)
+                         : kda::gate_per_token(gate) ? ntok * H * sizeof(float) : 0;
   const size_t b_bytes = ntok * H * sizeof(float);
   const size_t s_bytes = (size_t)N * H * d_v * d_k * sizeof(float);
   if (gate == KDA_GATE_NONE) alpha = nullptr;
@@ -146,7 +150,7 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v, const fl
 kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
                                  const float *beta, float *S, int N, int H, int d_k, int d_v, float scale,
                                  kda_dtype dtype, void *o, hipStream_t stream) {
-  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_SCALAR && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED_GATE;
+  if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
   if (N < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
@@ -157,8 +161,8 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, co
   const void *ptrs[] = {q, k, v, alpha, beta, S, o};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
-  const size_t a_bytes = gate == KDA_GATE_CHANNEL ? units * d_k * sizeof(float)
-                         : gate == KDA_GATE_SCALAR ? units * sizeof(float) : 0;
+  const size_t a_bytes = kda::gate_per_channel(gate) ? units * d_k * sizeof(float)
+                         : kda::gate_per_token(gate) ? units * sizeof(float) : 0;
   if (units > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
   const size_t es = dtype == KDA_BF16 ? 2 : 4;
   const Range ro = range_of(o, units * d_v * es);
@@ -191,7 +195,7 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, co
 kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
                              const float *beta, const float *S_in, float *S_out, int N, int Tk, int H, int d_k,
                              int d_v, float scale, kda_dtype dtype, void *o, hipStream_t stream) {
-  if (gate != KDA_GATE_CHANNEL && gate != KDA_GATE_SCALAR && gate != KDA_GATE_NONE) return KDA_ERR_UNSUPPORTED_GATE;
+  if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
   if (N < 0 || H <= 0 || Tk < 0) return KDA_ERR_BAD_SHAPE;
@@ -206,8 +210,8 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
   const size_t es = dtype == KDA_BF16 ? 2 : 4;
-  const size_t a_bytes = gate == KDA_GATE_CHANNEL ? toks * d_k * sizeof(float)
-                         : gate == KDA_GATE_SCALAR ? toks * sizeof(float) : 0;
+  const size_t a_bytes = kda::gate_per_channel(gate) ? toks * d_k * sizeof(float)
+                         : kda::gate_per_token(gate) ? toks * sizeof(float) : 0;
   const size_t s_bytes = units * d_v * d_k * sizeof(float);
   // the state is updated in place or written to a disjoint buffer
   if (S_in != S_out && overlaps(range_of(S_in, s_bytes), range_of(S_out, s_bytes))) return KDA_ERR_ALIAS;

@@ -31,8 +31,9 @@ namespace {
 
 struct DecodeKArgs {
   const void *q, *k, *v;
-  // alpha: [.., H, d_k] for kGateChannel, [.., H] for kGateScalar, unused
-  // for kGateNone (the kernel is instantiated per form)
+  // alpha: [.., H, d_k] for the per-channel forms, [.., H] for the
+  // per-token forms, unused without a gate; the log forms hold log(alpha)
+  // (the kernel is instantiated per form)
   const float *alpha, *beta;
   const float *S_in;
   float *S_out;  // may be S_in
@@ -159,10 +160,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
       const size_t ix = tok_index(t);
       load4<E>(reinterpret_cast<const E *>(a.k) + ix * DK + c0, x[g].kk);
       load4<E>(reinterpret_cast<const E *>(a.q) + ix * DK + c0, x[g].qq);
-      if constexpr (GATE == kGateChannel) {
+      if constexpr (gate_per_channel(GATE)) {
         load4<float>(a.alpha + ix * DK + c0, x[g].al);
       } else {
-        const float al = GATE == kGateScalar ? a.alpha[ix] : 1.f;
+        const float al = gate_per_token(GATE) ? a.alpha[ix] : 1.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) x[g].al[j] = al;
       }
@@ -196,7 +197,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     for (int g = 0; g < G; ++g) {
       const int t = t0 + g;
       if (G > 1 && t >= Tk) break;
-      const TokIn<NI> &y = x[g];
+      TokIn<NI> &y = x[g];
+      if constexpr (gate_is_log(GATE)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y.al[j] = gate_from_log(y.al[j]);
+      }
       E *orow = reinterpret_cast<E *>(a.o) + tok_index(t) * DV;
       float kq = 0.f;
 #pragma unroll
@@ -265,6 +270,8 @@ hipError_t run_decode_gate(const DecodeArgs &a, const DecodeKArgs &ka, hipStream
     case kGateChannel: return run_decode_dv<DK, E, kGateChannel>(a, ka, s);
     case kGateScalar: return run_decode_dv<DK, E, kGateScalar>(a, ka, s);
     case kGateNone: return run_decode_dv<DK, E, kGateNone>(a, ka, s);
+    case kGateLogChannel: return run_decode_dv<DK, E, kGateLogChannel>(a, ka, s);
+    case kGateLogScalar: return run_decode_dv<DK, E, kGateLogScalar>(a, ka, s);
   }
   return hipErrorInvalidValue;
 }

@@ -15,6 +15,13 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kChunk = 64;   // tokens per chunk of the chunkwise schedule
 constexpr int kThreads = 256;
 
+// A gate from its logarithm: e^g = 2^(g log2 e) on the hardware exponential
+// (v_exp_f32).  Rounding g log2 e costs a relative error of about |g| 2^-24
+// on top of the instruction's own; g = -inf gives exactly 0.
+__device__ __forceinline__ float gate_from_log(float g) {
+  return __builtin_amdgcn_exp2f(g * 1.4426950408889634f);
+}
+
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 

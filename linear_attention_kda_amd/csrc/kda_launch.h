@@ -74,7 +74,11 @@ inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
 }
 
 // gate kinds (kda_gate): 0 per key channel, 1 one per token and head, 2 none
-constexpr int kGateChannel = 0, kGateScalar = 1, kGateNone = 2;
+constexpr int kGateChannel = 0, kGateScalar = 1, kGateNone = 2, kGateLogChannel = 3, kGateLogScalar = 4;
+// gate forms that read one value per key channel / one per token and head
+constexpr bool gate_per_channel(int g) { return g == kGateChannel || g == kGateLogChannel; }
+constexpr bool gate_per_token(int g) { return g == kGateScalar || g == kGateLogScalar; }
+constexpr bool gate_is_log(int g) { return g == kGateLogChannel || g == kGateLogScalar; }
 
 struct PrefillArgs {
   const void *q, *k, *v;

@@ -161,7 +161,7 @@ __device__ __forceinline__ int frag_index(int i, int c) {
 struct PrepKArgs {
   const void *q, *k;
   const float *alpha, *beta;
-  int gate;  // kGateChannel: alpha [.., H, d_k]; kGateScalar: alpha [.., H]; kGateNone: unused
+  int gate;  // a kGate* form: alpha [.., H, d_k] per channel, [.., H] per token, unused for none
   ChunkSource src;
   int H;
   float scale;
@@ -382,17 +382,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const size_t hs = (size_t)a.H * DK;  // token stride of q, k, alpha
   const size_t base = (size_t)t0 * hs + (size_t)h * DK + c0;
   // gates of channels ch0 .. ch0+3 of token t0 + tk (tk a valid chunk index):
-  // per channel, one shared value, or none (see kda_gate)
+  // per channel, one shared value, or none, given as gates or as their
+  // logarithms (see kda_gate)
   auto gate4 = [&](int tk, int ch0, float *al, bool nontemporal) {
     const size_t tok = (size_t)t0 + tk;
-    if constexpr (GATE == kGateChannel) {
+    if constexpr (gate_per_channel(GATE)) {
       const f32x4 *p = reinterpret_cast<const f32x4 *>(a.alpha + tok * hs + (size_t)h * DK + ch0);
       const f32x4 x = nontemporal ? __builtin_nontemporal_load(p) : *p;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = x[j];
+      for (int j = 0; j < 4; ++j) al[j] = gate_is_log(GATE) ? gate_from_log(x[j]) : x[j];
     } else {
       float x = 1.f;
-      if constexpr (GATE == kGateScalar) x = a.alpha[tok * a.H + h];
+      if constexpr (gate_per_token(GATE)) {
+        x = a.alpha[tok * a.H + h];
+        if constexpr (gate_is_log(GATE)) x = gate_from_log(x);
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) al[j] = x;
     }
@@ -1307,12 +1311,22 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.ws_records = records;
     pa.lay = lay;
     const dim3 pg((unsigned)P.max_chunks, a.H);
-    if (a.gate == kGateScalar)
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar>), pg, dim3(kThreads), 0, stream, pa);
-    else if (a.gate == kGateNone)
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone>), pg, dim3(kThreads), 0, stream, pa);
-    else
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel>), pg, dim3(kThreads), 0, stream, pa);
+    switch (a.gate) {
+      case kGateScalar:
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar>), pg, dim3(kThreads), 0, stream, pa);
+        break;
+      case kGateNone:
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone>), pg, dim3(kThreads), 0, stream, pa);
+        break;
+      case kGateLogChannel:
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogChannel>), pg, dim3(kThreads), 0, stream, pa);
+        break;
+      case kGateLogScalar:
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogScalar>), pg, dim3(kThreads), 0, stream, pa);
+        break;
+      default:
+        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel>), pg, dim3(kThreads), 0, stream, pa);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

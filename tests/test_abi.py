@@ -115,8 +115,12 @@ def _fwd_gated(kda, gate, **kw):
 
 def test_gated_validation(kda):
     P = ctypes.c_void_p
-    assert _fwd_gated(kda, 3) == 10                           # unknown gate
+    assert _fwd_gated(kda, 5) == 10                           # unknown gate
     assert _fwd_gated(kda, -1) == 10
+    assert _fwd_gated(kda, kda.KDA_GATE_LOG_SCALAR, alpha=None) == 1   # log gates need alpha
+    assert _fwd_gated(kda, kda.KDA_GATE_LOG_CHANNEL, alpha=P(0x40008)) == 5
+    # a log per-channel gate has the per-channel extent: o inside it aliases
+    assert _fwd_gated(kda, kda.KDA_GATE_LOG_CHANNEL, o=P(0x40000 + 256)) == 8
     assert _fwd_gated(kda, kda.KDA_GATE_SCALAR, alpha=None) == 1   # scalar gates need alpha
     assert _fwd_gated(kda, kda.KDA_GATE_CHANNEL, alpha=None) == 1
     assert _fwd_gated(kda, kda.KDA_GATE_SCALAR, alpha=P(0x40004)) == 5
@@ -135,6 +139,8 @@ def test_gated_validation(kda):
         return kda.lib.kda_decode_step_gated(a["q"], a["k"], a["v"], alpha, gate, a["beta"], a["S"], 2, 2,
                                              16, 16, 0.0, kda.KDA_F32, a["o"], None)
     assert dec(7, P(0x40000)) == 10
+    assert dec(kda.KDA_GATE_LOG_CHANNEL, None) == 1
+    assert dec(kda.KDA_GATE_LOG_SCALAR, P(0x40002)) == 5
     assert dec(kda.KDA_GATE_SCALAR, None) == 1
     assert dec(kda.KDA_GATE_CHANNEL, P(0x40008)) == 5
     assert dec(kda.KDA_GATE_NONE, None, o=P(0x60000)) == 8   # o aliases S, alpha unused
