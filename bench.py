@@ -35,8 +35,9 @@ NSETS = 4
 # Each figure belongs to the kernel source with the given sha256 prefix and is
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
-    "prefill": ("kda_prefill.hip", "fe9c646be16a16b5", 480_342_425),
-    "decode": ("kda_decode.hip", "621875230307cbcf", 1_086_896_844),
+    "prefill": ("kda_prefill.hip", "0b0cfa0e7add40ac", 480_363_213),
+    "decode": ("kda_decode.hip", "f38948dc0d2cc0e0", 1_086_888_550),
+    "decode_tokens": ("kda_decode.hip", "f38948dc0d2cc0e0", 1_125_201_920),
 }
 
 
@@ -162,7 +163,7 @@ def bench_decode_tokens(args, torch, kda, inputs, Tk=4):
             "us_per_launch": launch_us,
             "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "bytes_per_launch": nbytes}}
+                         "traffic": measured_traffic("decode_tokens"), "bytes_per_launch": nbytes}}
 
 
 def bench_decode(args, torch, kda, inputs):
