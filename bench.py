@@ -113,8 +113,18 @@ def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     mean_ms = e0.elapsed_time(e1) / steps
+    # the spread of single calls, from a separate short run with events
+    # around each call (not used for the throughput)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        step(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    single = sorted(a.elapsed_time(b) for a, b in ev)
     return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=wall, ms_per_step=wall * 1e3 / steps,
-                call_ms_mean=mean_ms, tokens=B * T)
+                call_ms_mean=mean_ms, call_ms_median=single[len(single) // 2], call_ms_min=single[0],
+                tokens=B * T)
 
 
 def decode_tokens_bytes(N, H, dk, dv, Tk, esize=2):
@@ -289,6 +299,8 @@ def main():
                      "kernel": "kda_chunk_fwd call (chunk_prep_kernel + chunk_scan_kernel)",
                      "algorithmic_bytes": nbytes,
                      "call_us_mean": round(pf["call_ms_mean"] * 1e3, 2),
+                     "single_call_us_median": round(pf["call_ms_median"] * 1e3, 2),
+                     "single_call_us_min": round(pf["call_ms_min"] * 1e3, 2),
                      "mfma_frac": round(flops / call_s / 1e12 / BF16_PEAK_TFLOPS, 4)},
     }
     if not args.no_decode:

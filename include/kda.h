@@ -28,11 +28,13 @@
  *  - dtype selects the element type of q, k, v and o (KDA_F32 or KDA_BF16).
  *    alpha, beta and every state tensor are always fp32.
  *  - d_k and d_v must each be one of 16, 32, 64, 128.
- *  - Errors are returned, never printed; nothing aborts.  Only conditions the
- *    host can check are validated.  Values outside alpha, beta in [0,1],
- *    non-monotone cu_seqlens or a non-unit k are not detected: the result is
- *    then unspecified, but every memory access stays inside the buffers the
- *    shapes describe.  A launch failure reported by the HIP runtime returns
+ *  - Errors are returned, never printed; nothing aborts.  By default only
+ *    conditions the host can check are validated.  Values outside alpha,
+ *    beta in [0,1], non-monotone cu_seqlens or a non-unit k are then not
+ *    detected: the result is unspecified, but every memory access stays
+ *    inside the buffers the shapes describe.  With value checks on (see
+ *    kda_set_validation) they return KDA_ERR_INVALID_VALUE before any work
+ *    is launched.  A launch failure reported by the HIP runtime returns
  *    KDA_ERR_HIP.
  */
 #ifndef KDA_H_
@@ -59,7 +61,8 @@ typedef enum {
   KDA_ERR_VARLEN_REQUIRES_B1 = 7,  /* cu_seqlens given with B != 1           */
   KDA_ERR_ALIAS = 8,               /* o overlaps an input                    */
   KDA_ERR_HIP = 9,                 /* the HIP runtime reported an error      */
-  KDA_ERR_UNSUPPORTED_GATE = 10    /* gate is not a kda_gate value           */
+  KDA_ERR_UNSUPPORTED_GATE = 10,   /* gate is not a kda_gate value           */
+  KDA_ERR_INVALID_VALUE = 11       /* a value check failed (validation on)   */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -95,6 +98,23 @@ typedef enum {
 
 /* Text for a status code (static storage; never NULL). */
 const char *kda_status_string(kda_status s);
+
+/*
+ * Value checks, a debugging aid: with enable != 0 every compute entry point
+ * first runs a device kernel over its inputs and returns
+ * KDA_ERR_INVALID_VALUE, launching nothing else, if
+ *   - a gate is outside [0, 1] (a log gate above 0), or NaN,
+ *   - a beta is outside [0, 1], or NaN,
+ *   - a key's squared norm differs from 1 by more than 1/64 (page "Kimi
+ *     Delta Attention (KDA)", section "DeltaNet: writing the error instead of
+ *     the value": the write replaces the value stored along k when |k| = 1),
+ *   - cu_seqlens does not start at 0, decreases, or does not end at T.
+ * The check reads every input once more and then SYNCHRONISES `stream`
+ * (the only case in which a call waits for the device).  The initial state
+ * is on when the environment variable KDA_VALIDATE holds a nonzero integer
+ * at load time.  Process-wide; returns the previous setting.
+ */
+int kda_set_validation(int enable);
 
 /*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes (host-only

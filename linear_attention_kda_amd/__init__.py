@@ -9,7 +9,8 @@ missing that raises ImportError (there is no fallback).
 _BINDING_NAMES = ("EXPORTED", "GATES", "KDA_BF16", "KDA_F32", "KDA_GATE_CHANNEL", "KDA_GATE_LOG_CHANNEL",
                   "KDA_GATE_LOG_SCALAR", "KDA_GATE_NONE",
                   "KDA_GATE_SCALAR", "LIB_PATH", "KdaError", "chunk_fwd", "chunk_fwd_workspace_size",
-                  "decode_step", "decode_tokens", "lib", "status_string")
+                  "decode_step", "decode_tokens", "lib", "set_validation", "status_string",
+                  "KDA_ERR_INVALID_VALUE")
 
 
 def __getattr__(name):

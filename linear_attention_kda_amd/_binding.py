@@ -30,8 +30,9 @@ _PER_CHANNEL = (KDA_GATE_CHANNEL, KDA_GATE_LOG_CHANNEL)
 _PER_TOKEN = (KDA_GATE_SCALAR, KDA_GATE_LOG_SCALAR)
 
 # names exported by include/kda.h
-EXPORTED = ("kda_status_string", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
+EXPORTED = ("kda_status_string", "kda_set_validation", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_fwd_gated", "kda_decode_step", "kda_decode_step_gated", "kda_decode_tokens")
+KDA_ERR_INVALID_VALUE = 11
 
 
 class KdaError(RuntimeError):
@@ -66,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.kda_decode_tokens.restype = i32
     lib.kda_decode_tokens.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                       vp, vp]
+    lib.kda_set_validation.restype = i32
+    lib.kda_set_validation.argtypes = [i32]
     return lib
 
 
@@ -74,6 +77,14 @@ lib = _load()
 
 def status_string(status: int) -> str:
     return lib.kda_status_string(int(status)).decode()
+
+
+def set_validation(enable: bool) -> bool:
+    """Turn the library's device-side value checks on or off (process-wide);
+    returns the previous setting.  While on, every call synchronises its
+    stream and raises KdaError (status KDA_ERR_INVALID_VALUE) on inputs
+    outside the method's domain."""
+    return bool(lib.kda_set_validation(1 if enable else 0))
 
 
 def chunk_fwd_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, N: int = -1,

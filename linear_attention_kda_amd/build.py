@@ -17,7 +17,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_PATH = os.path.join(PKG_DIR, "libkda.so")
 
-SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_prefill.hip", "kda_decode.hip", "kda_validate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON_FLAGS = [

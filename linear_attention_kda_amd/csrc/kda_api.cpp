@@ -7,7 +7,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <atomic>
 #include <cstdint>
+#include <cstdlib>
 
 #include "kda_launch.h"
 
@@ -33,6 +35,25 @@ float default_scale(float scale, int dk) {
   return scale > 0.f ? scale : 1.0f / std::sqrt((float)dk);
 }
 
+// Value checks: off unless KDA_VALIDATE is set to a nonzero integer in the
+// environment when the library is loaded, or kda_set_validation(1) is called.
+std::atomic<int> g_validate{[] {
+  const char *e = std::getenv("KDA_VALIDATE");
+  return e && std::atoi(e) != 0 ? 1 : 0;
+}()};
+
+// Runs the device checks when they are on.  KDA_OK when off or clean.
+kda_status check_values(const float *alpha, size_t n_alpha, kda_gate gate, const float *beta, size_t n_beta,
+                        const void *k, size_t n_krows, int d_k, kda_dtype dtype, const int32_t *cu, int n_seq,
+                        int total, hipStream_t stream) {
+  if (!g_validate.load(std::memory_order_relaxed)) return KDA_OK;
+  kda::ValidateArgs v{alpha, alpha ? n_alpha : 0, kda::gate_is_log(gate), beta, n_beta, k, n_krows, d_k,
+                      dtype == KDA_BF16, cu, n_seq, total};
+  unsigned bits = 0;
+  if (kda::run_validation(v, stream, &bits) != hipSuccess) return KDA_ERR_HIP;
+  return bits ? KDA_ERR_INVALID_VALUE : KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -50,8 +71,14 @@ const char *kda_status_string(kda_status s) {
     case KDA_ERR_ALIAS: return "the output overlaps an input";
     case KDA_ERR_HIP: return "the HIP runtime reported an error";
     case KDA_ERR_UNSUPPORTED_GATE: return "gate must be a kda_gate value (channel, scalar, none, log channel, log scalar)";
+    case KDA_ERR_INVALID_VALUE:
+      return "an input value is out of range (gate or beta outside [0, 1], a key of norm not 1, or bad cu_seqlens)";
   }
   return "unknown status";
+}
+
+int kda_set_validation(int enable) {
+  return g_validate.exchange(enable ? 1 : 0);
 }
 
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int N, kda_dtype dtype) {
@@ -117,6 +144,9 @@ kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v, cons
       if (overlaps(ro, r)) return KDA_ERR_ALIAS;
   }
   if (N == 0) return KDA_OK;
+  if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, ntok * H, k, ntok * H, d_k,
+                                         dtype, cu_seqlens, N, T, stream))
+    return st;
 
   kda::PrefillArgs a;
   a.q = q;
@@ -171,6 +201,9 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, co
                        range_of(beta, units * sizeof(float)), range_of(S, units * d_v * d_k * sizeof(float))};
   for (const Range &r : ins)
     if (overlaps(ro, r)) return KDA_ERR_ALIAS;
+  if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, units, k, units, d_k, dtype,
+                                         nullptr, 0, 0, stream))
+    return st;
 
   kda::DecodeArgs a;
   a.q = q;
@@ -222,6 +255,9 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
                          range_of(beta, toks * sizeof(float)), range_of(S_in, s_bytes), range_of(S_out, s_bytes)};
     for (const Range &r : ins)
       if (overlaps(ro, r)) return KDA_ERR_ALIAS;
+    if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, toks, k, toks, d_k, dtype,
+                                           nullptr, 0, 0, stream))
+      return st;
   }
 
   kda::DecodeArgs a;

@@ -96,6 +96,26 @@ struct PrefillArgs {
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 
+// Optional value checks (see kda_set_validation).  Bits of the result:
+constexpr unsigned kValidateAlpha = 1, kValidateBeta = 2, kValidateKey = 4, kValidateOffsets = 8;
+constexpr float kValidateKeyTol = 1.0f / 64;  // | |k|^2 - 1 | allowed
+struct ValidateArgs {
+  const float *alpha;   // null when the gate form reads none
+  size_t n_alpha;
+  bool gate_log;
+  const float *beta;
+  size_t n_beta;
+  const void *k;
+  size_t n_krows;
+  int dk;
+  bool k_bf16;
+  const int32_t *cu;    // null for a dense batch
+  int n_seq, total;
+};
+// Runs the checks on `stream`, waits for them and returns the violated
+// conditions in *bits (0: none).  Synchronises the stream.
+hipError_t run_validation(const ValidateArgs &v, hipStream_t stream, unsigned *bits);
+
 struct DecodeArgs {
   const void *q, *k, *v;
   const float *alpha, *beta;

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(kda):
 
 
 def test_status_strings(kda):
-    for s in range(11):
+    for s in range(12):
         assert kda.status_string(s) and kda.status_string(s) != "unknown status"
     assert kda.status_string(99) == "unknown status"
 
@@ -163,3 +163,14 @@ def test_decode_tokens_validation(kda):
     assert call(o=P(0x100000)) == 8                 # o overlaps a state
     assert call(gate=kda.KDA_GATE_SCALAR, alpha=None) == 1
     assert call(N=0) == 0
+
+
+def test_set_validation_toggles(kda):
+    # host-side switch only: no compute call is made here
+    prev = kda.set_validation(True)
+    try:
+        assert kda.set_validation(True) is True
+        assert kda.set_validation(False) is True
+        assert kda.set_validation(False) is False
+    finally:
+        kda.set_validation(prev)
