@@ -56,7 +56,8 @@ def prefill_bytes(B, T, H, dk, dv, esize=2, s0=False, gate_form="channel"):
     fp32, S_final (and S0) fp32."""
     tok = B * T * H
     alpha = {"channel": tok * dk * 4, "scalar": tok * 4, "none": 0,
-             "log_channel": tok * dk * 4, "log_scalar": tok * 4}[gate_form]
+             "log_channel": tok * dk * 4, "log_scalar": tok * 4,
+             "softplus_channel": tok * dk * 4, "softplus_scalar": tok * 4}[gate_form]
     return (tok * (2 * dk + 2 * dv) * esize + alpha + tok * 4
             + (2 if s0 else 1) * B * H * dv * dk * 4)
 
@@ -72,7 +73,7 @@ def decode_bytes(N, H, dk, dv, esize=2):
     return units * (2 * dv * dk * 4 + (2 * dk + 2 * dv) * esize + dk * 4 + 4)
 
 
-def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None):
+def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None, act=0):
     w = inputs.WORKLOADS["prefill"]
     B, T, H, dk, dv = w["B"], w["T"], w["H"], w["dk"], w["dv"]
     steps = steps or args.steps
@@ -95,7 +96,7 @@ def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None):
     def step(i):
         inp, ws, o, S = sets[i % NSETS]
         kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], gate=gate_form, out=o,
-                      S_final=S, workspace=ws)
+                      S_final=S, workspace=ws, act=act)
 
     for i in range(args.warmup):
         step(i)
@@ -254,7 +255,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=1024)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-gate-forms", action="store_true",
@@ -309,10 +310,14 @@ def main():
     if not args.no_gate_forms:
         # the same workload with the gate in other forms: one gate per (token,
         # head) (Gated DeltaNet), and per-channel gates given as log(alpha)
-        forms = (("scalar", "prefill_scalar_gate", "one fp32 gate per (token, head)"),
-                 ("log_channel", "prefill_log_gate", "per-channel fp32 gates given as log(alpha)"))
-        for form, key, what in forms:
-            sg = bench_prefill(args, torch, kda, inputs, gate_form=form, steps=max(20, args.steps // 4))
+        forms = (("scalar", "prefill_scalar_gate", "one fp32 gate per (token, head)", 0),
+                 ("log_channel", "prefill_log_gate", "per-channel fp32 gates given as log(alpha)", 0),
+                 ("softplus_channel", "prefill_fused_inputs",
+                  "raw q, k (SiLU and unit length applied on load), beta logits (sigmoid on load), "
+                  "per-channel gate logits g with alpha = exp(-softplus(g))",
+                  kda.KDA_ACT_QK_SILU_L2NORM | kda.KDA_ACT_BETA_SIGMOID))
+        for form, key, what, act in forms:
+            sg = bench_prefill(args, torch, kda, inputs, gate_form=form, steps=max(20, args.steps // 4), act=act)
             sb = prefill_bytes(sg["B"], sg["T"], sg["H"], sg["dk"], sg["dv"], gate_form=form)
             ach = sb / (sg["call_ms_mean"] * 1e-3) / 1e9
             result[key] = {

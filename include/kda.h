@@ -62,7 +62,8 @@ typedef enum {
   KDA_ERR_ALIAS = 8,               /* o overlaps an input                    */
   KDA_ERR_HIP = 9,                 /* the HIP runtime reported an error      */
   KDA_ERR_UNSUPPORTED_GATE = 10,   /* gate is not a kda_gate value           */
-  KDA_ERR_INVALID_VALUE = 11       /* a value check failed (validation on)   */
+  KDA_ERR_INVALID_VALUE = 11,      /* a value check failed (validation on)   */
+  KDA_ERR_UNSUPPORTED_ACT = 12     /* input_act has bits no kda_input_act has */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -79,13 +80,18 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  *   KDA_GATE_NONE         no forgetting; alpha is not read and may be NULL
  *   KDA_GATE_LOG_CHANNEL  as KDA_GATE_CHANNEL, holding log(alpha) <= 0
  *   KDA_GATE_LOG_SCALAR   as KDA_GATE_SCALAR, holding log(alpha) <= 0
+ *   KDA_GATE_SOFTPLUS_CHANNEL  as KDA_GATE_CHANNEL, holding logits g with
+ *                         alpha = exp(-softplus(g)) = 1 / (1 + e^g)
+ *   KDA_GATE_SOFTPLUS_SCALAR   the same, one logit per token and head
  * The log forms take the gate as the same page's section "Two schedules of
  * computation for one recurrence" describes the production pipeline taking
  * it (decays as logarithms); a model computing alpha = exp(-softplus(x))
  * passes -softplus(x) and skips the exponential pass over the gates.  The
  * kernels take exp on load (fp32, hardware exp2 of g log2 e, relative error
  * about |g| 2^-23; -inf gives a gate of exactly 0) and
- * then run unchanged.  Gates must lie in [0, 1] (log gates in [-inf, 0]);
+ * then run unchanged.  The softplus forms take the gate of the model code
+ * around the method (alpha = exp(-softplus(g)), the gate of the prefill
+ * workload's recipe) straight from its logits; large g gives 0.  Gates must lie in [0, 1] (log gates in [-inf, 0]);
  * values outside are not checked and give unspecified results.
  */
 typedef enum {
@@ -93,8 +99,26 @@ typedef enum {
   KDA_GATE_SCALAR = 1,
   KDA_GATE_NONE = 2,
   KDA_GATE_LOG_CHANNEL = 3,
-  KDA_GATE_LOG_SCALAR = 4
+  KDA_GATE_LOG_SCALAR = 4,
+  KDA_GATE_SOFTPLUS_CHANNEL = 5,
+  KDA_GATE_SOFTPLUS_SCALAR = 6
 } kda_gate;
+
+/*
+ * Activations applied to raw inputs as the kernels load them (bit flags),
+ * so a model needs no separate pass over q, k and beta.  They are those of
+ * the delta-rule block's model code on the pages (page "22580: from GPT-2
+ * to Kimi K3, explained", section "DeltaNet, or Fast Weight Programmers",
+ * the forward of the layer with a write strength): q and k
+ * go through SiLU and are then scaled to unit length over d_k per token and
+ * head (x / max(|x|, 1e-12)); beta goes through a sigmoid.  fp32 math on
+ * the hardware exponential, reciprocal and reciprocal square root.
+ */
+typedef enum {
+  KDA_ACT_NONE = 0,
+  KDA_ACT_QK_SILU_L2NORM = 1,
+  KDA_ACT_BETA_SIGMOID = 2
+} kda_input_act;
 
 /* Text for a status code (static storage; never NULL). */
 const char *kda_status_string(kda_status s);
@@ -194,6 +218,20 @@ kda_status kda_decode_step(const void *q, const void *k, const void *v,
  * the per-channel forms, [N, H] for the scalar forms, unused (may be NULL)
  * for KDA_GATE_NONE.  An unknown gate returns KDA_ERR_UNSUPPORTED_GATE.
  */
+/*
+ * kda_chunk_fwd_gated with input activations: input_act is a bitwise OR of
+ * kda_input_act flags, applied to the raw q, k and beta before the method
+ * (with KDA_ACT_QK_SILU_L2NORM, k need not be a unit vector).  Unknown bits
+ * return KDA_ERR_UNSUPPORTED_ACT.  Everything else as for kda_chunk_fwd.
+ */
+kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v,
+                            const float *alpha, kda_gate gate, const float *beta,
+                            unsigned input_act, const float *S0,
+                            const int32_t *cu_seqlens, int N, int B, int T, int H,
+                            int d_k, int d_v, float scale, kda_dtype dtype, void *o,
+                            float *S_final, void *workspace,
+                            size_t workspace_bytes, hipStream_t stream);
+
 kda_status kda_decode_step_gated(const void *q, const void *k, const void *v,
                                  const float *alpha, kda_gate gate,
                                  const float *beta, float *S, int N, int H,
@@ -225,6 +263,17 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v,
                              float *S_out, int N, int Tk, int H, int d_k,
                              int d_v, float scale, kda_dtype dtype, void *o,
                              hipStream_t stream);
+
+/*
+ * kda_decode_tokens with input activations (see kda_chunk_fwd_ex); with
+ * Tk = 1 and S_out == S_in it is a decode step on raw inputs.
+ */
+kda_status kda_decode_tokens_ex(const void *q, const void *k, const void *v,
+                                const float *alpha, kda_gate gate,
+                                const float *beta, unsigned input_act,
+                                const float *S_in, float *S_out, int N,
+                                int Tk, int H, int d_k, int d_v, float scale,
+                                kda_dtype dtype, void *o, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -24,14 +24,21 @@ KDA_GATE_SCALAR = 1
 KDA_GATE_NONE = 2
 KDA_GATE_LOG_CHANNEL = 3
 KDA_GATE_LOG_SCALAR = 4
+KDA_GATE_SOFTPLUS_CHANNEL = 5
+KDA_GATE_SOFTPLUS_SCALAR = 6
 GATES = {"channel": KDA_GATE_CHANNEL, "scalar": KDA_GATE_SCALAR, "none": KDA_GATE_NONE,
-         "log_channel": KDA_GATE_LOG_CHANNEL, "log_scalar": KDA_GATE_LOG_SCALAR}
-_PER_CHANNEL = (KDA_GATE_CHANNEL, KDA_GATE_LOG_CHANNEL)
-_PER_TOKEN = (KDA_GATE_SCALAR, KDA_GATE_LOG_SCALAR)
+         "log_channel": KDA_GATE_LOG_CHANNEL, "log_scalar": KDA_GATE_LOG_SCALAR,
+         "softplus_channel": KDA_GATE_SOFTPLUS_CHANNEL, "softplus_scalar": KDA_GATE_SOFTPLUS_SCALAR}
+_PER_CHANNEL = (KDA_GATE_CHANNEL, KDA_GATE_LOG_CHANNEL, KDA_GATE_SOFTPLUS_CHANNEL)
+_PER_TOKEN = (KDA_GATE_SCALAR, KDA_GATE_LOG_SCALAR, KDA_GATE_SOFTPLUS_SCALAR)
+# input activations (kda_input_act flags)
+KDA_ACT_QK_SILU_L2NORM = 1
+KDA_ACT_BETA_SIGMOID = 2
 
 # names exported by include/kda.h
 EXPORTED = ("kda_status_string", "kda_set_validation", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
-            "kda_chunk_fwd_gated", "kda_decode_step", "kda_decode_step_gated", "kda_decode_tokens")
+            "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_decode_step", "kda_decode_step_gated",
+            "kda_decode_tokens", "kda_decode_tokens_ex")
 KDA_ERR_INVALID_VALUE = 11
 
 
@@ -67,6 +74,12 @@ def _load() -> ctypes.CDLL:
     lib.kda_decode_tokens.restype = i32
     lib.kda_decode_tokens.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32,
                                       vp, vp]
+    lib.kda_chunk_fwd_ex.restype = i32
+    lib.kda_chunk_fwd_ex.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, i32, i32, i32, i32, i32,
+                                     i32, f32, i32, vp, vp, vp, sz, vp]
+    lib.kda_decode_tokens_ex.restype = i32
+    lib.kda_decode_tokens_ex.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, i32, i32, i32, i32,
+                                         i32, f32, i32, vp, vp]
     lib.kda_set_validation.restype = i32
     lib.kda_set_validation.argtypes = [i32]
     return lib
@@ -134,9 +147,11 @@ def _stream(device):
 
 
 def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gate=None, out=None,
-              S_final=None, workspace=None):
+              S_final=None, workspace=None, act=0):
     """Chunked prefill.  Returns (o, S_final).
 
+    ``act``: kda_input_act flags (KDA_ACT_QK_SILU_L2NORM, KDA_ACT_BETA_SIGMOID)
+    applied to the raw q, k and beta as the kernels load them.
     Dense batch: q, k [B, T, H, d_k]; v [B, T, H, d_v]; beta [B, T, H].
     alpha: [B, T, H, d_k] (gate "channel"), [B, T, H] (gate "scalar"), or
     None (gate "none"); ``gate`` defaults to what alpha's shape says.
@@ -188,20 +203,27 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gat
     ws_need = chunk_fwd_workspace_size(B, T, H, d_k, d_v, N if cu_seqlens is not None else -1, dt)
     if workspace is None or workspace.numel() < ws_need:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
-    st = lib.kda_chunk_fwd_gated(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), _ptr(S0),
-                                 _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
-                                 float(scale) if scale else 0.0, dt, _ptr(out), _ptr(S_final),
-                                 _ptr(workspace), workspace.numel(), _stream(dev))
+    st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), int(act), _ptr(S0),
+                              _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
+                              float(scale) if scale else 0.0, dt, _ptr(out), _ptr(S_final),
+                              _ptr(workspace), workspace.numel(), _stream(dev))
     if st != 0:
-        raise KdaError("kda_chunk_fwd_gated", st)
+        raise KdaError("kda_chunk_fwd_ex", st)
     return out, S_final
 
 
-def decode_step(q, k, v, alpha, beta, S, scale=None, *, gate=None, out=None):
+def decode_step(q, k, v, alpha, beta, S, scale=None, *, gate=None, out=None, act=0):
     """One token for N sequences: q, k [N, H, d_k]; v [N, H, d_v]; beta [N, H];
     alpha [N, H, d_k] (gate "channel"), [N, H] ("scalar") or None ("none");
-    S [N, H, d_v, d_k] fp32, updated in place.  Returns o."""
+    S [N, H, d_v, d_k] fp32, updated in place.  Returns o.  With input
+    activations (``act``) the step runs as one token of decode_tokens."""
     import torch
+    if act:
+        o, _ = decode_tokens(q.unsqueeze(1), k.unsqueeze(1), v.unsqueeze(1),
+                             None if alpha is None else alpha.unsqueeze(1), beta.unsqueeze(1), S, S_out=S,
+                             scale=scale, gate=gate, act=act,
+                             out=None if out is None else out.unsqueeze(1))
+        return o.squeeze(1)
     dt = _dtype_code(q)
     gc = _gate_code(gate, alpha, q)
     if gc == KDA_GATE_NONE:
@@ -227,13 +249,14 @@ def decode_step(q, k, v, alpha, beta, S, scale=None, *, gate=None, out=None):
     return out
 
 
-def decode_tokens(q, k, v, alpha, beta, S_in, S_out=None, scale=None, *, gate=None, out=None):
+def decode_tokens(q, k, v, alpha, beta, S_in, S_out=None, scale=None, *, gate=None, out=None, act=0):
     """Tk tokens per sequence in one launch: q, k [N, Tk, H, d_k]; v
     [N, Tk, H, d_v]; beta [N, Tk, H]; alpha [N, Tk, H, d_k] ("channel"),
     [N, Tk, H] ("scalar") or None ("none").  The state is read from S_in
     ([N, H, d_v, d_k] fp32) and the state after the last token is written to
     S_out: a new tensor by default, so S_in stays the checkpoint; pass
-    S_out=S_in to update in place.  Returns (o [N, Tk, H, d_v], S_out)."""
+    S_out=S_in to update in place.  ``act`` as for chunk_fwd.  Returns
+    (o [N, Tk, H, d_v], S_out)."""
     import torch
     dt = _dtype_code(q)
     gc = _gate_code(gate, alpha, q)
@@ -261,9 +284,9 @@ def decode_tokens(q, k, v, alpha, beta, S_in, S_out=None, scale=None, *, gate=No
         raise ValueError("S_out must be a contiguous, 16-byte aligned float32 tensor shaped like S_in")
     if out is None:
         out = torch.empty((N, Tk, H, d_v), dtype=v.dtype, device=q.device)
-    st = lib.kda_decode_tokens(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), _ptr(S_in),
-                               _ptr(S_out), N, Tk, H, d_k, d_v, float(scale) if scale else 0.0, dt,
-                               _ptr(out), _stream(q.device))
+    st = lib.kda_decode_tokens_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), int(act),
+                                  _ptr(S_in), _ptr(S_out), N, Tk, H, d_k, d_v, float(scale) if scale else 0.0,
+                                  dt, _ptr(out), _stream(q.device))
     if st != 0:
-        raise KdaError("kda_decode_tokens", st)
+        raise KdaError("kda_decode_tokens_ex", st)
     return out, S_out

@@ -16,9 +16,10 @@
 namespace {
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+constexpr unsigned kActAll = KDA_ACT_QK_SILU_L2NORM | KDA_ACT_BETA_SIGMOID;
 bool valid_gate(kda_gate g) {
   return g == KDA_GATE_CHANNEL || g == KDA_GATE_SCALAR || g == KDA_GATE_NONE || g == KDA_GATE_LOG_CHANNEL ||
-         g == KDA_GATE_LOG_SCALAR;
+         g == KDA_GATE_LOG_SCALAR || g == KDA_GATE_SOFTPLUS_CHANNEL || g == KDA_GATE_SOFTPLUS_SCALAR;
 }
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -44,11 +45,13 @@ std::atomic<int> g_validate{[] {
 
 // Runs the device checks when they are on.  KDA_OK when off or clean.
 kda_status check_values(const float *alpha, size_t n_alpha, kda_gate gate, const float *beta, size_t n_beta,
-                        const void *k, size_t n_krows, int d_k, kda_dtype dtype, const int32_t *cu, int n_seq,
-                        int total, hipStream_t stream) {
+                        unsigned act, const void *k, size_t n_krows, int d_k, kda_dtype dtype, const int32_t *cu,
+                        int n_seq, int total, hipStream_t stream) {
   if (!g_validate.load(std::memory_order_relaxed)) return KDA_OK;
-  kda::ValidateArgs v{alpha, alpha ? n_alpha : 0, kda::gate_is_log(gate), beta, n_beta, k, n_krows, d_k,
-                      dtype == KDA_BF16, cu, n_seq, total};
+  const int range = kda::gate_is_log(gate) ? 1 : kda::gate_is_softplus(gate) ? 2 : 0;
+  // keys normalised on load need no unit norm
+  kda::ValidateArgs v{alpha, alpha ? n_alpha : 0, range, beta, n_beta, (act & kda::kActBeta) != 0, k,
+                      (act & kda::kActQK) ? 0 : n_krows, d_k, dtype == KDA_BF16, cu, n_seq, total};
   unsigned bits = 0;
   if (kda::run_validation(v, stream, &bits) != hipSuccess) return KDA_ERR_HIP;
   return bits ? KDA_ERR_INVALID_VALUE : KDA_OK;
@@ -73,6 +76,7 @@ const char *kda_status_string(kda_status s) {
     case KDA_ERR_UNSUPPORTED_GATE: return "gate must be a kda_gate value (channel, scalar, none, log channel, log scalar)";
     case KDA_ERR_INVALID_VALUE:
       return "an input value is out of range (gate or beta outside [0, 1], a key of norm not 1, or bad cu_seqlens)";
+    case KDA_ERR_UNSUPPORTED_ACT: return "input_act has bits that are not kda_input_act flags";
   }
   return "unknown status";
 }
@@ -105,7 +109,16 @@ kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v, cons
                                const float *beta, const float *S0, const int32_t *cu_seqlens, int N, int B, int T,
                                int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o, float *S_final,
                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  return kda_chunk_fwd_ex(q, k, v, alpha, gate, beta, KDA_ACT_NONE, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale,
+                          dtype, o, S_final, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                            const float *beta, unsigned input_act, const float *S0, const int32_t *cu_seqlens, int N,
+                            int B, int T, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
+                            float *S_final, void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
+  if (input_act & ~kActAll) return KDA_ERR_UNSUPPORTED_ACT;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
   if (B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
@@ -144,8 +157,8 @@ kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v, cons
       if (overlaps(ro, r)) return KDA_ERR_ALIAS;
   }
   if (N == 0) return KDA_OK;
-  if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, ntok * H, k, ntok * H, d_k,
-                                         dtype, cu_seqlens, N, T, stream))
+  if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, ntok * H, input_act, k,
+                                         ntok * H, d_k, dtype, cu_seqlens, N, T, stream))
     return st;
 
   kda::PrefillArgs a;
@@ -154,6 +167,7 @@ kda_status kda_chunk_fwd_gated(const void *q, const void *k, const void *v, cons
   a.v = v;
   a.alpha = alpha;
   a.gate = (int)gate;
+  a.act = input_act;
   a.beta = beta;
   a.S0 = S0;
   a.cu_seqlens = cu_seqlens;
@@ -201,8 +215,8 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, co
                        range_of(beta, units * sizeof(float)), range_of(S, units * d_v * d_k * sizeof(float))};
   for (const Range &r : ins)
     if (overlaps(ro, r)) return KDA_ERR_ALIAS;
-  if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, units, k, units, d_k, dtype,
-                                         nullptr, 0, 0, stream))
+  if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, units, 0, k, units, d_k,
+                                         dtype, nullptr, 0, 0, stream))
     return st;
 
   kda::DecodeArgs a;
@@ -211,6 +225,7 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, co
   a.v = v;
   a.alpha = alpha;
   a.gate = (int)gate;
+  a.act = 0;
   a.beta = beta;
   a.S_in = S;
   a.S = S;
@@ -228,7 +243,16 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, co
 kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
                              const float *beta, const float *S_in, float *S_out, int N, int Tk, int H, int d_k,
                              int d_v, float scale, kda_dtype dtype, void *o, hipStream_t stream) {
+  return kda_decode_tokens_ex(q, k, v, alpha, gate, beta, KDA_ACT_NONE, S_in, S_out, N, Tk, H, d_k, d_v, scale,
+                              dtype, o, stream);
+}
+
+kda_status kda_decode_tokens_ex(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                                const float *beta, unsigned input_act, const float *S_in, float *S_out, int N,
+                                int Tk, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
+                                hipStream_t stream) {
   if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
+  if (input_act & ~kActAll) return KDA_ERR_UNSUPPORTED_ACT;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
   if (N < 0 || H <= 0 || Tk < 0) return KDA_ERR_BAD_SHAPE;
@@ -255,8 +279,8 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
                          range_of(beta, toks * sizeof(float)), range_of(S_in, s_bytes), range_of(S_out, s_bytes)};
     for (const Range &r : ins)
       if (overlaps(ro, r)) return KDA_ERR_ALIAS;
-    if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, toks, k, toks, d_k, dtype,
-                                           nullptr, 0, 0, stream))
+    if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, toks, input_act, k, toks,
+                                           d_k, dtype, nullptr, 0, 0, stream))
       return st;
   }
 
@@ -266,6 +290,7 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
   a.v = v;
   a.alpha = alpha;
   a.gate = (int)gate;
+  a.act = input_act;
   a.beta = beta;
   a.S_in = S_in;
   a.S = S_out;

@@ -39,6 +39,7 @@ struct DecodeKArgs {
   float *S_out;  // may be S_in
   void *o;
   float scale;
+  unsigned act;    // kAct* input activations
   unsigned units;  // sequences x heads (< 2^31)
   int H, Tk;     // heads; tokens per sequence (inputs are [N, Tk, H, .])
 };
@@ -58,30 +59,6 @@ __device__ __forceinline__ void load4<float>(const float *p, float *out) {
   const f32x4 x = *reinterpret_cast<const f32x4 *>(p);
 #pragma unroll
   for (int i = 0; i < 4; ++i) out[i] = x[i];
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over aligned groups of LPR lanes, every lane receiving its group's
-// sum, in registers: DPP quad permutes for lane distance 1 and 2, the half-row
-// and row mirrors for 4 and 8 (once the smaller groups hold equal sums a
-// mirror reads the other half), and the row swap of gfx950 for 16.
-template <int LPR>
-__device__ __forceinline__ float group_sum(float x) {
-  static_assert(LPR >= 1 && LPR <= 32, "group of at most 32 lanes");
-  if constexpr (LPR >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
-  if constexpr (LPR >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
-  if constexpr (LPR >= 8) x += dpp<0x141>(x);   // row_half_mirror
-  if constexpr (LPR >= 16) x += dpp<0x140>(x);  // row_mirror
-  if constexpr (LPR >= 32) {
-    // rows 2i and 2i+1 trade places between the two results
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-  }
-  return x;
 }
 
 // Work split: a unit's state is NACC wave-wide KiB accesses.  A workgroup of
@@ -201,7 +178,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
       if constexpr (gate_is_log(GATE)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) y.al[j] = gate_from_log(y.al[j]);
+      } else if constexpr (gate_is_softplus(GATE)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) y.al[j] = gate_from_softplus_logit(y.al[j]);
       }
+      if (a.act & kActQK) {  // q, k <- SiLU, then unit length over d_k (LPR lanes)
+        float sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y.kk[j] = silu_f(y.kk[j]);
+          y.qq[j] = silu_f(y.qq[j]);
+          sk += y.kk[j] * y.kk[j];
+          sq += y.qq[j] * y.qq[j];
+        }
+        const float rk = inv_norm(group_sum<LPR>(sk)), rq = inv_norm(group_sum<LPR>(sq));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          y.kk[j] *= rk;
+          y.qq[j] *= rq;
+        }
+      }
+      if (a.act & kActBeta) y.beta = sigmoid_f(y.beta);
       E *orow = reinterpret_cast<E *>(a.o) + tok_index(t) * DV;
       float kq = 0.f;
 #pragma unroll
@@ -272,13 +269,16 @@ hipError_t run_decode_gate(const DecodeArgs &a, const DecodeKArgs &ka, hipStream
     case kGateNone: return run_decode_dv<DK, E, kGateNone>(a, ka, s);
     case kGateLogChannel: return run_decode_dv<DK, E, kGateLogChannel>(a, ka, s);
     case kGateLogScalar: return run_decode_dv<DK, E, kGateLogScalar>(a, ka, s);
+    case kGateSoftplusChannel: return run_decode_dv<DK, E, kGateSoftplusChannel>(a, ka, s);
+    case kGateSoftplusScalar: return run_decode_dv<DK, E, kGateSoftplusScalar>(a, ka, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename E>
 hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
-  DecodeKArgs ka{a.q, a.k, a.v, a.alpha, a.beta, a.S_in, a.S, a.o, a.scale, (unsigned)((size_t)a.N * a.H), a.H, a.Tk};
+  DecodeKArgs ka{a.q, a.k, a.v, a.alpha, a.beta, a.S_in, a.S, a.o, a.scale, a.act, (unsigned)((size_t)a.N * a.H),
+                 a.H, a.Tk};
   switch (a.dk) {
     case 16: return run_decode_gate<16, E>(a, ka, s);
     case 32: return run_decode_gate<32, E>(a, ka, s);

@@ -15,12 +15,47 @@ typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 constexpr int kChunk = 64;   // tokens per chunk of the chunkwise schedule
 constexpr int kThreads = 256;
 
-// A gate from its logarithm: e^g = 2^(g log2 e) on the hardware exponential
-// (v_exp_f32).  Rounding g log2 e costs a relative error of about |g| 2^-24
-// on top of the instruction's own; g = -inf gives exactly 0.
-__device__ __forceinline__ float gate_from_log(float g) {
-  return __builtin_amdgcn_exp2f(g * 1.4426950408889634f);
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
 }
+
+// Sum over aligned groups of LPR lanes, every lane receiving its group's
+// sum, in registers: DPP quad permutes for lane distance 1 and 2, the half-row
+// and row mirrors for 4 and 8 (once the smaller groups hold equal sums a
+// mirror reads the other half), and the row swap of gfx950 for 16.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LPR >= 1 && LPR <= 32, "group of at most 32 lanes");
+  if constexpr (LPR >= 2) x += dpp<0xB1>(x);    // quad_perm [1,0,3,2]
+  if constexpr (LPR >= 4) x += dpp<0x4E>(x);    // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 8) x += dpp<0x141>(x);   // row_half_mirror
+  if constexpr (LPR >= 16) x += dpp<0x140>(x);  // row_mirror
+  if constexpr (LPR >= 32) {
+    // rows 2i and 2i+1 trade places between the two results
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  }
+  return x;
+}
+
+// e^x = 2^(x log2 e) on the hardware exponential (v_exp_f32).  Rounding
+// x log2 e costs a relative error of about |x| 2^-24 on top of the
+// instruction's own; -inf gives exactly 0.
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+
+// A gate from its logarithm.
+__device__ __forceinline__ float gate_from_log(float g) { return fast_exp(g); }
+
+// A gate from a softplus logit: exp(-softplus(g)) = 1 / (1 + e^g), on the
+// hardware reciprocal; large g gives 0, very negative g gives 1.
+__device__ __forceinline__ float gate_from_softplus_logit(float g) { return __builtin_amdgcn_rcpf(1.f + fast_exp(g)); }
+
+__device__ __forceinline__ float sigmoid_f(float x) { return __builtin_amdgcn_rcpf(1.f + fast_exp(-x)); }
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+// 1 / max(|x|, 1e-12) from a sum of squares (the normalisation of a vector).
+__device__ __forceinline__ float inv_norm(float sumsq) { return __builtin_amdgcn_rsqf(fmaxf(sumsq, 1e-24f)); }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }

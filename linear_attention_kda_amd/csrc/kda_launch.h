@@ -73,17 +73,27 @@ inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
   return P;
 }
 
-// gate kinds (kda_gate): 0 per key channel, 1 one per token and head, 2 none
-constexpr int kGateChannel = 0, kGateScalar = 1, kGateNone = 2, kGateLogChannel = 3, kGateLogScalar = 4;
+// gate forms (kda_gate): gates, their logarithms or softplus logits, one per
+// key channel or one per token and head, or none
+constexpr int kGateChannel = 0, kGateScalar = 1, kGateNone = 2, kGateLogChannel = 3, kGateLogScalar = 4,
+              kGateSoftplusChannel = 5, kGateSoftplusScalar = 6;
 // gate forms that read one value per key channel / one per token and head
-constexpr bool gate_per_channel(int g) { return g == kGateChannel || g == kGateLogChannel; }
-constexpr bool gate_per_token(int g) { return g == kGateScalar || g == kGateLogScalar; }
+constexpr bool gate_per_channel(int g) {
+  return g == kGateChannel || g == kGateLogChannel || g == kGateSoftplusChannel;
+}
+constexpr bool gate_per_token(int g) { return g == kGateScalar || g == kGateLogScalar || g == kGateSoftplusScalar; }
 constexpr bool gate_is_log(int g) { return g == kGateLogChannel || g == kGateLogScalar; }
+constexpr bool gate_is_softplus(int g) { return g == kGateSoftplusChannel || g == kGateSoftplusScalar; }
+
+// input activations applied on load (kda_input_act bits)
+constexpr unsigned kActQK = 1;    // q, k <- L2-normalised SiLU, per token and head
+constexpr unsigned kActBeta = 2;  // beta <- sigmoid(beta)
 
 struct PrefillArgs {
   const void *q, *k, *v;
   const float *alpha, *beta, *S0;
   int gate;
+  unsigned act;               // kAct* bits
   const int32_t *cu_seqlens;  // device, or null for a dense batch
   void *o;
   float *S_final;
@@ -102,11 +112,12 @@ constexpr float kValidateKeyTol = 1.0f / 64;  // | |k|^2 - 1 | allowed
 struct ValidateArgs {
   const float *alpha;   // null when the gate form reads none
   size_t n_alpha;
-  bool gate_log;
+  int gate_range;       // 0: gates in [0, 1]; 1: log gates <= 0; 2: any number (logits)
   const float *beta;
   size_t n_beta;
+  bool beta_logits;     // beta is a logit (sigmoid on load): any number
   const void *k;
-  size_t n_krows;
+  size_t n_krows;       // 0 when k is normalised on load
   int dk;
   bool k_bf16;
   const int32_t *cu;    // null for a dense batch
@@ -120,6 +131,7 @@ struct DecodeArgs {
   const void *q, *k, *v;
   const float *alpha, *beta;
   int gate;
+  unsigned act;       // kAct* bits
   const float *S_in;  // state read
   float *S;           // state written (may be S_in)
   void *o;

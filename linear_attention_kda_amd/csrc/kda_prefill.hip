@@ -162,6 +162,7 @@ struct PrepKArgs {
   const void *q, *k;
   const float *alpha, *beta;
   int gate;  // a kGate* form: alpha [.., H, d_k] per channel, [.., H] per token, unused for none
+  unsigned act;  // kAct* input activations
   ChunkSource src;
   int H;
   float scale;
@@ -264,6 +265,13 @@ __device__ __forceinline__ void tile64_out(E *dst, const float *src, const float
   }
 }
 
+// The gate a stored value stands for, per gate form.
+template <int GATE> __device__ __forceinline__ float gate_value(float x) {
+  if constexpr (gate_is_log(GATE)) return gate_from_log(x);
+  else if constexpr (gate_is_softplus(GATE)) return gate_from_softplus_logit(x);
+  else return x;
+}
+
 // Four elements of E from / to fp32.
 template <typename E> struct Four;
 template <> struct Four<bf16> {
@@ -350,7 +358,7 @@ __device__ __forceinline__ void tile_ij(int p, int &I, int &J) {
 // Exact path (a chunk with some D_{0:63} below 2^-100, e.g. a gate of 0):
 // no division at all.  Kbnd and Qbnd as above, Kend from suffix products, and
 // R and A summed channel by channel with running products of the gates.
-template <int DK, typename E, int GATE>
+template <int DK, typename E, int GATE, bool ACTQK>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrepKArgs a) {
   typedef LdsFrag<E, DK, 64> LK;   // Kbnd, Qbnd, k / a: rows = tokens, K = d_k
   typedef LdsFrag<E, 64, DK> LT;   // Kend^T: rows = channels, K = tokens
@@ -367,6 +375,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   static_assert(ARENA >= 4 * DK * 4, "the gate totals live at the start of the arena");
   __shared__ __attribute__((aligned(16))) char arena[ARENA];
   __shared__ float sBeta[kChunk];
+  __shared__ float sInvNorm[2][kChunk];  // 1/|SiLU(k)|, 1/|SiLU(q)| per token (input activation only)
 
   const int h = blockIdx.y;
   const long long c = blockIdx.x;
@@ -384,18 +393,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // gates of channels ch0 .. ch0+3 of token t0 + tk (tk a valid chunk index):
   // per channel, one shared value, or none, given as gates or as their
   // logarithms (see kda_gate)
-  auto gate4 = [&](int tk, int ch0, float *al, bool nontemporal) {
+  // (raw = true: the stored values, for gate_value<GATE> later)
+  auto gate4 = [&](int tk, int ch0, float *al, bool nontemporal, bool raw = false) {
     const size_t tok = (size_t)t0 + tk;
     if constexpr (gate_per_channel(GATE)) {
       const f32x4 *p = reinterpret_cast<const f32x4 *>(a.alpha + tok * hs + (size_t)h * DK + ch0);
       const f32x4 x = nontemporal ? __builtin_nontemporal_load(p) : *p;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = gate_is_log(GATE) ? gate_from_log(x[j]) : x[j];
+      for (int j = 0; j < 4; ++j) al[j] = raw ? x[j] : gate_value<GATE>(x[j]);
     } else {
       float x = 1.f;
       if constexpr (gate_per_token(GATE)) {
         x = a.alpha[tok * a.H + h];
-        if constexpr (gate_is_log(GATE)) x = gate_from_log(x);
+        if (!raw) x = gate_value<GATE>(x);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) al[j] = x;
@@ -409,7 +419,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // first write of the operand images, which reuse this space
   float *sTau = reinterpret_cast<float *>(arena);
 
-  if (tid < kChunk) sBeta[tid] = tid < L ? a.beta[(size_t)(t0 + tid) * a.H + h] : 0.f;
+  if (tid < kChunk) {
+    float b = 0.f;
+    if (tid < L) {
+      b = a.beta[(size_t)(t0 + tid) * a.H + h];
+      if (a.act & kActBeta) b = sigmoid_f(b);
+    }
+    sBeta[tid] = b;
+  }
 
   // ---- loads and in-block prefix products.  Padded tokens (index >= L)
   // take q = k = 0 and alpha = 1; their loads read a valid token instead.
@@ -425,11 +442,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const bool live = tok < L;
     const size_t off = base + (size_t)min(tok, L - 1) * hs;
     float al[4];
-    gate4(min(tok, L - 1), c0, al, true);
+    gate4(min(tok, L - 1), c0, al, true, true);   // converted below, after the q, k activation
     kraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(k + off));
     qraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(q + off));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pa[u][j] = live ? al[j] : 1.f;
+    for (int j = 0; j < 4; ++j) pa[u][j] = al[j];
+  }
+  // optional input activation: q, k <- SiLU, then unit length over the d_k
+  // channels of the token (CG lanes hold one token's channels)
+  if constexpr (ACTQK) {
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      float kx[4], qx[4], sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kx[j] = silu_f((float)kraw[u][j]);
+        qx[j] = silu_f((float)qraw[u][j]);
+        sk += kx[j] * kx[j];
+        sq += qx[j] * qx[j];
+      }
+      const float rk = inv_norm(group_sum<CG>(sk)), rq = inv_norm(group_sum<CG>(sq));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kx[j] *= rk;
+        qx[j] *= rq;
+      }
+      kraw[u] = F4::pack(kx);
+      qraw[u] = F4::pack(qx);
+      // for the exact path, which reads q and k again from memory
+      if (cg == 0) {
+        sInvNorm[0][tb0 + u] = rk;
+        sInvNorm[1][tb0 + u] = rq;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one token at a time: bounds the live values
+    }
   }
   // k (or q) of token u, channel j, zero for padded tokens
   auto kval = [&](int u, int j) {
@@ -446,10 +492,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     float run = 1.f;
 #pragma unroll
     for (int u = 0; u < TPL; ++u) {
-      run *= pa[u][j];
+      run *= tb0 + u < L ? gate_value<GATE>(pa[u][j]) : 1.f;
       pa[u][j] = run;
     }
     tot[j] = run;
+    if constexpr (gate_is_softplus(GATE)) __builtin_amdgcn_sched_barrier(0);
   }
   // exclusive product over the lanes of earlier sub-ranges of the block
   // (lanes cg + CG th' for th' < th); Hillis-Steele scan with stride CG
@@ -647,48 +694,64 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       }
     }
   } else {
-    // R and A channel by channel: thread (j, quarter) runs D_{j+1:i} over i
-    // for its quarter of the channels; the four quarters are summed across
-    // neighbouring lanes.
-    constexpr int CQ = DK / 4;
+    // R and A channel by channel: thread (j, part) runs D_{j+1:i} over i for
+    // CQ channels; the NQ parts of row j sit in neighbouring lanes and are
+    // summed across them.  At most 16 channels per lane keep the running
+    // products in few registers (this path is rare: with more channels per
+    // lane its registers would push values of the common path into
+    // scratch); with NQ > 4 the 64 rows take NQ/4 passes.
+    constexpr int CQ = DK / 4 > 16 ? 16 : DK / 4;
+    constexpr int NQ = DK / CQ;          // lanes per row
+    constexpr int JP = kThreads / NQ;    // rows per pass
     float *sA = reinterpret_cast<float *>(sX);
-    const int j = tid >> 2, qd = tid & 3;
-    const size_t cb = (size_t)t0 * hs + (size_t)h * DK + qd * CQ;
-    float kj[CQ], rho[CQ];
-#pragma unroll
-    for (int cc = 0; cc < CQ; cc += 4) {
-      F4::load(k + cb + (size_t)min(j, L - 1) * hs + cc, kj + cc);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kj[cc + e] = j < L ? kj[cc + e] : 0.f;
-        rho[cc + e] = 1.f;
-      }
-    }
-    for (int i = 0; i < kChunk; ++i) {
-      const bool live = i < L;
-      const size_t off = cb + (size_t)min(i, L - 1) * hs;
-      float racc = 0.f, aacc = 0.f;
+    const int qd = tid % NQ;
+#pragma unroll 1
+    for (int jb = 0; jb < kChunk; jb += JP) {
+      const int j = jb + tid / NQ;
+      const size_t cb = (size_t)t0 * hs + (size_t)h * DK + qd * CQ;
+      float kj[CQ], rho[CQ];
 #pragma unroll
       for (int cc = 0; cc < CQ; cc += 4) {
-        float al[4], kx[4], qx[4];
-        gate4(min(i, L - 1), qd * CQ + cc, al, false);
-        F4::load(k + off + cc, kx);
-        F4::load(q + off + cc, qx);
+        F4::load(k + cb + (size_t)min(j, L - 1) * hs + cc, kj + cc);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          if (i > j) rho[cc + e] *= live ? al[e] : 1.f;
-          const float wgt = i >= j ? kj[cc + e] * rho[cc + e] : 0.f;
-          racc += (live ? kx[e] : 0.f) * wgt;
-          aacc += (live ? qx[e] : 0.f) * wgt;
+          if constexpr (ACTQK) kj[cc + e] = (float)(E)(silu_f(kj[cc + e]) * sInvNorm[0][min(j, L - 1)]);
+          kj[cc + e] = j < L ? kj[cc + e] : 0.f;
+          rho[cc + e] = 1.f;
         }
       }
-      racc += __shfl_xor(racc, 1);
-      aacc += __shfl_xor(aacc, 1);
-      racc += __shfl_xor(racc, 2);
-      aacc += __shfl_xor(aacc, 2);
-      if (qd == 0) {
-        sR[i * LDR + j] = i > j ? sBeta[i] * racc : 0.f;
-        sA[i * LDR + j] = i >= j ? a.scale * aacc : 0.f;
+      for (int i = 0; i < kChunk; ++i) {
+        const bool live = i < L;
+        const size_t off = cb + (size_t)min(i, L - 1) * hs;
+        float racc = 0.f, aacc = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CQ; cc += 4) {
+          float al[4], kx[4], qx[4];
+          gate4(min(i, L - 1), qd * CQ + cc, al, false);
+          F4::load(k + off + cc, kx);
+          F4::load(q + off + cc, qx);
+          if constexpr (ACTQK) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // rounded to E like the activated values of the fast path
+              kx[e] = (float)(E)(silu_f(kx[e]) * sInvNorm[0][min(i, L - 1)]);
+              qx[e] = (float)(E)(silu_f(qx[e]) * sInvNorm[1][min(i, L - 1)]);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (i > j) rho[cc + e] *= live ? al[e] : 1.f;
+            const float wgt = i >= j ? kj[cc + e] * rho[cc + e] : 0.f;
+            racc += (live ? kx[e] : 0.f) * wgt;
+            aacc += (live ? qx[e] : 0.f) * wgt;
+          }
+        }
+        racc = group_sum<NQ>(racc);
+        aacc = group_sum<NQ>(aacc);
+        if (qd == 0) {
+          sR[i * LDR + j] = i > j ? sBeta[i] * racc : 0.f;
+          sA[i * LDR + j] = i >= j ? a.scale * aacc : 0.f;
+        }
       }
     }
     // Kend^T straight to the record (scattered; this path is rare)
@@ -1260,6 +1323,35 @@ void chunk_scan_kernel(ScanKArgs a) {
       *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
 }
 
+// The prep kernel for a gate form, with or without the q, k activation.
+template <int DK, typename E, bool ACTQK>
+void launch_prep(int gate, dim3 grid, hipStream_t stream, const PrepKArgs &pa) {
+  switch (gate) {
+    case kGateScalar:
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+      break;
+    case kGateNone:
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+      break;
+    case kGateLogChannel:
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogChannel, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+      break;
+    case kGateLogScalar:
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogScalar, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+      break;
+    case kGateSoftplusChannel:
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusChannel, ACTQK>), grid, dim3(kThreads), 0, stream,
+                         pa);
+      break;
+    case kGateSoftplusScalar:
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusScalar, ACTQK>), grid, dim3(kThreads), 0, stream,
+                         pa);
+      break;
+    default:
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+  }
+}
+
 // LDS held by one stage (record + value slices) of a scan configuration.
 template <int DK, typename E> constexpr bool scan_stage_fits(int nt, int cw) {
   return RecordShape<DK, E>::bytes + cw * 64 * 16 * nt * (int)sizeof(E) <= 160 * 1024 - 1024;
@@ -1299,6 +1391,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.k = a.k;
     pa.alpha = a.alpha;
     pa.gate = a.gate;
+    pa.act = a.act;
     pa.beta = a.beta;
     pa.src.T = a.T;
     pa.src.nct = nct;
@@ -1311,22 +1404,10 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.ws_records = records;
     pa.lay = lay;
     const dim3 pg((unsigned)P.max_chunks, a.H);
-    switch (a.gate) {
-      case kGateScalar:
-        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar>), pg, dim3(kThreads), 0, stream, pa);
-        break;
-      case kGateNone:
-        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone>), pg, dim3(kThreads), 0, stream, pa);
-        break;
-      case kGateLogChannel:
-        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogChannel>), pg, dim3(kThreads), 0, stream, pa);
-        break;
-      case kGateLogScalar:
-        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogScalar>), pg, dim3(kThreads), 0, stream, pa);
-        break;
-      default:
-        hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel>), pg, dim3(kThreads), 0, stream, pa);
-    }
+    if (a.act & kActQK)
+      launch_prep<DK, E, true>(a.gate, pg, stream, pa);
+    else
+      launch_prep<DK, E, false>(a.gate, pg, stream, pa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -20,9 +20,10 @@ __device__ unsigned g_validate_bits;
 struct ValidateKArgs {
   const float *alpha;
   size_t n_alpha;
-  int gate_log;          // alpha holds log(gate): must be <= 0 (-inf allowed)
+  int gate_range;        // 0: in [0, 1]; 1: log gates, <= 0 (-inf allowed); 2: logits, any number
   const float *beta;
   size_t n_beta;
+  int beta_logits;       // beta goes through a sigmoid: any number
   const void *k;
   size_t n_krows;        // rows of d_k elements
   int dk, k_bf16;
@@ -41,12 +42,12 @@ __global__ __launch_bounds__(kThreads) void validate_kernel(ValidateKArgs a) {
   unsigned bits = 0;
   for (size_t i = tid; i < a.n_alpha; i += stride) {
     const float x = a.alpha[i];
-    const bool ok = a.gate_log ? (x <= 0.f) : (x >= 0.f && x <= 1.f);  // false for NaN
+    const bool ok = a.gate_range == 1 ? (x <= 0.f) : a.gate_range == 2 ? (x == x) : (x >= 0.f && x <= 1.f);
     if (!ok) bits |= kValidateAlpha;
   }
   for (size_t i = tid; i < a.n_beta; i += stride) {
     const float x = a.beta[i];
-    if (!(x >= 0.f && x <= 1.f)) bits |= kValidateBeta;
+    if (!(x >= 0.f && x <= 1.f) && !(a.beta_logits && x == x)) bits |= kValidateBeta;
   }
   for (size_t r = tid; r < a.n_krows; r += stride) {
     float s = 0.f;
@@ -78,7 +79,7 @@ hipError_t run_validation(const ValidateArgs &v, hipStream_t stream, unsigned *b
   hipError_t e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_validate_bits), &zero, sizeof(zero), 0,
                                         hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return e;
-  ValidateKArgs ka{v.alpha, v.n_alpha, v.gate_log ? 1 : 0, v.beta, v.n_beta, v.k, v.n_krows, v.dk,
+  ValidateKArgs ka{v.alpha, v.n_alpha, v.gate_range, v.beta, v.n_beta, v.beta_logits ? 1 : 0, v.k, v.n_krows, v.dk,
                    v.k_bf16 ? 1 : 0, v.cu, v.n_seq, v.total};
   const size_t work = v.n_alpha > v.n_krows ? v.n_alpha : v.n_krows;
   const unsigned blocks = (unsigned)(work / kThreads + 1 < 4096 ? work / kThreads + 1 : 4096);

@@ -46,22 +46,31 @@ def _unit(x: torch.Tensor) -> torch.Tensor:
     return x / torch.linalg.vector_norm(x, dim=-1, keepdim=True)
 
 
-def _gate(shape, gen, device, gate: str, alpha_lo: float = 0.9, log: bool = False) -> torch.Tensor:
-    """Gates alpha, or log(alpha) with log=True (the same draws either way)."""
+def _gate(shape, gen, device, gate: str, alpha_lo: float = 0.9, form: str = "") -> torch.Tensor:
+    """Gates alpha (form ""), log(alpha) ("log") or logits g with
+    alpha = exp(-softplus(g)) ("softplus"); the same draws in every form."""
     if gate == "uniform":
         a = torch.empty(shape, device=device).uniform_(alpha_lo, 1.0, generator=gen)
-        return torch.log(a) if log else a
+        if form == "softplus":
+            return torch.log1p(-a) - torch.log(a)      # alpha = 1 / (1 + e^g)
+        return torch.log(a) if form == "log" else a
     g = torch.empty(shape, device=device).normal_(-4.0, 1.0, generator=gen)
+    if form == "softplus":
+        return g
     la = -torch.nn.functional.softplus(g)
-    return la if log else torch.exp(la)
+    return la if form == "log" else torch.exp(la)
+
+
+def _gate_kind(gate_form: str) -> str:
+    return gate_form.split("_")[0] if gate_form.startswith(("log_", "softplus_")) else ""
 
 
 def _gate_shape(lead, dk, gate_form):
     """alpha's shape for a gate form: one value per key channel, one per token
     and head, or none at all."""
-    if gate_form in ("channel", "log_channel"):
+    if gate_form in ("channel", "log_channel", "softplus_channel"):
         return (*lead, dk)
-    if gate_form in ("scalar", "log_scalar"):
+    if gate_form in ("scalar", "log_scalar", "softplus_scalar"):
         return tuple(lead)
     if gate_form == "none":
         return None
@@ -72,14 +81,16 @@ def dense(B, T, H, dk, dv, dtype=torch.bfloat16, gate="softplus", alpha_lo=0.9,
           s0_std=None, seed=0, device="cpu", gate_form="channel"):
     """A dense [B, T, H, .] batch.  Returns a dict of tensors on `device`.
     gate_form "scalar" draws one gate per (token, head), "none" returns
-    alpha = None, "log_channel" / "log_scalar" return log(alpha) of the same
-    draws; the draws of the other tensors do not change."""
+    alpha = None, "log_channel" / "log_scalar" return log(alpha) and
+    "softplus_channel" / "softplus_scalar" the logits g (alpha =
+    exp(-softplus(g))) of the same draws; the draws of the other tensors do
+    not change."""
     gen = torch.Generator(device=device).manual_seed(seed)
     q = torch.empty((B, T, H, dk), device=device).normal_(generator=gen)
     k = _unit(torch.empty((B, T, H, dk), device=device).normal_(generator=gen))
     v = torch.empty((B, T, H, dv), device=device).normal_(generator=gen)
     shape = _gate_shape((B, T, H), dk, gate_form)
-    alpha = (_gate(shape, gen, device, gate, alpha_lo, log=gate_form.startswith("log"))
+    alpha = (_gate(shape, gen, device, gate, alpha_lo, form=_gate_kind(gate_form))
              if shape is not None else None)
     beta = torch.sigmoid(torch.empty((B, T, H), device=device).normal_(generator=gen))
     S0 = None
@@ -111,7 +122,7 @@ def packed(lengths, H, dk, dv, dtype=torch.bfloat16, gate="softplus", s0_std=0.0
     k = _unit(torch.empty((T, H, dk), device=device).normal_(generator=gen))
     v = torch.empty((T, H, dv), device=device).normal_(generator=gen)
     shape = _gate_shape((T, H), dk, gate_form)
-    alpha = _gate(shape, gen, device, gate, log=gate_form.startswith("log")) if shape is not None else None
+    alpha = _gate(shape, gen, device, gate, form=_gate_kind(gate_form)) if shape is not None else None
     beta = torch.sigmoid(torch.empty((T, H), device=device).normal_(generator=gen))
     if stress and alpha is not None and gate_form == "channel":
         q4 = H // 4

@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(kda):
 
 
 def test_status_strings(kda):
-    for s in range(12):
+    for s in range(13):
         assert kda.status_string(s) and kda.status_string(s) != "unknown status"
     assert kda.status_string(99) == "unknown status"
 
@@ -115,7 +115,8 @@ def _fwd_gated(kda, gate, **kw):
 
 def test_gated_validation(kda):
     P = ctypes.c_void_p
-    assert _fwd_gated(kda, 5) == 10                           # unknown gate
+    assert _fwd_gated(kda, 7) == 10                           # unknown gate
+    assert _fwd_gated(kda, 99) == 10
     assert _fwd_gated(kda, -1) == 10
     assert _fwd_gated(kda, kda.KDA_GATE_LOG_SCALAR, alpha=None) == 1   # log gates need alpha
     assert _fwd_gated(kda, kda.KDA_GATE_LOG_CHANNEL, alpha=P(0x40008)) == 5
@@ -157,12 +158,26 @@ def test_decode_tokens_validation(kda):
                                          a["So"], a["N"], a["Tk"], a["H"], 16, 16, 0.0, kda.KDA_F32, a["o"],
                                          None)
     assert call(Tk=-1) == 2
-    assert call(gate=5) == 10
+    assert call(gate=7) == 10
     assert call(Si=None) == 1
     assert call(So=P(0x100000 + 256)) == 8          # partial overlap of the two states
     assert call(o=P(0x100000)) == 8                 # o overlaps a state
     assert call(gate=kda.KDA_GATE_SCALAR, alpha=None) == 1
     assert call(N=0) == 0
+
+
+def test_ex_rejects_unknown_activation_bits(kda):
+    # rejected before any pointer is looked at or any work is launched
+    P = ctypes.c_void_p
+    st = kda.lib.kda_chunk_fwd_ex(P(0x10000), P(0x20000), P(0x30000), P(0x40000), kda.KDA_GATE_CHANNEL,
+                                  P(0x50000), 4, None, None, 2, 2, 8, 2, 16, 16, 0.0, kda.KDA_BF16,
+                                  P(0x60000), P(0x70000), P(0x80000), 1 << 30, None)
+    assert st == 12
+    st = kda.lib.kda_decode_tokens_ex(P(0x10000), P(0x20000), P(0x30000), P(0x40000), kda.KDA_GATE_CHANNEL,
+                                      P(0x50000), 8, P(0x100000), P(0x200000), 2, 3, 2, 16, 16, 0.0,
+                                      kda.KDA_F32, P(0x90000), None)
+    assert st == 12
+    assert kda.status_string(12) != "unknown status"
 
 
 def test_set_validation_toggles(kda):
