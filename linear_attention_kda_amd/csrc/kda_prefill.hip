@@ -419,14 +419,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // first write of the operand images, which reuse this space
   float *sTau = reinterpret_cast<float *>(arena);
 
-  if (tid < kChunk) {
-    float b = 0.f;
-    if (tid < L) {
-      b = a.beta[(size_t)(t0 + tid) * a.H + h];
-      if (a.act & kActBeta) b = sigmoid_f(b);
-    }
-    sBeta[tid] = b;
-  }
+  // beta of token tid % 64 (a valid token for every lane: no branch around
+  // the load), requested with the inputs below and stored to LDS after them,
+  // so no load waits for another
+  const float braw = a.beta[(size_t)(t0 + min(tid % kChunk, L - 1)) * a.H + h];
 
   // ---- loads and in-block prefix products.  Padded tokens (index >= L)
   // take q = k = 0 and alpha = 1; their loads read a valid token instead.
@@ -448,35 +444,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
     for (int j = 0; j < 4; ++j) pa[u][j] = al[j];
   }
-  // optional input activation: q, k <- SiLU, then unit length over the d_k
-  // channels of the token (CG lanes hold one token's channels)
-  if constexpr (ACTQK) {
-#pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      float kx[4], qx[4], sk = 0.f, sq = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kx[j] = silu_f((float)kraw[u][j]);
-        qx[j] = silu_f((float)qraw[u][j]);
-        sk += kx[j] * kx[j];
-        sq += qx[j] * qx[j];
-      }
-      const float rk = inv_norm(group_sum<CG>(sk)), rq = inv_norm(group_sum<CG>(sq));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kx[j] *= rk;
-        qx[j] *= rq;
-      }
-      kraw[u] = F4::pack(kx);
-      qraw[u] = F4::pack(qx);
-      // for the exact path, which reads q and k again from memory
-      if (cg == 0) {
-        sInvNorm[0][tb0 + u] = rk;
-        sInvNorm[1][tb0 + u] = rq;
-      }
-      __builtin_amdgcn_sched_barrier(0);  // one token at a time: bounds the live values
-    }
-  }
+  if (tid < kChunk) sBeta[tid] = tid < L ? ((a.act & kActBeta) ? sigmoid_f(braw) : braw) : 0.f;
   // k (or q) of token u, channel j, zero for padded tokens
   auto kval = [&](int u, int j) {
     const float x = (float)kraw[u][j];
@@ -520,6 +488,35 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   for (int u = 0; u < TPL; ++u)
 #pragma unroll
     for (int j = 0; j < 4; ++j) pa[u][j] *= excl[j];
+  // optional input activation: q, k <- SiLU, then unit length over the d_k
+  // channels of the token (CG lanes hold one token's channels)
+  if constexpr (ACTQK) {
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      float kx[4], qx[4], sk = 0.f, sq = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kx[j] = silu_f((float)kraw[u][j]);
+        qx[j] = silu_f((float)qraw[u][j]);
+        sk += kx[j] * kx[j];
+        sq += qx[j] * qx[j];
+      }
+      const float rk = inv_norm(group_sum<CG>(sk)), rq = inv_norm(group_sum<CG>(sq));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        kx[j] *= rk;
+        qx[j] *= rq;
+      }
+      kraw[u] = F4::pack(kx);
+      qraw[u] = F4::pack(qx);
+      // for the exact path, which reads q and k again from memory
+      if (cg == 0) {
+        sInvNorm[0][tb0 + u] = rk;
+        sInvNorm[1][tb0 + u] = rq;
+      }
+      __builtin_amdgcn_sched_barrier(0);  // one token at a time: bounds the live values
+    }
+  }
   if (th == TH - 1) *reinterpret_cast<f32x4 *>(sTau + w * DK + c0) = f32x4{incl[0], incl[1], incl[2], incl[3]};
   __syncthreads();
 
