@@ -65,3 +65,16 @@ def test_decode_tokens_zero_tokens_copies_state():
     torch.cuda.synchronize()
     assert o.shape == (3, 0, 2, 64)
     assert torch.equal(S_out, inp["S0"])
+
+
+@pytest.mark.parametrize("dk,dv,Tk", [(32, 64, 5), (64, 16, 4), (128, 32, 2), (16, 128, 7)])
+def test_decode_tokens_head_sizes(dk, dv, Tk):
+    import linear_attention_kda_amd as kda
+    announce(f"decode_tokens N=3 Tk={Tk} H=2 dk={dk} dv={dv} bf16")
+    inp = to_dev(inputs.dense(3, Tk, 2, dk, dv, torch.bfloat16, gate="uniform", alpha_lo=0.9, s0_std=0.05,
+                              seed=24 + dk + dv))
+    o, S_out = kda.decode_tokens(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_prefill(inp)
+    check("o", o, o_ref, TOL[torch.bfloat16])
+    check("S_out", S_out, S_ref, TOL[torch.bfloat16])

@@ -130,3 +130,14 @@ def test_decode_fused_inputs(gate_form, dtype):
     o1_ref, S1_ref = oracle.decode(r1["q"], r1["k"], r1["v"], r1["alpha"], r1["beta"], S.double().cpu().numpy())
     check("o step", o1, o1_ref, TOL[dtype])
     check("S step", S1, S1_ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 32), (32, 128), (128, 16)])
+def test_fused_inputs_head_sizes(dk, dv):
+    announce(f"fused inputs dense B=2 T=100 H=2 dk={dk} dv={dv} bf16")
+    inp = _raw(to_dev(inputs.dense(2, 100, 2, dk, dv, torch.bfloat16, s0_std=0.02, seed=55 + dk,
+                                   gate_form="softplus_channel")), 55 + dk)
+    o, S = _run(inp, "softplus_channel", QK | BETA)
+    o_ref, S_ref = oracle_prefill(_activated(inp, QK | BETA, "softplus_channel", dk))
+    check("o", o, o_ref, TOL[torch.bfloat16])
+    check("S_final", S, S_ref, TOL[torch.bfloat16])
