@@ -20,11 +20,21 @@ struct ChunkRecordLayout {
   size_t kh;    // k_i D_{0:i}          rows i (64),  K = d_k
   size_t qh;    // q_i D_{0:i}          rows i (64),  K = d_k
   size_t ktt;   // k_j D_{j+1:63}       rows c (d_k), K = 64 tokens (transposed)
-  size_t tb;    // (I + R)^{-1} Diag(beta), rows i (64), K = 64, zero above the diagonal
-  size_t aqk;   // scaled causal q-k scores incl. diagonal, rows i, K = 64, zero above
+  size_t tb;    // (I + R)^{-1} Diag(beta), rows i (64), K = 64, lower triangle (see tri_*)
+  size_t aqk;   // scaled causal q-k scores incl. diagonal, rows i, K = 64, lower triangle
   size_t p63;   // [dk] fp32 whole-chunk decay D_{0:63}
   size_t bytes; // record size (multiple of 1024)
 };
+
+// The two lower-triangular 64 x 64 operands (Tb and A) keep, for each 16-row
+// tile I, only the k-slabs that hold a column at or left of the diagonal:
+// slabs of 32 columns for 2-byte elements, 16 for 4-byte ones, one 1 KiB
+// fragment (64 lanes x 16 bytes) per (tile, slab).  The slabs of tile I start
+// at fragment tri_slab0(I).
+constexpr int tri_slab_width(int esize) { return esize == 2 ? 32 : 16; }
+constexpr int tri_slabs(int I, int esize) { return (16 * (I + 1) + tri_slab_width(esize) - 1) / tri_slab_width(esize); }
+constexpr int tri_slab0(int I, int esize) { return I == 0 ? 0 : tri_slab0(I - 1, esize) + tri_slabs(I - 1, esize); }
+constexpr size_t tri_bytes(int esize) { return (size_t)tri_slab0(4, esize) * 1024; }
 
 inline ChunkRecordLayout chunk_record_layout(int dk, int esize) {
   ChunkRecordLayout L;
@@ -32,8 +42,8 @@ inline ChunkRecordLayout chunk_record_layout(int dk, int esize) {
   L.qh = L.kh + (size_t)64 * dk * esize;
   L.ktt = L.qh + (size_t)64 * dk * esize;
   L.tb = L.ktt + (size_t)64 * dk * esize;
-  L.aqk = L.tb + (size_t)64 * 64 * esize;
-  L.p63 = L.aqk + (size_t)64 * 64 * esize;
+  L.aqk = L.tb + tri_bytes(esize);
+  L.p63 = L.aqk + tri_bytes(esize);
   size_t end = L.p63 + (size_t)dk * sizeof(float);
   L.bytes = (end + 1023) / 1024 * 1024;
   return L;

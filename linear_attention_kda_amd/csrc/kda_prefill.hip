@@ -157,6 +157,25 @@ __device__ __forceinline__ int frag_index(int i, int c) {
   return (((i >> 4) * F::NU + c / F::W) * 64 + (i & 15) + 16 * g) * F::KS + pos;
 }
 
+// Element offset of A(i, c) in a lower-triangular 64 x 64 operand stored
+// without its zero slabs (tri_slab0 in kda_launch.h); the position rule within
+// a fragment is that of frag_index.
+template <typename E>
+__device__ __forceinline__ int tri_index(int i, int c) {
+  typedef FragShape<E, 64> F;
+  const int ci = c % F::W;
+  int g, pos;
+  if constexpr (F::wide) {
+    const int cc = ci & 15;
+    g = cc >> 2;
+    pos = (ci >> 4) * 4 + (cc & 3);
+  } else {
+    g = ci >> 2;
+    pos = ci & 3;
+  }
+  return ((tri_slab0(i >> 4, (int)sizeof(E)) + c / F::W) * 64 + (i & 15) + 16 * g) * F::KS + pos;
+}
+
 // ======================================================= kernel 1: chunk prep
 struct PrepKArgs {
   const void *q, *k;
@@ -244,17 +263,21 @@ template <> struct SlotVec<float, 4> {
 };
 
 // Row tiles I0 .. I1-1 of a 64 x 64 fp32 tile in LDS (row stride LDR), masked
-// to j <= i and scaled per column by colscale (or not), to the record in
-// fragment order, slot by slot, by threads t0 .. t0 + nthr - 1.
+// to j <= i and scaled per column by colscale (or not), to a lower-triangular
+// record operand (tri_index layout), slot by slot, by threads t0 .. t0 + nthr - 1.
 template <typename E, int LDR>
 __device__ __forceinline__ void tile64_out(E *dst, const float *src, const float *colscale, int I0 = 0, int I1 = 4,
                                            int t0 = 0, int nthr = kThreads) {
   typedef FragShape<E, 64> F;
   typedef SlotVec<E, F::KS> SV;
+  constexpr int es = (int)sizeof(E);
   if ((int)threadIdx.x < t0) return;
-  for (int s = I0 * F::NU * 64 + threadIdx.x - t0; s < I1 * F::NU * 64; s += nthr) {
-    const int ts = s >> 6, L = s & 63;
-    const int i = 16 * (ts / F::NU) + (L & 15), slab = ts % F::NU, g = L >> 4;
+  for (int s = tri_slab0(I0, es) * 64 + threadIdx.x - t0; s < tri_slab0(I1, es) * 64; s += nthr) {
+    const int fr = s >> 6, L = s & 63;
+    int I = 0;
+#pragma unroll
+    for (int J = 1; J < 4; ++J) I += fr >= tri_slab0(J, es);
+    const int i = 16 * I + (L & 15), slab = fr - tri_slab0(I, es), g = L >> 4;
     float x[F::KS];
 #pragma unroll
     for (int e = 0; e < F::KS; ++e) {
@@ -655,17 +678,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
           av[r] = jb + r <= i ? at[s][r] : 0.f;
         }
         *reinterpret_cast<f32x4 *>(sR + i * LDR + jb) = f32x4{rv[0], rv[1], rv[2], rv[3]};
-        *reinterpret_cast<typename F4::vec *>(gA + frag_index<E, 64>(i, jb)) = F4::pack(av);
+        *reinterpret_cast<typename F4::vec *>(gA + tri_index<E>(i, jb)) = F4::pack(av);
       }
     }
-    // blocks above the diagonal of A are zero
-    for (int idx = tid; idx < 6 * 64; idx += kThreads) {
-      const int u = idx >> 6, ln = idx & 63;
-      const int I = u < 3 ? 0 : (u < 5 ? 1 : 2);
-      const int J = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
-      const float z[4] = {0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<typename F4::vec *>(gA + frag_index<E, 64>(16 * I + (ln & 15), 16 * J + 4 * (ln >> 4))) =
-          F4::pack(z);
+    // blocks above the diagonal of A that share a stored slab with the
+    // diagonal are zero
+    for (int idx = tid; idx < 16 * 64; idx += kThreads) {
+      const int I = idx >> 8, J = (idx >> 6) & 3, ln = idx & 63;
+      if (J > I && 16 * J / FragShape<E, 64>::W < tri_slabs(I, (int)sizeof(E))) {
+        const float z[4] = {0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<typename F4::vec *>(gA + tri_index<E>(16 * I + (ln & 15), 16 * J + 4 * (ln >> 4))) =
+            F4::pack(z);
+      }
     }
     // Kend^T into its LDS image (copied out after the next barrier): four
     // consecutive tokens of one channel are contiguous there
@@ -939,7 +963,7 @@ __device__ __forceinline__ void lds_dma16_nt(const void *src, uint32_t lds_base)
 template <int DK, typename E> struct RecordShape {
   static constexpr int es = sizeof(E);
   static constexpr int kh = 0, qh = 64 * DK * es, ktt = 128 * DK * es, tb = 192 * DK * es;
-  static constexpr int aqk = tb + 4096 * es, p63 = aqk + 4096 * es;
+  static constexpr int aqk = tb + (int)tri_bytes(es), p63 = aqk + (int)tri_bytes(es);
   static constexpr int bytes = (p63 + DK * 4 + 1023) / 1024 * 1024;
 };
 
@@ -1176,12 +1200,12 @@ void chunk_scan_kernel(ScanKArgs a) {
     for (int u = 0; u < UT; ++u)
 #pragma unroll
       for (int I = 0; I < 4; ++I)
-        if (need(I, u)) ftb[I][u] = BT::load1(Tb + I * TILE_T, u);
+        if (need(I, u)) ftb[I][u] = BT::load1(Tb + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
 #pragma unroll
     for (int u = 0; u < UT; ++u)
 #pragma unroll
       for (int I = 0; I < 4; ++I)
-        if (need(I, u)) faq[I][u] = BT::load1(Aq + I * TILE_T, u);
+        if (need(I, u)) faq[I][u] = BT::load1(Aq + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
 #pragma unroll
     for (int u = 0; u < UT; ++u)
 #pragma unroll

@@ -39,13 +39,15 @@ def test_status_strings(kda):
 
 def test_workspace_size(kda):
     # dense: one record per (chunk, head); a record holds three 64 x d_k tiles,
-    # two 64 x 64 tiles and d_k floats, rounded up to 1 KiB
-    rec = (3 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 128 * 4 + 1023) // 1024 * 1024
+    # two lower-triangular 64 x 64 tiles stored as the 1 KiB fragments of the
+    # k-slabs that reach the diagonal (6 slabs of 32 columns in bf16) and d_k
+    # floats, rounded up to 1 KiB
+    rec = (3 * 64 * 128 * 2 + 2 * 6 * 1024 + 128 * 4 + 1023) // 1024 * 1024
     assert kda.chunk_fwd_workspace_size(4, 2048, 16, 128, 128, -1, kda.KDA_BF16) == 4 * 32 * 16 * rec
     assert kda.chunk_fwd_workspace_size(2, 0, 3, 32, 32, -1, kda.KDA_F32) == 0
     # packed: tables plus (ceil(T/64) + N) chunk slots
     packed = kda.chunk_fwd_workspace_size(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)
-    rec64 = (3 * 64 * 64 * 2 + 2 * 64 * 64 * 2 + 64 * 4 + 1023) // 1024 * 1024
+    rec64 = (3 * 64 * 64 * 2 + 2 * 6 * 1024 + 64 * 4 + 1023) // 1024 * 1024
     assert packed >= (16 + 5) * 2 * rec64
     # invalid sizes
     assert kda.chunk_fwd_workspace_size(1, 10, 2, 48, 64, -1, kda.KDA_BF16) == 0
