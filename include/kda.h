@@ -141,6 +141,43 @@ const char *kda_status_string(kda_status s);
 int kda_set_validation(int enable);
 
 /*
+ * How kda_chunk_fwd schedules its two kernels (chunk preparation, which is
+ * parallel over all chunks, and the scan, which walks each sequence's chunks
+ * in order; page "Kimi Delta Attention (KDA)", section "Two schedules of
+ * computation for one recurrence").
+ *   KDA_SCHEDULE_TWO_PHASE: the preparation of every chunk, then the scan,
+ *     on `stream`.
+ *   KDA_SCHEDULE_OVERLAP: both at once on two internal streams confined to
+ *     disjoint halves of the compute units, the scan copying each chunk's
+ *     record as soon as its preparation is published (ready bits in the
+ *     workspace; producer and consumer of a record run on the same XCD, so
+ *     the record is read from that XCD's L2).  The call forks from and joins
+ *     back to `stream` with events, so it stays asynchronous and ordered on
+ *     `stream`.  Used for dense bf16 batches with d_k = d_v = 128 on a full
+ *     MI355X (256 CUs); other calls run two-phase.  Both schedules give
+ *     bitwise identical results.  Calls from several host threads are
+ *     serialised around the internal streams, which are created on the first
+ *     overlapped call (if that fails, e.g. under stream capture, the device
+ *     stays on two-phase).  If the preparation cannot run for more than about
+ *     a second (another process holding its compute units), the scan stops
+ *     waiting and its results are wrong; the schedule's error word in the
+ *     workspace records that.
+ *   KDA_SCHEDULE_AUTO (default): overlap when supported and the scan's
+ *     workgroups (B * H * d_v / 32) fit on half of the chip, with at least 8
+ *     chunks per sequence (long sequences over few heads, where the two-phase
+ *     scan leaves half of the chip idle); else two-phase.
+ * The initial value is taken from the environment variable KDA_SCHEDULE
+ * (0, 1 or 2) at load time.  Process-wide; returns the previous setting, or
+ * -1 (nothing changed) for an unknown value.
+ */
+typedef enum {
+  KDA_SCHEDULE_AUTO = 0,
+  KDA_SCHEDULE_TWO_PHASE = 1,
+  KDA_SCHEDULE_OVERLAP = 2
+} kda_schedule;
+int kda_set_schedule(int schedule);
+
+/*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes (host-only
  * arithmetic, no device call).  For a packed batch pass B = 1 and N = the
  * number of sequences; for a dense batch N may be anything (with B = 1 and

@@ -10,7 +10,8 @@ _BINDING_NAMES = ("EXPORTED", "GATES", "KDA_BF16", "KDA_F32", "KDA_GATE_CHANNEL"
                   "KDA_GATE_LOG_SCALAR", "KDA_GATE_NONE",
                   "KDA_GATE_SCALAR", "KDA_GATE_SOFTPLUS_CHANNEL", "KDA_GATE_SOFTPLUS_SCALAR",
                   "KDA_ACT_QK_SILU_L2NORM", "KDA_ACT_BETA_SIGMOID", "LIB_PATH", "KdaError", "chunk_fwd", "chunk_fwd_workspace_size",
-                  "decode_step", "decode_tokens", "lib", "set_validation", "status_string",
+                  "decode_step", "decode_tokens", "lib", "set_validation", "set_schedule", "status_string",
+                  "KDA_SCHEDULE_AUTO", "KDA_SCHEDULE_TWO_PHASE", "KDA_SCHEDULE_OVERLAP", "SCHEDULES",
                   "KDA_ERR_INVALID_VALUE")
 
 

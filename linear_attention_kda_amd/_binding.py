@@ -34,9 +34,15 @@ _PER_TOKEN = (KDA_GATE_SCALAR, KDA_GATE_LOG_SCALAR, KDA_GATE_SOFTPLUS_SCALAR)
 # input activations (kda_input_act flags)
 KDA_ACT_QK_SILU_L2NORM = 1
 KDA_ACT_BETA_SIGMOID = 2
+# prefill schedules (kda_schedule)
+KDA_SCHEDULE_AUTO = 0
+KDA_SCHEDULE_TWO_PHASE = 1
+KDA_SCHEDULE_OVERLAP = 2
+SCHEDULES = {"auto": KDA_SCHEDULE_AUTO, "two_phase": KDA_SCHEDULE_TWO_PHASE, "overlap": KDA_SCHEDULE_OVERLAP}
 
 # names exported by include/kda.h
-EXPORTED = ("kda_status_string", "kda_set_validation", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
+EXPORTED = ("kda_status_string", "kda_set_validation", "kda_set_schedule", "kda_chunk_fwd_workspace_size",
+            "kda_chunk_fwd",
             "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_decode_step", "kda_decode_step_gated",
             "kda_decode_tokens", "kda_decode_tokens_ex")
 KDA_ERR_INVALID_VALUE = 11
@@ -82,6 +88,8 @@ def _load() -> ctypes.CDLL:
                                          i32, f32, i32, vp, vp]
     lib.kda_set_validation.restype = i32
     lib.kda_set_validation.argtypes = [i32]
+    lib.kda_set_schedule.restype = i32
+    lib.kda_set_schedule.argtypes = [i32]
     return lib
 
 
@@ -98,6 +106,16 @@ def set_validation(enable: bool) -> bool:
     stream and raises KdaError (status KDA_ERR_INVALID_VALUE) on inputs
     outside the method's domain."""
     return bool(lib.kda_set_validation(1 if enable else 0))
+
+
+def set_schedule(schedule: str) -> str:
+    """Choose how chunk_fwd schedules its kernels: "auto", "two_phase" or
+    "overlap" (process-wide; see kda_set_schedule); returns the previous
+    setting's name."""
+    if schedule not in SCHEDULES:
+        raise ValueError(f"schedule must be one of {sorted(SCHEDULES)}")
+    prev = lib.kda_set_schedule(SCHEDULES[schedule])
+    return {v: k for k, v in SCHEDULES.items()}[prev]
 
 
 def chunk_fwd_workspace_size(B: int, T: int, H: int, d_k: int, d_v: int, N: int = -1,

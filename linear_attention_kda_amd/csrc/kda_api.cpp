@@ -43,6 +43,14 @@ std::atomic<int> g_validate{[] {
   return e && std::atoi(e) != 0 ? 1 : 0;
 }()};
 
+// Prefill schedule (kda_set_schedule): KDA_SCHEDULE in the environment at
+// load time, else automatic.
+std::atomic<int> g_schedule{[] {
+  const char *e = std::getenv("KDA_SCHEDULE");
+  const int v = e ? std::atoi(e) : 0;
+  return v == kda::kScheduleTwoPhase || v == kda::kScheduleOverlap ? v : kda::kScheduleAuto;
+}()};
+
 // Runs the device checks when they are on.  KDA_OK when off or clean.
 kda_status check_values(const float *alpha, size_t n_alpha, kda_gate gate, const float *beta, size_t n_beta,
                         unsigned act, const void *k, size_t n_krows, int d_k, kda_dtype dtype, const int32_t *cu,
@@ -83,6 +91,12 @@ const char *kda_status_string(kda_status s) {
 
 int kda_set_validation(int enable) {
   return g_validate.exchange(enable ? 1 : 0);
+}
+
+int kda_set_schedule(int schedule) {
+  if (schedule != KDA_SCHEDULE_AUTO && schedule != KDA_SCHEDULE_TWO_PHASE && schedule != KDA_SCHEDULE_OVERLAP)
+    return -1;
+  return g_schedule.exchange(schedule);
 }
 
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int N, kda_dtype dtype) {
@@ -162,6 +176,7 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const f
     return st;
 
   kda::PrefillArgs a;
+  a.schedule = g_schedule.load(std::memory_order_relaxed);
   a.q = q;
   a.k = k;
   a.v = v;

@@ -49,12 +49,21 @@ inline ChunkRecordLayout chunk_record_layout(int dk, int esize) {
   return L;
 }
 
-// Workspace = [index tables (packed batches only)] [chunk records].
+// Control words of the overlapped schedule (int32, after one ready flag per
+// record): per-XCD task counters of the prep and of the scan, and an error word.
+constexpr int kSchedPrepNext = 0, kSchedScanNext = 8, kSchedError = 16, kSchedWords = 64;
+// kSchedError values: a flag wait timed out / a record came from another XCD
+constexpr int kSchedErrTimeout = 1, kSchedErrXcd = 2;
+
+// Workspace = [index tables (packed batches only)] [chunk records]
+//             [ready flags + control words (dense batches only)].
 struct WorkspacePlan {
   int n_seq;           // sequences
   long long max_chunks;// chunk slots (dense: exact count)
   size_t tables_bytes; // 0 for dense batches
   size_t record_bytes;
+  size_t sched;        // byte offset of the flags (dense only; 0 bytes for packed)
+  size_t sched_bytes;
   size_t total;
   // int32 table offsets (in elements from the workspace start), packed only
   size_t seq_tok0, seq_chunk0, chunk_t0, chunk_len;
@@ -79,7 +88,10 @@ inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
     P.max_chunks = (long long)B * (((long long)T + kChunkTokens - 1) / kChunkTokens);
     P.tables_bytes = 0;
   }
-  P.total = P.tables_bytes + (size_t)P.max_chunks * H * P.record_bytes;
+  P.sched = P.tables_bytes + (size_t)P.max_chunks * H * P.record_bytes;
+  P.sched_bytes = packed || P.max_chunks == 0 ? 0
+                  : (((size_t)P.max_chunks * H + kSchedWords) * sizeof(int32_t) + 255) / 256 * 256;
+  P.total = P.sched + P.sched_bytes;
   return P;
 }
 
@@ -99,7 +111,12 @@ constexpr bool gate_is_softplus(int g) { return g == kGateSoftplusChannel || g =
 constexpr unsigned kActQK = 1;    // q, k <- L2-normalised SiLU, per token and head
 constexpr unsigned kActBeta = 2;  // beta <- sigmoid(beta)
 
+// Prefill schedules (kda_set_schedule): automatic, always prep then scan, or
+// prep and scan overlapped whenever the shapes allow it.
+constexpr int kScheduleAuto = 0, kScheduleTwoPhase = 1, kScheduleOverlap = 2;
+
 struct PrefillArgs {
+  int schedule;               // kSchedule*
   const void *q, *k, *v;
   const float *alpha, *beta, *S0;
   int gate;

@@ -33,7 +33,11 @@
 #include "kda_device.h"
 #include "kda_launch.h"
 
+#include <hip/hip_ext.h>
+
 #include <cstdlib>
+#include <cstring>
+#include <mutex>
 #include <type_traits>
 
 namespace kda {
@@ -187,7 +191,20 @@ struct PrepKArgs {
   float scale;
   char *ws_records;
   ChunkRecordLayout lay;
+  // overlapped schedule (null otherwise): the ready words (ready_words per
+  // unit), the control words (kSchedWords) and the number of units
+  int *ready, *ctl;
+  int ready_words, n_units;
 };
+
+// Index of the XCD (accelerator complex die) this wave runs on, 0..7.  Each
+// XCD has its own L2; the overlapped schedule keeps the producer and the
+// consumer of every chunk record on one XCD.
+__device__ __forceinline__ int xcd_id() {
+  unsigned x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return (int)(x & 7);
+}
 
 // LDS image of a fragment-ordered operand (FragShape<E, K>, ROWS rows), slot
 // by slot in record order.  Within each 16-row group the rows are XOR-swizzled
@@ -381,7 +398,7 @@ __device__ __forceinline__ void tile_ij(int p, int &I, int &J) {
 // Exact path (a chunk with some D_{0:63} below 2^-100, e.g. a gate of 0):
 // no division at all.  Kbnd and Qbnd as above, Kend from suffix products, and
 // R and A summed channel by channel with running products of the gates.
-template <int DK, typename E, int GATE, bool ACTQK>
+template <int DK, typename E, int GATE, bool ACTQK, bool SCHED = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrepKArgs a) {
   typedef LdsFrag<E, DK, 64> LK;   // Kbnd, Qbnd, k / a: rows = tokens, K = d_k
   typedef LdsFrag<E, 64, DK> LT;   // Kend^T: rows = channels, K = tokens
@@ -400,429 +417,458 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   __shared__ float sBeta[kChunk];
   __shared__ float sInvNorm[2][kChunk];  // 1/|SiLU(k)|, 1/|SiLU(q)| per token (input activation only)
 
-  const int h = blockIdx.y;
-  const long long c = blockIdx.x;
-  long long t0;
-  int L;
-  if (!chunk_span(a.src, c, t0, L)) return;
+  // one record: chunk slot c, head h
+  auto prep_one = [&](const long long c, const int h) {
+    long long t0;
+    int L;
+    if (!chunk_span(a.src, c, t0, L)) return;
 
-  char *rec = a.ws_records + ((size_t)c * a.H + h) * a.lay.bytes;
-  const int tid = threadIdx.x, w = wave_id(), l = lane_id();
-  const int cg = l % CG, th = l / CG, c0 = 4 * cg;
-  const E *q = reinterpret_cast<const E *>(a.q);
-  const E *k = reinterpret_cast<const E *>(a.k);
-  const size_t hs = (size_t)a.H * DK;  // token stride of q, k, alpha
-  const size_t base = (size_t)t0 * hs + (size_t)h * DK + c0;
-  // gates of channels ch0 .. ch0+3 of token t0 + tk (tk a valid chunk index):
-  // per channel, one shared value, or none, given as gates or as their
-  // logarithms (see kda_gate)
-  // (raw = true: the stored values, for gate_value<GATE> later)
-  auto gate4 = [&](int tk, int ch0, float *al, bool nontemporal, bool raw = false) {
-    const size_t tok = (size_t)t0 + tk;
-    if constexpr (gate_per_channel(GATE)) {
-      const f32x4 *p = reinterpret_cast<const f32x4 *>(a.alpha + tok * hs + (size_t)h * DK + ch0);
-      const f32x4 x = nontemporal ? __builtin_nontemporal_load(p) : *p;
+    char *rec = a.ws_records + ((size_t)c * a.H + h) * a.lay.bytes;
+    const int tid = threadIdx.x, w = wave_id(), l = lane_id();
+    const int cg = l % CG, th = l / CG, c0 = 4 * cg;
+    const E *q = reinterpret_cast<const E *>(a.q);
+    const E *k = reinterpret_cast<const E *>(a.k);
+    const size_t hs = (size_t)a.H * DK;  // token stride of q, k, alpha
+    const size_t base = (size_t)t0 * hs + (size_t)h * DK + c0;
+    // gates of channels ch0 .. ch0+3 of token t0 + tk (tk a valid chunk index):
+    // per channel, one shared value, or none, given as gates or as their
+    // logarithms (see kda_gate)
+    // (raw = true: the stored values, for gate_value<GATE> later)
+    auto gate4 = [&](int tk, int ch0, float *al, bool nontemporal, bool raw = false) {
+      const size_t tok = (size_t)t0 + tk;
+      if constexpr (gate_per_channel(GATE)) {
+        const f32x4 *p = reinterpret_cast<const f32x4 *>(a.alpha + tok * hs + (size_t)h * DK + ch0);
+        const f32x4 x = nontemporal ? __builtin_nontemporal_load(p) : *p;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = raw ? x[j] : gate_value<GATE>(x[j]);
-    } else {
-      float x = 1.f;
-      if constexpr (gate_per_token(GATE)) {
-        x = a.alpha[tok * a.H + h];
-        if (!raw) x = gate_value<GATE>(x);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) al[j] = x;
-    }
-  };
-  char *sKh = arena, *sQh = arena + LK::BYTES, *sKd = arena + 2 * LK::BYTES;
-  float *sR = reinterpret_cast<float *>(arena);
-  float *sT = reinterpret_cast<float *>(arena + RT_BYTES);
-  char *sX = arena + 2 * RT_BYTES;     // Kend^T staging (fast) or A in fp32 (exact)
-  // whole-block gate products; read before the barrier that precedes the
-  // first write of the operand images, which reuse this space
-  float *sTau = reinterpret_cast<float *>(arena);
-
-  // beta of token tid % 64 (a valid token for every lane: no branch around
-  // the load), requested with the inputs below and stored to LDS after them,
-  // so no load waits for another
-  const float braw = a.beta[(size_t)(t0 + min(tid % kChunk, L - 1)) * a.H + h];
-
-  // ---- loads and in-block prefix products.  Padded tokens (index >= L)
-  // take q = k = 0 and alpha = 1; their loads read a valid token instead.
-  // Each input byte is read once here, so the loads carry the nontemporal
-  // hint (measured faster: they do not displace the records in the caches).
-  const int tb0 = 16 * w + TPL * th;   // first token of this lane
-  // q and k stay packed in their own type until used (register budget)
-  typename F4::vec kraw[TPL], qraw[TPL];
-  float pa[TPL][4];
-#pragma unroll
-  for (int u = 0; u < TPL; ++u) {
-    const int tok = tb0 + u;
-    const bool live = tok < L;
-    const size_t off = base + (size_t)min(tok, L - 1) * hs;
-    float al[4];
-    gate4(min(tok, L - 1), c0, al, true, true);   // converted below, after the q, k activation
-    kraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(k + off));
-    qraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(q + off));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pa[u][j] = al[j];
-  }
-  if (tid < kChunk) sBeta[tid] = tid < L ? ((a.act & kActBeta) ? sigmoid_f(braw) : braw) : 0.f;
-  // k (or q) of token u, channel j, zero for padded tokens
-  auto kval = [&](int u, int j) {
-    const float x = (float)kraw[u][j];
-    return tb0 + u < L ? x : 0.f;
-  };
-  auto qval = [&](int u, int j) {
-    const float x = (float)qraw[u][j];
-    return tb0 + u < L ? x : 0.f;
-  };
-  float tot[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    float run = 1.f;
-#pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      run *= tb0 + u < L ? gate_value<GATE>(pa[u][j]) : 1.f;
-      pa[u][j] = run;
-    }
-    tot[j] = run;
-    if constexpr (gate_is_softplus(GATE)) __builtin_amdgcn_sched_barrier(0);
-  }
-  // exclusive product over the lanes of earlier sub-ranges of the block
-  // (lanes cg + CG th' for th' < th); Hillis-Steele scan with stride CG
-  float incl[4], excl[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) incl[j] = tot[j];
-#pragma unroll
-  for (int d = 1; d < TH; d <<= 1) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float y = __shfl(incl[j], l - d * CG);
-      if (th >= d) incl[j] *= y;
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float y = __shfl(incl[j], l - CG);
-    excl[j] = th >= 1 ? y : 1.f;
-  }
-#pragma unroll
-  for (int u = 0; u < TPL; ++u)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pa[u][j] *= excl[j];
-  // optional input activation: q, k <- SiLU, then unit length over the d_k
-  // channels of the token (CG lanes hold one token's channels)
-  if constexpr (ACTQK) {
-#pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      float kx[4], qx[4], sk = 0.f, sq = 0.f;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kx[j] = silu_f((float)kraw[u][j]);
-        qx[j] = silu_f((float)qraw[u][j]);
-        sk += kx[j] * kx[j];
-        sq += qx[j] * qx[j];
-      }
-      const float rk = inv_norm(group_sum<CG>(sk)), rq = inv_norm(group_sum<CG>(sq));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kx[j] *= rk;
-        qx[j] *= rq;
-      }
-      kraw[u] = F4::pack(kx);
-      qraw[u] = F4::pack(qx);
-      // for the exact path, which reads q and k again from memory
-      if (cg == 0) {
-        sInvNorm[0][tb0 + u] = rk;
-        sInvNorm[1][tb0 + u] = rq;
-      }
-      __builtin_amdgcn_sched_barrier(0);  // one token at a time: bounds the live values
-    }
-  }
-  if (th == TH - 1) *reinterpret_cast<f32x4 *>(sTau + w * DK + c0) = f32x4{incl[0], incl[1], incl[2], incl[3]};
-  __syncthreads();
-
-  // ---- chunk prefix a = (blocks before) * (in-block prefix); D_{0:63}
-  float fb[4], gb[4], p63[4];
-  {
-    f32x4 tau[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b) tau[b] = *reinterpret_cast<const f32x4 *>(sTau + b * DK + c0);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float before = 1.f, after = 1.f;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b < w) before *= tau[b][j];
-        if (b > w) after *= tau[b][j];
-      }
-      fb[j] = before;
-      gb[j] = after;
-      p63[j] = tau[0][j] * tau[1][j] * tau[2][j] * tau[3][j];
-    }
-  }
-  int weak = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) weak |= !(p63[j] >= 0x1p-100f);
-  const bool exact = __syncthreads_or(weak) != 0;   // uniform over the workgroup
-
-  // ---- Kbnd, s Qbnd (both paths) and k / a (fast path) into LDS
-  typename F4::vec ktt[TPL];   // Kend rows of this lane's tokens, packed (written later)
-#pragma unroll
-  for (int u = 0; u < TPL; ++u) {
-    const int tok = tb0 + u;
-    float kh[4], qh[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float av = pa[u][j] * fb[j];
-      kh[j] = kval(u, j) * av;
-      qh[j] = qval(u, j) * av * a.scale;
-      pa[u][j] = av;
-    }
-    *reinterpret_cast<typename F4::vec *>(sKh + LK::elem_off(tok, c0)) = F4::pack(kh);
-    *reinterpret_cast<typename F4::vec *>(sQh + LK::elem_off(tok, c0)) = F4::pack(qh);
-  }
-  if (!exact) {
-#pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      const int tok = tb0 + u;
-      float kd[4], kt[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        kd[j] = kval(u, j) * __builtin_amdgcn_rcpf(pa[u][j]);
-        kt[j] = kd[j] * p63[j];
-      }
-      *reinterpret_cast<typename F4::vec *>(sKd + LK::elem_off(tok, c0)) = F4::pack(kd);
-      ktt[u] = F4::pack(kt);
-    }
-  } else {
-    // D_{j+1:63} without division: in-lane exclusive suffix, times the later
-    // sub-ranges of the block, times the later blocks.  The gates are read
-    // again (this path is rare).
-    float sfx[TPL][4], run[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) run[j] = 1.f;
-#pragma unroll
-    for (int u = TPL - 1; u >= 0; --u) {
-      const int tok = tb0 + u;
-      float al[4];
-      gate4(min(tok, L - 1), c0, al, false);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sfx[u][j] = run[j];
-        run[j] *= tok < L ? al[j] : 1.f;
-      }
-    }
-    float later[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) later[j] = 1.f;
-    for (int d = 1; d < TH; ++d) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float y = __shfl(run[j], l + d * CG);
-        if (th + d < TH) later[j] *= y;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < TPL; ++u) {
-      float kt[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) kt[j] = kval(u, j) * sfx[u][j] * later[j] * gb[j];
-      ktt[u] = F4::pack(kt);
-    }
-  }
-  __syncthreads();
-
-  // ---- fast path: R^T and A^T tiles on the matrix cores.  Pair (I, J),
-  // I >= J: D[j][i] over j in block J (rows), i in block I (columns).
-  constexpr int NP = 3;  // pairs per wave: w, w + 4, w + 8 (< 10)
-  f32x4 rt[NP], at[NP];
-  if (!exact) {
-#pragma unroll
-    for (int s = 0; s < NP; ++s) {
-      const int p = w + 4 * s;
-      rt[s] = at[s] = zero4();
-      if (p < 10) {
-        int I, J;
-        tile_ij(p, I, J);
-#pragma unroll
-        for (int u = 0; u < LK::F::NU; ++u) {
-          const char *ad = sKd + LK::slot_off(J, u, l & 15, l >> 4);
-          rt[s] = slot_mma<E, DK>(ad, sKh + LK::slot_off(I, u, l & 15, l >> 4), rt[s]);
-          at[s] = slot_mma<E, DK>(ad, sQh + LK::slot_off(I, u, l & 15, l >> 4), at[s]);
-        }
-      }
-    }
-  }
-  copy_out<LK>(rec + a.lay.kh, sKh);
-  copy_out<LK>(rec + a.lay.qh, sQh);
-  __syncthreads();  // phase-1 images are dead from here on
-
-  E *gA = reinterpret_cast<E *>(rec + a.lay.aqk);
-  if (!exact) {
-    // R (scaled by beta_i, j < i) to LDS for the solve; A (j <= i) straight to
-    // the record: lane (i, g) holds A[i][16J + 4g .. +3], four consecutive
-    // elements of one record slot.
-#pragma unroll
-    for (int s = 0; s < NP; ++s) {
-      const int p = w + 4 * s;
-      if (p < 10) {
-        int I, J;
-        tile_ij(p, I, J);
-        const int i = 16 * I + (l & 15), jb = 16 * J + 4 * (l >> 4);
-        float rv[4], av[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          rv[r] = jb + r < i ? sBeta[i] * rt[s][r] : 0.f;
-          av[r] = jb + r <= i ? at[s][r] : 0.f;
-        }
-        *reinterpret_cast<f32x4 *>(sR + i * LDR + jb) = f32x4{rv[0], rv[1], rv[2], rv[3]};
-        *reinterpret_cast<typename F4::vec *>(gA + tri_index<E>(i, jb)) = F4::pack(av);
-      }
-    }
-    // blocks above the diagonal of A that share a stored slab with the
-    // diagonal are zero
-    for (int idx = tid; idx < 16 * 64; idx += kThreads) {
-      const int I = idx >> 8, J = (idx >> 6) & 3, ln = idx & 63;
-      if (J > I && 16 * J / FragShape<E, 64>::W < tri_slabs(I, (int)sizeof(E))) {
-        const float z[4] = {0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<typename F4::vec *>(gA + tri_index<E>(16 * I + (ln & 15), 16 * J + 4 * (ln >> 4))) =
-            F4::pack(z);
-      }
-    }
-    // Kend^T into its LDS image (copied out after the next barrier): four
-    // consecutive tokens of one channel are contiguous there
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (TPL >= 4) {
-#pragma unroll
-        for (int u = 0; u < TPL; u += 4) {
-          typename F4::vec v;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const E x = ktt[u + e][j];
-            v[e] = x;
-          }
-          *reinterpret_cast<typename F4::vec *>(sX + LT::elem_off(c0 + j, tb0 + u)) = v;
-        }
+        for (int j = 0; j < 4; ++j) al[j] = raw ? x[j] : gate_value<GATE>(x[j]);
       } else {
-#pragma unroll
-        for (int u = 0; u < TPL; ++u) {
-          const E x = ktt[u][j];
-          *reinterpret_cast<E *>(sX + LT::elem_off(c0 + j, tb0 + u)) = x;
+        float x = 1.f;
+        if constexpr (gate_per_token(GATE)) {
+          x = a.alpha[tok * a.H + h];
+          if (!raw) x = gate_value<GATE>(x);
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) al[j] = x;
+      }
+    };
+    char *sKh = arena, *sQh = arena + LK::BYTES, *sKd = arena + 2 * LK::BYTES;
+    float *sR = reinterpret_cast<float *>(arena);
+    float *sT = reinterpret_cast<float *>(arena + RT_BYTES);
+    char *sX = arena + 2 * RT_BYTES;     // Kend^T staging (fast) or A in fp32 (exact)
+    // whole-block gate products; read before the barrier that precedes the
+    // first write of the operand images, which reuse this space
+    float *sTau = reinterpret_cast<float *>(arena);
+
+    // beta of token tid % 64 (a valid token for every lane: no branch around
+    // the load), requested with the inputs below and stored to LDS after them,
+    // so no load waits for another
+    const float braw = a.beta[(size_t)(t0 + min(tid % kChunk, L - 1)) * a.H + h];
+
+    // ---- loads and in-block prefix products.  Padded tokens (index >= L)
+    // take q = k = 0 and alpha = 1; their loads read a valid token instead.
+    // Each input byte is read once here, so the loads carry the nontemporal
+    // hint (measured faster: they do not displace the records in the caches).
+    const int tb0 = 16 * w + TPL * th;   // first token of this lane
+    // q and k stay packed in their own type until used (register budget)
+    typename F4::vec kraw[TPL], qraw[TPL];
+    float pa[TPL][4];
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      const int tok = tb0 + u;
+      const bool live = tok < L;
+      const size_t off = base + (size_t)min(tok, L - 1) * hs;
+      float al[4];
+      gate4(min(tok, L - 1), c0, al, true, true);   // converted below, after the q, k activation
+      kraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(k + off));
+      qraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(q + off));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pa[u][j] = al[j];
+    }
+    if (tid < kChunk) sBeta[tid] = tid < L ? ((a.act & kActBeta) ? sigmoid_f(braw) : braw) : 0.f;
+    // k (or q) of token u, channel j, zero for padded tokens
+    auto kval = [&](int u, int j) {
+      const float x = (float)kraw[u][j];
+      return tb0 + u < L ? x : 0.f;
+    };
+    auto qval = [&](int u, int j) {
+      const float x = (float)qraw[u][j];
+      return tb0 + u < L ? x : 0.f;
+    };
+    float tot[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float run = 1.f;
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        run *= tb0 + u < L ? gate_value<GATE>(pa[u][j]) : 1.f;
+        pa[u][j] = run;
+      }
+      tot[j] = run;
+      if constexpr (gate_is_softplus(GATE)) __builtin_amdgcn_sched_barrier(0);
+    }
+    // exclusive product over the lanes of earlier sub-ranges of the block
+    // (lanes cg + CG th' for th' < th); Hillis-Steele scan with stride CG
+    float incl[4], excl[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) incl[j] = tot[j];
+#pragma unroll
+    for (int d = 1; d < TH; d <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float y = __shfl(incl[j], l - d * CG);
+        if (th >= d) incl[j] *= y;
       }
     }
-  } else {
-    // R and A channel by channel: thread (j, part) runs D_{j+1:i} over i for
-    // CQ channels; the NQ parts of row j sit in neighbouring lanes and are
-    // summed across them.  At most 16 channels per lane keep the running
-    // products in few registers (this path is rare: with more channels per
-    // lane its registers would push values of the common path into
-    // scratch); with NQ > 4 the 64 rows take NQ/4 passes.
-    constexpr int CQ = DK / 4 > 16 ? 16 : DK / 4;
-    constexpr int NQ = DK / CQ;          // lanes per row
-    constexpr int JP = kThreads / NQ;    // rows per pass
-    float *sA = reinterpret_cast<float *>(sX);
-    const int qd = tid % NQ;
-#pragma unroll 1
-    for (int jb = 0; jb < kChunk; jb += JP) {
-      const int j = jb + tid / NQ;
-      const size_t cb = (size_t)t0 * hs + (size_t)h * DK + qd * CQ;
-      float kj[CQ], rho[CQ];
 #pragma unroll
-      for (int cc = 0; cc < CQ; cc += 4) {
-        F4::load(k + cb + (size_t)min(j, L - 1) * hs + cc, kj + cc);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if constexpr (ACTQK) kj[cc + e] = (float)(E)(silu_f(kj[cc + e]) * sInvNorm[0][min(j, L - 1)]);
-          kj[cc + e] = j < L ? kj[cc + e] : 0.f;
-          rho[cc + e] = 1.f;
-        }
-      }
-      for (int i = 0; i < kChunk; ++i) {
-        const bool live = i < L;
-        const size_t off = cb + (size_t)min(i, L - 1) * hs;
-        float racc = 0.f, aacc = 0.f;
-#pragma unroll
-        for (int cc = 0; cc < CQ; cc += 4) {
-          float al[4], kx[4], qx[4];
-          gate4(min(i, L - 1), qd * CQ + cc, al, false);
-          F4::load(k + off + cc, kx);
-          F4::load(q + off + cc, qx);
-          if constexpr (ACTQK) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              // rounded to E like the activated values of the fast path
-              kx[e] = (float)(E)(silu_f(kx[e]) * sInvNorm[0][min(i, L - 1)]);
-              qx[e] = (float)(E)(silu_f(qx[e]) * sInvNorm[1][min(i, L - 1)]);
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (i > j) rho[cc + e] *= live ? al[e] : 1.f;
-            const float wgt = i >= j ? kj[cc + e] * rho[cc + e] : 0.f;
-            racc += (live ? kx[e] : 0.f) * wgt;
-            aacc += (live ? qx[e] : 0.f) * wgt;
-          }
-        }
-        racc = group_sum<NQ>(racc);
-        aacc = group_sum<NQ>(aacc);
-        if (qd == 0) {
-          sR[i * LDR + j] = i > j ? sBeta[i] * racc : 0.f;
-          sA[i * LDR + j] = i >= j ? a.scale * aacc : 0.f;
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float y = __shfl(incl[j], l - CG);
+      excl[j] = th >= 1 ? y : 1.f;
     }
-    // Kend^T straight to the record (scattered; this path is rare)
-    E *gT = reinterpret_cast<E *>(rec + a.lay.ktt);
 #pragma unroll
     for (int u = 0; u < TPL; ++u)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const E x = ktt[u][jj];
-        gT[frag_index<E, 64>(c0 + jj, tb0 + u)] = x;
+      for (int j = 0; j < 4; ++j) pa[u][j] *= excl[j];
+    // optional input activation: q, k <- SiLU, then unit length over the d_k
+    // channels of the token (CG lanes hold one token's channels)
+    if constexpr (ACTQK) {
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        float kx[4], qx[4], sk = 0.f, sq = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kx[j] = silu_f((float)kraw[u][j]);
+          qx[j] = silu_f((float)qraw[u][j]);
+          sk += kx[j] * kx[j];
+          sq += qx[j] * qx[j];
+        }
+        const float rk = inv_norm(group_sum<CG>(sk)), rq = inv_norm(group_sum<CG>(sq));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kx[j] *= rk;
+          qx[j] *= rq;
+        }
+        kraw[u] = F4::pack(kx);
+        qraw[u] = F4::pack(qx);
+        // for the exact path, which reads q and k again from memory
+        if (cg == 0) {
+          sInvNorm[0][tb0 + u] = rk;
+          sInvNorm[1][tb0 + u] = rq;
+        }
+        __builtin_amdgcn_sched_barrier(0);  // one token at a time: bounds the live values
       }
-  }
-  __syncthreads();
-
-  if (w == 0 && th == 0) *reinterpret_cast<f32x4 *>(rec + a.lay.p63 + 4 * c0) = f32x4{p63[0], p63[1], p63[2], p63[3]};
-
-  // ---- T = (I + R)^{-1}.  Wave 0 inverts the four diagonal 16x16 blocks by
-  // forward substitution while waves 1-3 copy Kend^T (or A) out; then three
-  // levels of off-diagonal blocks, T_IJ = -T_II sum_K R_IK T_KJ, and the
-  // waves a level leaves idle write the row tiles of Tb = T Diag(beta) whose
-  // blocks are final.
-  E *gTb = reinterpret_cast<E *>(rec + a.lay.tb);
-  if (w == 0) {
-    const int b = l >> 4, jc = l & 15;
-    float X[16];
-#pragma unroll
-    for (int m = 0; m < 16; ++m) {
-      float s = m == jc ? 1.f : 0.f;
-#pragma unroll
-      for (int p = 0; p < m; ++p) s -= sR[(16 * b + m) * LDR + 16 * b + p] * X[p];
-      X[m] = s;
     }
+    if (th == TH - 1) *reinterpret_cast<f32x4 *>(sTau + w * DK + c0) = f32x4{incl[0], incl[1], incl[2], incl[3]};
+    __syncthreads();
+
+    // ---- chunk prefix a = (blocks before) * (in-block prefix); D_{0:63}
+    float fb[4], gb[4], p63[4];
+    {
+      f32x4 tau[4];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) sT[(16 * b + m) * LDR + 16 * b + jc] = X[m];
-  } else if (!exact) {
-    copy_out<LT>(rec + a.lay.ktt, sX, 64, kThreads - 64);
-  } else {
-    tile64_out<E, LDR>(gA, reinterpret_cast<const float *>(sX), nullptr, 0, 4, 64, kThreads - 64);
+      for (int b = 0; b < 4; ++b) tau[b] = *reinterpret_cast<const f32x4 *>(sTau + b * DK + c0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float before = 1.f, after = 1.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if (b < w) before *= tau[b][j];
+          if (b > w) after *= tau[b][j];
+        }
+        fb[j] = before;
+        gb[j] = after;
+        p63[j] = tau[0][j] * tau[1][j] * tau[2][j] * tau[3][j];
+      }
+    }
+    int weak = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) weak |= !(p63[j] >= 0x1p-100f);
+    const bool exact = __syncthreads_or(weak) != 0;   // uniform over the workgroup
+
+    // ---- Kbnd, s Qbnd (both paths) and k / a (fast path) into LDS
+    typename F4::vec ktt[TPL];   // Kend rows of this lane's tokens, packed (written later)
+#pragma unroll
+    for (int u = 0; u < TPL; ++u) {
+      const int tok = tb0 + u;
+      float kh[4], qh[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float av = pa[u][j] * fb[j];
+        kh[j] = kval(u, j) * av;
+        qh[j] = qval(u, j) * av * a.scale;
+        pa[u][j] = av;
+      }
+      *reinterpret_cast<typename F4::vec *>(sKh + LK::elem_off(tok, c0)) = F4::pack(kh);
+      *reinterpret_cast<typename F4::vec *>(sQh + LK::elem_off(tok, c0)) = F4::pack(qh);
+    }
+    if (!exact) {
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        const int tok = tb0 + u;
+        float kd[4], kt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          kd[j] = kval(u, j) * __builtin_amdgcn_rcpf(pa[u][j]);
+          kt[j] = kd[j] * p63[j];
+        }
+        *reinterpret_cast<typename F4::vec *>(sKd + LK::elem_off(tok, c0)) = F4::pack(kd);
+        ktt[u] = F4::pack(kt);
+      }
+    } else {
+      // D_{j+1:63} without division: in-lane exclusive suffix, times the later
+      // sub-ranges of the block, times the later blocks.  The gates are read
+      // again (this path is rare).
+      float sfx[TPL][4], run[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) run[j] = 1.f;
+#pragma unroll
+      for (int u = TPL - 1; u >= 0; --u) {
+        const int tok = tb0 + u;
+        float al[4];
+        gate4(min(tok, L - 1), c0, al, false);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sfx[u][j] = run[j];
+          run[j] *= tok < L ? al[j] : 1.f;
+        }
+      }
+      float later[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) later[j] = 1.f;
+      for (int d = 1; d < TH; ++d) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float y = __shfl(run[j], l + d * CG);
+          if (th + d < TH) later[j] *= y;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        float kt[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) kt[j] = kval(u, j) * sfx[u][j] * later[j] * gb[j];
+        ktt[u] = F4::pack(kt);
+      }
+    }
+    __syncthreads();
+
+    // ---- fast path: R^T and A^T tiles on the matrix cores.  Pair (I, J),
+    // I >= J: D[j][i] over j in block J (rows), i in block I (columns).
+    constexpr int NP = 3;  // pairs per wave: w, w + 4, w + 8 (< 10)
+    f32x4 rt[NP], at[NP];
+    if (!exact) {
+#pragma unroll
+      for (int s = 0; s < NP; ++s) {
+        const int p = w + 4 * s;
+        rt[s] = at[s] = zero4();
+        if (p < 10) {
+          int I, J;
+          tile_ij(p, I, J);
+#pragma unroll
+          for (int u = 0; u < LK::F::NU; ++u) {
+            const char *ad = sKd + LK::slot_off(J, u, l & 15, l >> 4);
+            rt[s] = slot_mma<E, DK>(ad, sKh + LK::slot_off(I, u, l & 15, l >> 4), rt[s]);
+            at[s] = slot_mma<E, DK>(ad, sQh + LK::slot_off(I, u, l & 15, l >> 4), at[s]);
+          }
+        }
+      }
+    }
+    copy_out<LK>(rec + a.lay.kh, sKh);
+    copy_out<LK>(rec + a.lay.qh, sQh);
+    __syncthreads();  // phase-1 images are dead from here on
+
+    E *gA = reinterpret_cast<E *>(rec + a.lay.aqk);
+    if (!exact) {
+      // R (scaled by beta_i, j < i) to LDS for the solve; A (j <= i) straight to
+      // the record: lane (i, g) holds A[i][16J + 4g .. +3], four consecutive
+      // elements of one record slot.
+#pragma unroll
+      for (int s = 0; s < NP; ++s) {
+        const int p = w + 4 * s;
+        if (p < 10) {
+          int I, J;
+          tile_ij(p, I, J);
+          const int i = 16 * I + (l & 15), jb = 16 * J + 4 * (l >> 4);
+          float rv[4], av[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            rv[r] = jb + r < i ? sBeta[i] * rt[s][r] : 0.f;
+            av[r] = jb + r <= i ? at[s][r] : 0.f;
+          }
+          *reinterpret_cast<f32x4 *>(sR + i * LDR + jb) = f32x4{rv[0], rv[1], rv[2], rv[3]};
+          *reinterpret_cast<typename F4::vec *>(gA + tri_index<E>(i, jb)) = F4::pack(av);
+        }
+      }
+      // blocks above the diagonal of A that share a stored slab with the
+      // diagonal are zero
+      for (int idx = tid; idx < 16 * 64; idx += kThreads) {
+        const int I = idx >> 8, J = (idx >> 6) & 3, ln = idx & 63;
+        if (J > I && 16 * J / FragShape<E, 64>::W < tri_slabs(I, (int)sizeof(E))) {
+          const float z[4] = {0.f, 0.f, 0.f, 0.f};
+          *reinterpret_cast<typename F4::vec *>(gA + tri_index<E>(16 * I + (ln & 15), 16 * J + 4 * (ln >> 4))) =
+              F4::pack(z);
+        }
+      }
+      // Kend^T into its LDS image (copied out after the next barrier): four
+      // consecutive tokens of one channel are contiguous there
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (TPL >= 4) {
+#pragma unroll
+          for (int u = 0; u < TPL; u += 4) {
+            typename F4::vec v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const E x = ktt[u + e][j];
+              v[e] = x;
+            }
+            *reinterpret_cast<typename F4::vec *>(sX + LT::elem_off(c0 + j, tb0 + u)) = v;
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < TPL; ++u) {
+            const E x = ktt[u][j];
+            *reinterpret_cast<E *>(sX + LT::elem_off(c0 + j, tb0 + u)) = x;
+          }
+        }
+      }
+    } else {
+      // R and A channel by channel: thread (j, part) runs D_{j+1:i} over i for
+      // CQ channels; the NQ parts of row j sit in neighbouring lanes and are
+      // summed across them.  At most 16 channels per lane keep the running
+      // products in few registers (this path is rare: with more channels per
+      // lane its registers would push values of the common path into
+      // scratch); with NQ > 4 the 64 rows take NQ/4 passes.
+      constexpr int CQ = DK / 4 > 16 ? 16 : DK / 4;
+      constexpr int NQ = DK / CQ;          // lanes per row
+      constexpr int JP = kThreads / NQ;    // rows per pass
+      float *sA = reinterpret_cast<float *>(sX);
+      const int qd = tid % NQ;
+#pragma unroll 1
+      for (int jb = 0; jb < kChunk; jb += JP) {
+        const int j = jb + tid / NQ;
+        const size_t cb = (size_t)t0 * hs + (size_t)h * DK + qd * CQ;
+        float kj[CQ], rho[CQ];
+#pragma unroll
+        for (int cc = 0; cc < CQ; cc += 4) {
+          F4::load(k + cb + (size_t)min(j, L - 1) * hs + cc, kj + cc);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (ACTQK) kj[cc + e] = (float)(E)(silu_f(kj[cc + e]) * sInvNorm[0][min(j, L - 1)]);
+            kj[cc + e] = j < L ? kj[cc + e] : 0.f;
+            rho[cc + e] = 1.f;
+          }
+        }
+        for (int i = 0; i < kChunk; ++i) {
+          const bool live = i < L;
+          const size_t off = cb + (size_t)min(i, L - 1) * hs;
+          float racc = 0.f, aacc = 0.f;
+#pragma unroll
+          for (int cc = 0; cc < CQ; cc += 4) {
+            float al[4], kx[4], qx[4];
+            gate4(min(i, L - 1), qd * CQ + cc, al, false);
+            F4::load(k + off + cc, kx);
+            F4::load(q + off + cc, qx);
+            if constexpr (ACTQK) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                // rounded to E like the activated values of the fast path
+                kx[e] = (float)(E)(silu_f(kx[e]) * sInvNorm[0][min(i, L - 1)]);
+                qx[e] = (float)(E)(silu_f(qx[e]) * sInvNorm[1][min(i, L - 1)]);
+              }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (i > j) rho[cc + e] *= live ? al[e] : 1.f;
+              const float wgt = i >= j ? kj[cc + e] * rho[cc + e] : 0.f;
+              racc += (live ? kx[e] : 0.f) * wgt;
+              aacc += (live ? qx[e] : 0.f) * wgt;
+            }
+          }
+          racc = group_sum<NQ>(racc);
+          aacc = group_sum<NQ>(aacc);
+          if (qd == 0) {
+            sR[i * LDR + j] = i > j ? sBeta[i] * racc : 0.f;
+            sA[i * LDR + j] = i >= j ? a.scale * aacc : 0.f;
+          }
+        }
+      }
+      // Kend^T straight to the record (scattered; this path is rare)
+      E *gT = reinterpret_cast<E *>(rec + a.lay.ktt);
+#pragma unroll
+      for (int u = 0; u < TPL; ++u)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const E x = ktt[u][jj];
+          gT[frag_index<E, 64>(c0 + jj, tb0 + u)] = x;
+        }
+    }
+    __syncthreads();
+
+    if (w == 0 && th == 0) *reinterpret_cast<f32x4 *>(rec + a.lay.p63 + 4 * c0) = f32x4{p63[0], p63[1], p63[2], p63[3]};
+
+    // ---- T = (I + R)^{-1}.  Wave 0 inverts the four diagonal 16x16 blocks by
+    // forward substitution while waves 1-3 copy Kend^T (or A) out; then three
+    // levels of off-diagonal blocks, T_IJ = -T_II sum_K R_IK T_KJ, and the
+    // waves a level leaves idle write the row tiles of Tb = T Diag(beta) whose
+    // blocks are final.
+    E *gTb = reinterpret_cast<E *>(rec + a.lay.tb);
+    if (w == 0) {
+      const int b = l >> 4, jc = l & 15;
+      float X[16];
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        float s = m == jc ? 1.f : 0.f;
+#pragma unroll
+        for (int p = 0; p < m; ++p) s -= sR[(16 * b + m) * LDR + 16 * b + p] * X[p];
+        X[m] = s;
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) sT[(16 * b + m) * LDR + 16 * b + jc] = X[m];
+    } else if (!exact) {
+      copy_out<LT>(rec + a.lay.ktt, sX, 64, kThreads - 64);
+    } else {
+      tile64_out<E, LDR>(gA, reinterpret_cast<const float *>(sX), nullptr, 0, 4, 64, kThreads - 64);
+    }
+    __syncthreads();
+    if (w < 3) inverse_offdiag_block<LDR>(w + 1, w, sR, sT);  // (1,0) (2,1) (3,2)
+    else tile64_out<E, LDR>(gTb, sT, sBeta, 0, 1, 192, 64);     // row tile 0 is final
+    __syncthreads();
+    if (w < 2) inverse_offdiag_block<LDR>(w + 2, w, sR, sT);  // (2,0) (3,1)
+    else tile64_out<E, LDR>(gTb, sT, sBeta, 1, 2, 128, 128);    // row tile 1
+    __syncthreads();
+    if (w == 0) inverse_offdiag_block<LDR>(3, 0, sR, sT);     // (3,0)
+    else tile64_out<E, LDR>(gTb, sT, sBeta, 2, 3, 64, 192);     // row tile 2
+    __syncthreads();
+    tile64_out<E, LDR>(gTb, sT, sBeta, 3, 4);                   // row tile 3
+  };
+
+  if constexpr (!SCHED) {
+    prep_one(blockIdx.x, blockIdx.y);
+    return;
   }
+  // Overlapped schedule (a separate instantiation): records of the units
+  // u = x (mod 8) are prepared on XCD x, chunk-major (chunk 0 of every such
+  // unit first).  A workgroup takes the next task from its XCD's counter (the
+  // dispatcher deals workgroups to the eight XCDs in turn, and the grid holds
+  // eight times the largest per-XCD task count, so every task is taken), and
+  // publishes the finished record by setting bit ci % 32 of the unit's ready
+  // word ci / 32 once its stores have reached L2.
+  __shared__ int sTask;
+  const int x = xcd_id();
+  const int nux = a.n_units > x ? (a.n_units - x + 7) / 8 : 0;
+  if (threadIdx.x == 0)
+    sTask = __hip_atomic_fetch_add(a.ctl + kSchedPrepNext + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
-  if (w < 3) inverse_offdiag_block<LDR>(w + 1, w, sR, sT);  // (1,0) (2,1) (3,2)
-  else tile64_out<E, LDR>(gTb, sT, sBeta, 0, 1, 192, 64);     // row tile 0 is final
+  const int t = sTask;
+  if (t >= nux * a.src.nct) return;
+  const int u = x + 8 * (t % nux), ci = t / nux;
+  const long long slot = (long long)(u / a.H) * a.src.nct + ci;
+  prep_one(slot, u % a.H);
+  __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are done
   __syncthreads();
-  if (w < 2) inverse_offdiag_block<LDR>(w + 2, w, sR, sT);  // (2,0) (3,1)
-  else tile64_out<E, LDR>(gTb, sT, sBeta, 1, 2, 128, 128);    // row tile 1
-  __syncthreads();
-  if (w == 0) inverse_offdiag_block<LDR>(3, 0, sR, sT);     // (3,0)
-  else tile64_out<E, LDR>(gTb, sT, sBeta, 2, 3, 64, 192);     // row tile 2
-  __syncthreads();
-  tile64_out<E, LDR>(gTb, sT, sBeta, 3, 4);                   // row tile 3
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_or(a.ready + (size_t)u * a.ready_words + (ci >> 5), 1 << (ci & 31), __ATOMIC_RELAXED,
+                          __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ======================================================= kernel 2: chunk scan
@@ -838,6 +884,11 @@ struct ScanKArgs {
   float scale;
   int n_units;                           // sequences * heads
   int wg_per_unit;                       // workgroups per unit (value tiles / waves per WG)
+  // overlapped schedule only: ready words (ready_words per unit, bit c % 32
+  // of word c / 32 set once chunk c's record is in L2) and control words
+  const int *ready;
+  int ready_words;
+  int *ctl;
 };
 
 // B operands built from accumulator tiles.  Tile q of a K x 16 operand holds
@@ -967,6 +1018,150 @@ template <int DK, typename E> struct RecordShape {
   static constexpr int bytes = (p63 + DK * 4 + 1023) / 1024 * 1024;
 };
 
+// One chunk of the scan for one compute wave, which owns 16*NT value columns
+// and keeps S^T (d_k x 16*NT) in fp32 accumulator tiles st[d_k/16][NT]:
+//   X_top = Kbnd S^T, X_bot = s Qbnd S^T, Ebar = V - X_top, E = Tb Ebar,
+//   O = X_bot + A E (into ov), S^T <- D_{0:63} S^T + Kend^T E.
+// `recb` is the chunk's record image in LDS; `vs` points at the wave's first
+// value column of the chunk's value tile in LDS (row stride VSTRIDE
+// elements).  Every product loop runs slab-major (the k slab outer, the
+// 16-row tiles inner), so consecutive matrix-core products are independent
+// and none waits for the previous one's result; the LDS operand reads of
+// later phases are issued early, in the order they are used.
+template <int DK, typename E, int NT, int VSTRIDE>
+__device__ __forceinline__ void scan_chunk(const char *recb, const E *vs, f32x4 (*st)[NT], f32x4 (*ov)[NT]) {
+  typedef RecordShape<DK, E> RS;
+  typedef FragShape<E, DK> FK;   // products over d_k
+  typedef FragShape<E, 64> FT;   // products over the 64 tokens
+  constexpr int CT = DK / 16;
+  constexpr int TILE_K = FK::NU * 64 * FK::KS;   // elements per 16-row tile, K = d_k
+  constexpr int TILE_T = FT::NU * 64 * FT::KS;   // elements per 16-row tile, K = 64
+  const int l = lane_id(), col = l & 15, g = l >> 4;
+  typedef BOps<E, DK> BK;
+  typedef BOps<E, 64> BT;
+  constexpr int UK = FK::NU, UT = FT::NU;          // slabs over d_k, over 64 tokens
+  const E *Kh = reinterpret_cast<const E *>(recb + RS::kh);
+  const E *Qh = reinterpret_cast<const E *>(recb + RS::qh);
+  const E *KtT = reinterpret_cast<const E *>(recb + RS::ktt);
+  const E *Tb = reinterpret_cast<const E *>(recb + RS::tb);
+  const E *Aq = reinterpret_cast<const E *>(recb + RS::aqk);
+  const float *P63 = reinterpret_cast<const float *>(recb + RS::p63);
+  // row tile I of Tb and A only needs slabs holding columns < 16 (I + 1)
+  auto need = [](int I, int u) { return u * FT::W < 16 * (I + 1); };
+
+  // B operands from the state; X_top = Kbnd S^T, X_bot = s Qbnd S^T
+  BK sb[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4 col_tiles[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) col_tiles[ct] = st[ct][nt];
+    sb[nt].build(col_tiles);
+  }
+  f32x4 xt[4][NT], xb[4][NT];
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) xt[I][nt] = xb[I][nt] = zero4();
+#pragma unroll
+  for (int u = 0; u < UK; ++u) {
+    typename BK::frag fk[4], fq[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      fk[I] = BK::load1(Kh + I * TILE_K, u);
+      fq[I] = BK::load1(Qh + I * TILE_K, u);
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        xt[I][nt] = sb[nt].mma1(fk[I], u, xt[I][nt]);
+        xb[I][nt] = sb[nt].mma1(fq[I], u, xb[I][nt]);
+      }
+  }
+  // operands of the later phases
+  typename BT::frag ftb[4][UT], faq[4][UT], fkt[CT][UT];
+  float vv[NT][4][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vv[nt][I][r] = to_f(vs[(16 * I + 4 * g + r) * VSTRIDE + 16 * nt + col]);
+#pragma unroll
+  for (int u = 0; u < UT; ++u)
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      if (need(I, u)) ftb[I][u] = BT::load1(Tb + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
+#pragma unroll
+  for (int u = 0; u < UT; ++u)
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      if (need(I, u)) faq[I][u] = BT::load1(Aq + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
+#pragma unroll
+  for (int u = 0; u < UT; ++u)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) fkt[ct][u] = BT::load1(KtT + ct * TILE_T, u);
+  f32x4 p[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) p[ct] = *reinterpret_cast<const f32x4 *>(P63 + 16 * ct + 4 * g);
+
+  // Ebar = V - X_top ; E = Tb Ebar
+  BT ebo[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4 eb[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) eb[I][r] = vv[nt][I][r] - xt[I][nt][r];
+    ebo[nt].build(eb);
+  }
+  f32x4 e[4][NT];
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) e[I][nt] = zero4();
+#pragma unroll
+  for (int u = 0; u < UT; ++u)
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      if (need(I, u))
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) e[I][nt] = ebo[nt].mma1(ftb[I][u], u, e[I][nt]);
+  // O = s Qbnd S^T + A E ;  S^T = D_{0:63} S^T + Kend^T E
+  BT eo[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4 et[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) et[I] = e[I][nt];
+    eo[nt].build(et);
+  }
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) ov[I][nt] = xb[I][nt];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[ct][nt][r] *= p[ct][r];
+#pragma unroll
+  for (int u = 0; u < UT; ++u) {
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      if (need(I, u))
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) ov[I][nt] = eo[nt].mma1(faq[I][u], u, ov[I][nt]);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) st[ct][nt] = eo[nt].mma1(fkt[ct][u], u, st[ct][nt]);
+  }
+}
+
 // Scan.  A workgroup serves one unit (sequence, head): CW compute waves, each
 // owning 16*NT value columns and keeping S^T (d_k x 16*NT) in fp32
 // accumulator tiles, plus one copy wave that streams the chunk records (and
@@ -978,7 +1173,7 @@ template <int DK, typename E> struct RecordShape {
 // conflict-free 16-byte reads, shared by the NT column tiles) and its B
 // operand from the wave's own accumulators.  Workgroups of one unit get ids
 // congruent mod 8, which the dispatcher sends to one XCD.
-template <int DK, typename E, int NT, int CW, int NCP>
+template <int DK, typename E, int NT, int CW, int NCP, bool SCHED = false>
 __global__ __launch_bounds__(64 * (CW + NCP)) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void chunk_scan_kernel(ScanKArgs a) {
   typedef RecordShape<DK, E> RS;
@@ -1005,11 +1200,25 @@ void chunk_scan_kernel(ScanKArgs a) {
   __shared__ __attribute__((aligned(16))) char otile[2][NBUF == 2 ? 64 * OROW : 16];
 
   const int w = wave_id(), l = lane_id(), col = l & 15, g = l >> 4;
-  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
-  const int u = (slot / a.wg_per_unit) * 8 + xcd;
+  int u, grp;  // unit and value-column group of this workgroup
+  if constexpr (SCHED) {
+    // overlapped schedule: the next (unit, group) ticket of this XCD, whose
+    // prep workers produce the records of units u = x (mod 8)
+    __shared__ int sTicket;
+    const int x = xcd_id();
+    if (threadIdx.x == 0)
+      sTicket = __hip_atomic_fetch_add(a.ctl + kSchedScanNext + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    u = x + 8 * (sTicket / a.wg_per_unit);
+    grp = sTicket % a.wg_per_unit;
+  } else {
+    const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+    u = (slot / a.wg_per_unit) * 8 + xcd;
+    grp = slot % a.wg_per_unit;
+  }
   if (u >= a.n_units) return;
   const int n = u / a.H, h = u % a.H;
-  const int vwg = (slot % a.wg_per_unit) * (CW * VC);  // first value column of the workgroup
+  const int vwg = grp * (CW * VC);  // first value column of the workgroup
   const int H = a.H, DV = a.dv;
   const bool copier = w >= CW;
   const int cpi = w - CW;                  // index among the copy waves
@@ -1087,9 +1296,45 @@ void chunk_scan_kernel(ScanKArgs a) {
                                              rs, off, 0, 2);
     }
   };
+  // Overlapped schedule: chunk ci's record may be copied once bit ci % 32 of
+  // the unit's ready word ci / 32 is set.  Lane 0 reads the word (bypassing
+  // the CU's L1: agent-scope load) only when the bit is not known yet; a wait
+  // longer than 1.3 s (the prep could not run) sets kSchedErrTimeout and the
+  // wave stops waiting: the results are then wrong, but the kernel always
+  // finishes.
+  unsigned known = 0;
+  int known_word = -1;
+  bool gave_up = false;
+  auto wait_rec = [&](int ci) {
+    if constexpr (SCHED) {
+      const int wd = ci >> 5;
+      const unsigned bit = 1u << (ci & 31);
+      if (wd != known_word) {
+        known_word = wd;
+        known = 0;
+      }
+      if ((known & bit) || gave_up) return;
+      const int *word = a.ready + (size_t)u * a.ready_words + wd;
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      for (;;) {
+        unsigned v = 0;
+        if (l == 0) v = (unsigned)__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        known = __builtin_amdgcn_readfirstlane(v);
+        if (known & bit) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > (1ull << 27)) {  // 100 MHz ticks
+          if (l == 0) __hip_atomic_fetch_or(a.ctl + kSchedError, kSchedErrTimeout, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+          gave_up = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+  };
   if (copier) {
     if (NBUF == 2) {
       if (nchunks > 0) {
+        wait_rec(0);
         copy_rec(0, rec0);
         if (vcopier) copy_v(0, vring[0]);
       }
@@ -1104,7 +1349,10 @@ void chunk_scan_kernel(ScanKArgs a) {
         // record buffer (ci+1)%2 and value slot (ci+2)%3 held chunk ci-1, which
         // every compute wave finished before the barrier that ended the
         // previous step
-        if (ci + 1 < nchunks) copy_rec(ci + 1, (ci & 1) ? rec0 : rec1);
+        if (ci + 1 < nchunks) {
+          wait_rec(ci + 1);
+          copy_rec(ci + 1, (ci & 1) ? rec0 : rec1);
+        }
         // the compute waves staged chunk ci-1's outputs before the last barrier
         if (cpi == 0 && ci > 0) store_tile(ci - 1, otile[(ci - 1) & 1]);
         if (vcopier && ci + 2 < nchunks) {
@@ -1139,135 +1387,8 @@ void chunk_scan_kernel(ScanKArgs a) {
       st[ct][nt] = a.S0 ? *reinterpret_cast<const f32x4 *>(a.S0 + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g)
                         : zero4();
 
-  // One chunk.  Every product loop runs slab-major (the k slab outer, the
-  // 16-row tiles inner), so consecutive matrix-core products are independent
-  // and none waits for the previous one's result; the LDS operand reads of
-  // later phases are issued early, in the order they are used.
   auto compute = [&](const char *recb, const E *vs, f32x4 (*ov)[NT]) {
-    typedef BOps<E, DK> BK;
-    typedef BOps<E, 64> BT;
-    constexpr int UK = FK::NU, UT = FT::NU;          // slabs over d_k, over 64 tokens
-    const E *Kh = reinterpret_cast<const E *>(recb + RS::kh);
-    const E *Qh = reinterpret_cast<const E *>(recb + RS::qh);
-    const E *KtT = reinterpret_cast<const E *>(recb + RS::ktt);
-    const E *Tb = reinterpret_cast<const E *>(recb + RS::tb);
-    const E *Aq = reinterpret_cast<const E *>(recb + RS::aqk);
-    const float *P63 = reinterpret_cast<const float *>(recb + RS::p63);
-    vs += w * VC;
-    // row tile I of Tb and A only needs slabs holding columns < 16 (I + 1)
-    auto need = [](int I, int u) { return u * FT::W < 16 * (I + 1); };
-
-    // B operands from the state; X_top = Kbnd S^T, X_bot = s Qbnd S^T
-    BK sb[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 col_tiles[CT];
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) col_tiles[ct] = st[ct][nt];
-      sb[nt].build(col_tiles);
-    }
-    f32x4 xt[4][NT], xb[4][NT];
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) xt[I][nt] = xb[I][nt] = zero4();
-#pragma unroll
-    for (int u = 0; u < UK; ++u) {
-      typename BK::frag fk[4], fq[4];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) {
-        fk[I] = BK::load1(Kh + I * TILE_K, u);
-        fq[I] = BK::load1(Qh + I * TILE_K, u);
-      }
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          xt[I][nt] = sb[nt].mma1(fk[I], u, xt[I][nt]);
-          xb[I][nt] = sb[nt].mma1(fq[I], u, xb[I][nt]);
-        }
-    }
-    // operands of the later phases
-    typename BT::frag ftb[4][UT], faq[4][UT], fkt[CT][UT];
-    float vv[NT][4][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vv[nt][I][r] = to_f(vs[(16 * I + 4 * g + r) * WC + 16 * nt + col]);
-#pragma unroll
-    for (int u = 0; u < UT; ++u)
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-        if (need(I, u)) ftb[I][u] = BT::load1(Tb + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
-#pragma unroll
-    for (int u = 0; u < UT; ++u)
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-        if (need(I, u)) faq[I][u] = BT::load1(Aq + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
-#pragma unroll
-    for (int u = 0; u < UT; ++u)
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct) fkt[ct][u] = BT::load1(KtT + ct * TILE_T, u);
-    f32x4 p[CT];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) p[ct] = *reinterpret_cast<const f32x4 *>(P63 + 16 * ct + 4 * g);
-
-    // Ebar = V - X_top ; E = Tb Ebar
-    BT ebo[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 eb[4];
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) eb[I][r] = vv[nt][I][r] - xt[I][nt][r];
-      ebo[nt].build(eb);
-    }
-    f32x4 e[4][NT];
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) e[I][nt] = zero4();
-#pragma unroll
-    for (int u = 0; u < UT; ++u)
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-        if (need(I, u))
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) e[I][nt] = ebo[nt].mma1(ftb[I][u], u, e[I][nt]);
-    // O = s Qbnd S^T + A E ;  S^T = D_{0:63} S^T + Kend^T E
-    BT eo[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      f32x4 et[4];
-#pragma unroll
-      for (int I = 0; I < 4; ++I) et[I] = e[I][nt];
-      eo[nt].build(et);
-    }
-#pragma unroll
-    for (int I = 0; I < 4; ++I)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) ov[I][nt] = xb[I][nt];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[ct][nt][r] *= p[ct][r];
-#pragma unroll
-    for (int u = 0; u < UT; ++u) {
-#pragma unroll
-      for (int I = 0; I < 4; ++I)
-        if (need(I, u))
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) ov[I][nt] = eo[nt].mma1(faq[I][u], u, ov[I][nt]);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) st[ct][nt] = eo[nt].mma1(fkt[ct][u], u, st[ct][nt]);
-    }
+    scan_chunk<DK, E, NT, WC>(recb, vs + w * VC, st, ov);
   };
 
   // outputs of chunk ci, stored after the next barrier so their latency
@@ -1344,32 +1465,37 @@ void chunk_scan_kernel(ScanKArgs a) {
       *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
 }
 
+// Zeroes the ready words and control words of the overlapped schedule.
+__global__ void sched_clear_kernel(int *p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
 // The prep kernel for a gate form, with or without the q, k activation.
-template <int DK, typename E, bool ACTQK>
+template <int DK, typename E, bool ACTQK, bool SCHED = false>
 void launch_prep(int gate, dim3 grid, hipStream_t stream, const PrepKArgs &pa) {
   switch (gate) {
     case kGateScalar:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
       break;
     case kGateNone:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
       break;
     case kGateLogChannel:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogChannel, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogChannel, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
       break;
     case kGateLogScalar:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogScalar, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogScalar, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
       break;
     case kGateSoftplusChannel:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusChannel, ACTQK>), grid, dim3(kThreads), 0, stream,
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusChannel, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream,
                          pa);
       break;
     case kGateSoftplusScalar:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusScalar, ACTQK>), grid, dim3(kThreads), 0, stream,
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusScalar, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream,
                          pa);
       break;
     default:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel, ACTQK>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
   }
 }
 
@@ -1389,6 +1515,123 @@ void launch_scan(int cw, dim3 grid, hipStream_t stream, const ScanKArgs &sa) {
 }
 
 // ================================================================ dispatch
+// CU-masked streams of the overlapped schedule, one set per device: the scan
+// on the first 128 CUs of the runtime's mask numbering (16 on each XCD) and
+// the prep on the other 128, so neither can hold the CUs the other needs.
+// Created on first use and kept for the life of the process.
+struct OverlapCtx {
+  bool tried = false, ok = false;
+  hipStream_t scan = nullptr, prep = nullptr;
+  hipEvent_t fork = nullptr, done_scan = nullptr, done_prep = nullptr;
+};
+std::mutex g_overlap_mu;  // guards g_overlap and the event sequence of a launch
+OverlapCtx g_overlap[64];
+constexpr int kScanCUs = 128;
+
+// The current device's streams, or null if the schedule cannot run there
+// (caller holds g_overlap_mu).
+OverlapCtx *overlap_ctx() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  OverlapCtx &c = g_overlap[dev];
+  if (!c.tried) {
+    c.tried = true;
+    int ncu = 0;
+    hipDeviceProp_t prop;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return nullptr;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return nullptr;
+    // eight XCDs of 32 CUs (the whole MI355X as one device)
+    if (ncu != 256 || std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return nullptr;
+    uint32_t ms[8] = {0}, mp[8] = {0};
+    for (int i = 0; i < ncu; ++i) (i < kScanCUs ? ms : mp)[i / 32] |= 1u << (i % 32);
+    if (hipExtStreamCreateWithCUMask(&c.scan, 8, ms) != hipSuccess) return nullptr;
+    if (hipExtStreamCreateWithCUMask(&c.prep, 8, mp) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&c.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&c.done_scan, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&c.done_prep, hipEventDisableTiming) != hipSuccess) return nullptr;
+    c.ok = true;
+  }
+  return c.ok ? &c : nullptr;
+}
+
+// Shapes the overlapped schedule supports: dense bf16 batches at
+// d_k = d_v = 128 (two records and two value tiles fill the scan's LDS).
+template <int DK, typename E> bool overlap_supported(const PrefillArgs &a) {
+  return DK == 128 && a.dv == 128 && sizeof(E) == 2 && !a.cu_seqlens && a.plan.sched_bytes > 0;
+}
+
+// Automatic choice: the overlap pays when the scan's workgroups (four per
+// unit at d_v = 128) fit on half of the chip, which the two-phase scan would
+// leave idle, and the chain is long enough to amortise the fork and join.
+bool overlap_chosen(const PrefillArgs &a, int nct) {
+  if (a.schedule == kScheduleTwoPhase) return false;
+  if (a.schedule == kScheduleOverlap) return true;
+  return (long long)a.B * a.H * (a.dv / 32) <= kScanCUs && nct >= 8;
+}
+
+// Overlapped schedule: clear the ready words on the caller's stream, then
+// fork to the two masked streams (the scan and the prep run at once, the
+// scan's copy waves waiting on each record's ready bit), and join back.
+template <int DK, typename E>
+hipError_t run_prefill_overlap(const PrefillArgs &a, hipStream_t stream, PrepKArgs pa, const ChunkRecordLayout &lay,
+                               char *records, OverlapCtx &ov) {
+  const WorkspacePlan &P = a.plan;
+  const int nct = (a.T + kChunk - 1) / kChunk;
+  const int n_units = a.B * a.H;
+  const int words = (nct + 31) / 32;  // ready words per unit
+  int *ready = reinterpret_cast<int *>(a.ws + P.sched);
+  int *ctl = ready + P.max_chunks * a.H;  // n_units * words <= chunk slots * heads
+  const int nclear = (int)(P.max_chunks * a.H) + kSchedWords;
+  hipLaunchKernelGGL(sched_clear_kernel, dim3((unsigned)min(64, (nclear + 255) / 256)), dim3(256), 0, stream, ready,
+                     nclear);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = hipEventRecord(ov.fork, stream)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(ov.scan, ov.fork, 0)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(ov.prep, ov.fork, 0)) != hipSuccess) return e;
+
+  if constexpr (DK == 128 && sizeof(E) == 2) {
+    ScanKArgs sa;
+    sa.v = a.v;
+    sa.S0 = a.S0;
+    sa.o = a.o;
+    sa.S_final = a.S_final;
+    sa.ws_records = records;
+    sa.lay = lay;
+    sa.H = a.H;
+    sa.dv = a.dv;
+    sa.T = a.T;
+    sa.nct = nct;
+    sa.seq_tok0 = sa.seq_chunk0 = nullptr;
+    sa.scale = a.scale;
+    sa.n_units = n_units;
+    sa.wg_per_unit = a.dv / 32;  // two compute waves of 16 columns per workgroup
+    sa.ready = ready;
+    sa.ready_words = words;
+    sa.ctl = ctl;
+    // a ticket per (unit, group): eight times those of the XCD with most units
+    const dim3 sg((unsigned)(8 * ((n_units + 7) / 8) * sa.wg_per_unit));
+    hipLaunchKernelGGL((chunk_scan_kernel<DK, E, 1, 2, 3, true>), sg, dim3(64 * 5), 0, ov.scan, sa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+
+    pa.ready = ready;
+    pa.ctl = ctl;
+    pa.ready_words = words;
+    pa.n_units = n_units;
+    // one workgroup per task: eight times the task count of the XCD with most units
+    const dim3 pg((unsigned)(8LL * ((n_units + 7) / 8) * nct));
+    if (a.act & kActQK)
+      launch_prep<DK, E, true, true>(a.gate, pg, ov.prep, pa);
+    else
+      launch_prep<DK, E, false, true>(a.gate, pg, ov.prep, pa);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if ((e = hipEventRecord(ov.done_scan, ov.scan)) != hipSuccess) return e;
+  if ((e = hipEventRecord(ov.done_prep, ov.prep)) != hipSuccess) return e;
+  if ((e = hipStreamWaitEvent(stream, ov.done_scan, 0)) != hipSuccess) return e;
+  return hipStreamWaitEvent(stream, ov.done_prep, 0);
+}
+
 template <int DK, typename E>
 hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
   const WorkspacePlan &P = a.plan;
@@ -1424,6 +1667,12 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.scale = a.scale;
     pa.ws_records = records;
     pa.lay = lay;
+    pa.ready = pa.ctl = nullptr;
+    pa.ready_words = pa.n_units = 0;
+    if (overlap_supported<DK, E>(a) && overlap_chosen(a, nct)) {
+      std::lock_guard<std::mutex> lock(g_overlap_mu);
+      if (OverlapCtx *ov = overlap_ctx()) return run_prefill_overlap<DK, E>(a, stream, pa, lay, records, *ov);
+    }
     const dim3 pg((unsigned)P.max_chunks, a.H);
     if (a.act & kActQK)
       launch_prep<DK, E, true>(a.gate, pg, stream, pa);

@@ -43,7 +43,11 @@ def test_workspace_size(kda):
     # k-slabs that reach the diagonal (6 slabs of 32 columns in bf16) and d_k
     # floats, rounded up to 1 KiB
     rec = (3 * 64 * 128 * 2 + 2 * 6 * 1024 + 128 * 4 + 1023) // 1024 * 1024
-    assert kda.chunk_fwd_workspace_size(4, 2048, 16, 128, 128, -1, kda.KDA_BF16) == 4 * 32 * 16 * rec
+    # then one int32 ready flag per record and 64 control words of the
+    # overlapped schedule, rounded up to 256 bytes
+    nrec = 4 * 32 * 16
+    sched = ((nrec + 64) * 4 + 255) // 256 * 256
+    assert kda.chunk_fwd_workspace_size(4, 2048, 16, 128, 128, -1, kda.KDA_BF16) == nrec * rec + sched
     assert kda.chunk_fwd_workspace_size(2, 0, 3, 32, 32, -1, kda.KDA_F32) == 0
     # packed: tables plus (ceil(T/64) + N) chunk slots
     packed = kda.chunk_fwd_workspace_size(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)

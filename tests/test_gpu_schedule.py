@@ -1,0 +1,107 @@
+"""The overlapped prefill schedule on the GPU: chunk preparation and the scan
+run at once on two disjoint sets of compute units, the scan taking each
+chunk's record as soon as its ready flag is set (page "Kimi Delta Attention
+(KDA)", section "Two schedules of computation for one recurrence": the
+parallel chunk stage feeds the sequential scan).  Both schedules execute the
+same arithmetic per chunk, so their results must be bitwise equal; one case
+per group is also checked against the fp64 oracle, and the schedule's error
+word (a timed-out wait or a record from another XCD) must stay clear."""
+import numpy as np
+import pytest
+import torch
+
+from linear_attention_kda_amd import inputs
+from tests.gpu_cases import TOL, announce, check, oracle_prefill, to_dev
+
+pytestmark = pytest.mark.gpu
+
+REC_BYTES = 62464          # one d=128 bf16 chunk record (see test_abi)
+ERR_WORD = 16              # index of the error word among the control words
+
+
+def _run(inp, schedule, gate="channel", act=0, ws=None):
+    import linear_attention_kda_amd as kda
+    prev = kda.set_schedule(schedule)
+    try:
+        o, S = kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp.get("S0"),
+                             gate=gate, act=act, workspace=ws)
+        torch.cuda.synchronize()
+    finally:
+        kda.set_schedule(prev)
+    return o, S
+
+
+def _workspace(B, T, H):
+    import linear_attention_kda_amd as kda
+    n = kda.chunk_fwd_workspace_size(B, T, H, 128, 128, -1, kda.KDA_BF16)
+    return torch.zeros(n, dtype=torch.uint8, device="cuda")
+
+
+def _error_word(ws, B, T, H):
+    nrec = B * ((T + 63) // 64) * H
+    off = nrec * REC_BYTES + (nrec + ERR_WORD) * 4
+    return int(ws[off:off + 4].cpu().numpy().view(np.int32)[0])
+
+
+@pytest.mark.parametrize("B,T,H,s0", [
+    (1, 64, 1, None),        # one chunk
+    (1, 65, 2, 0.02),        # a ragged second chunk
+    (2, 700, 3, 0.02),       # units not a multiple of eight
+    (4, 2048, 16, None),     # the prefill workload's shape, 64 units
+    (3, 1000, 32, 0.02),     # 96 units: more than the 64 scan CUs, so units take turns
+])
+def test_overlap_equals_two_phase(B, T, H, s0):
+    announce(f"schedule overlap vs two-phase, dense bf16 d=128 B={B} T={T} H={H} S0={s0}")
+    inp = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=s0, seed=21))
+    ws = _workspace(B, T, H)
+    o1, S1 = _run(inp, "overlap", ws=ws)
+    assert _error_word(ws, B, T, H) == 0
+    o2, S2 = _run(inp, "two_phase")
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_overlap_oracle():
+    announce("schedule overlap vs the fp64 oracle, B=2 T=300 H=4 d=128 bf16 with S0")
+    inp = to_dev(inputs.dense(2, 300, 4, 128, 128, torch.bfloat16, s0_std=0.02, seed=22))
+    o, S = _run(inp, "overlap")
+    o_ref, S_ref = oracle_prefill(inp)
+    check("o", o, o_ref, TOL[torch.bfloat16])
+    check("S_final", S, S_ref, TOL[torch.bfloat16])
+
+
+@pytest.mark.parametrize("gate", ["scalar", "none", "log_channel", "softplus_channel"])
+def test_overlap_gate_forms(gate):
+    announce(f"schedule overlap vs two-phase, gate form {gate}, B=2 T=520 H=4")
+    inp = to_dev(inputs.dense(2, 520, 4, 128, 128, torch.bfloat16, s0_std=0.02, seed=23, gate_form=gate))
+    o1, S1 = _run(inp, "overlap", gate=gate)
+    o2, S2 = _run(inp, "two_phase", gate=gate)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_overlap_fused_inputs_and_strong_decay():
+    import linear_attention_kda_amd as kda
+    announce("schedule overlap vs two-phase: fused input activations; a gate of 0 (exact prep path)")
+    inp = to_dev(inputs.dense(2, 400, 4, 128, 128, torch.bfloat16, s0_std=0.02, seed=24))
+    act = kda.KDA_ACT_QK_SILU_L2NORM | kda.KDA_ACT_BETA_SIGMOID
+    o1, S1 = _run(inp, "overlap", act=act)
+    o2, S2 = _run(inp, "two_phase", act=act)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    inp["alpha"][:, 100:140] = 0.0
+    o1, S1 = _run(inp, "overlap")
+    o2, S2 = _run(inp, "two_phase")
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+    o_ref, S_ref = oracle_prefill(inp)
+    check("o", o1, o_ref, TOL[torch.bfloat16])
+    check("S_final", S1, S_ref, TOL[torch.bfloat16])
+
+
+def test_overlap_repeated_calls_share_workspace():
+    announce("schedule overlap: three calls in a row on one workspace with different inputs")
+    B, T, H = 2, 640, 8
+    ws = _workspace(B, T, H)
+    for seed in (31, 32, 33):
+        inp = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=0.02, seed=seed))
+        o1, S1 = _run(inp, "overlap", ws=ws)
+        assert _error_word(ws, B, T, H) == 0
+        o2, S2 = _run(inp, "two_phase")
+        assert torch.equal(o1, o2) and torch.equal(S1, S2)
