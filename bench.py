@@ -35,9 +35,9 @@ NSETS = 4
 # Each figure belongs to the kernel source with the given sha256 prefix and is
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
-    "prefill": ("kda_prefill.hip", "0b0cfa0e7add40ac", 480_363_213),
-    "decode": ("kda_decode.hip", "f38948dc0d2cc0e0", 1_086_888_550),
-    "decode_tokens": ("kda_decode.hip", "f38948dc0d2cc0e0", 1_125_201_920),
+    "prefill": ("kda_prefill.hip", "53a0291cb62e9922", 464_175_104),
+    "decode": ("kda_decode.hip", "fab9d9aec69d4611", 1_086_896_640),
+    "decode_tokens": ("kda_decode.hip", "fab9d9aec69d4611", 1_125_209_088),
 }
 
 
@@ -126,6 +126,45 @@ def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None, act
     return dict(B=B, T=T, H=H, dk=dk, dv=dv, wall_s=wall, ms_per_step=wall * 1e3 / steps,
                 call_ms_mean=mean_ms, call_ms_median=single[len(single) // 2], call_ms_min=single[0],
                 tokens=B * T)
+
+
+def bench_long_context(args, torch, kda, inputs, steps=10, warmup=2):
+    """The long-context workload (B=1, H=32, T=65536, S0 given): one chunk
+    chain of 1024 steps per (sequence, head), under the automatic schedule
+    (which overlaps prep and scan for this shape) and under two-phase."""
+    w = inputs.WORKLOADS["long"]
+    B, T, H, dk, dv = w["B"], w["T"], w["H"], w["dk"], w["dv"]
+    dev = torch.device("cuda:0")
+    inp = inputs.workload("long", seed=0, device=dev)
+    o = torch.empty_like(inp["v"])
+    S = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.chunk_fwd_workspace_size(B, T, H, dk, dv, -1, kda.KDA_BF16), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for sched in ("auto", "two_phase"):
+        prev = kda.set_schedule(sched)
+        for _ in range(warmup):
+            kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"], out=o,
+                          S_final=S, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"], out=o,
+                          S_final=S, workspace=ws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kda.set_schedule(prev)
+        out[sched] = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = prefill_bytes(B, T, H, dk, dv, s0=True)
+    ach = nbytes / (out["auto"] * 1e-6) / 1e9
+    return {"workload": f"long-context prefill B={B} H={H} T={T} d_k=d_v={dk} bf16, S0 given",
+            "calls": steps, "call_us_mean": round(out["auto"], 1),
+            "call_us_two_phase": round(out["two_phase"], 1),
+            "tokens_per_s": round(B * T / (out["auto"] * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
 
 
 def decode_tokens_bytes(N, H, dk, dv, Tk, esize=2):
@@ -261,6 +300,10 @@ def main():
     ap.add_argument("--no-gate-forms", action="store_true",
                     help="skip the scalar-gate prefill line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--long-context", action="store_true",
+                    help="also time the long-context workload (B=1 H=32 T=65536) under both schedules")
+    ap.add_argument("--long-only", action="store_true",
+                    help="time only the long-context workload (for profiling); prints its object")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -273,6 +316,9 @@ def main():
     import linear_attention_kda_amd as kda
     from linear_attention_kda_amd import inputs
 
+    if args.long_only:
+        print(json.dumps({"long_context": bench_long_context(args, torch, kda, inputs)}), flush=True)
+        return
     pf = bench_prefill(args, torch, kda, inputs)
     nbytes = prefill_bytes(pf["B"], pf["T"], pf["H"], pf["dk"], pf["dv"])
     flops = prefill_flops(pf["B"], pf["T"], pf["H"], pf["dk"], pf["dv"])
@@ -326,6 +372,8 @@ def main():
                 "call_us_mean": round(sg["call_ms_mean"] * 1e3, 2),
                 "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": sb}}
+    if args.long_context:
+        result["long_context"] = bench_long_context(args, torch, kda, inputs)
     if args.copy_calib_mib:
         n = args.copy_calib_mib << 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
