@@ -66,7 +66,7 @@ struct WorkspacePlan {
   size_t sched_bytes;
   size_t total;
   // int32 table offsets (in elements from the workspace start), packed only
-  size_t seq_tok0, seq_chunk0, chunk_t0, chunk_len;
+  size_t seq_tok0, seq_chunk0, chunk_t0, chunk_len, seq_order;
 };
 
 inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
@@ -81,7 +81,8 @@ inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
     P.seq_chunk0 = P.seq_tok0 + (size_t)N + 1;
     P.chunk_t0 = P.seq_chunk0 + (size_t)N + 1;
     P.chunk_len = P.chunk_t0 + (size_t)P.max_chunks;
-    size_t n_int = P.chunk_len + (size_t)P.max_chunks;
+    P.seq_order = P.chunk_len + (size_t)P.max_chunks;
+    size_t n_int = P.seq_order + (size_t)N;
     P.tables_bytes = (n_int * sizeof(int32_t) + 255) / 256 * 256;
   } else {
     P.n_seq = B;

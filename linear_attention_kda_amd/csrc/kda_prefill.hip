@@ -50,7 +50,7 @@ namespace {
 __global__ __launch_bounds__(1024) void varlen_index_kernel(
     const int32_t *__restrict__ cu, int N, int T, int32_t *seq_tok0,
     int32_t *seq_chunk0, int32_t *chunk_t0, int32_t *chunk_len,
-    long long max_chunks) {
+    long long max_chunks, int32_t *seq_order) {
   __shared__ int32_t s[1024];
   const int tid = threadIdx.x;
   int tok_carry = 0;    // offset of the entry before this tile
@@ -104,6 +104,25 @@ __global__ __launch_bounds__(1024) void varlen_index_kernel(
     __syncthreads();
   }
   if (tid == 0) seq_chunk0[N] = chunk_carry;
+
+  // Scan order, longest sequence first: the scan's sequential chain of a
+  // sequence is as long as its chunk count, and the longest chains should
+  // not start last.  seq_order[r] is the sequence of rank r (more chunks
+  // first, ties by index), from a rank count over all pairs in LDS; with
+  // more than 1024 sequences the order stays the identity.
+  __syncthreads();  // seq_chunk0 complete (written by this workgroup)
+  if (N <= 1024) {
+    const int cnt = tid < N ? seq_chunk0[tid + 1] - seq_chunk0[tid] : -1;
+    s[tid] = cnt;
+    __syncthreads();
+    if (tid < N) {
+      int r = 0;
+      for (int j = 0; j < N; ++j) r += s[j] > cnt || (s[j] == cnt && j < tid);
+      seq_order[r] = tid;
+    }
+  } else {
+    for (int i = tid; i < N; i += 1024) seq_order[i] = i;
+  }
 }
 
 struct ChunkSource {
@@ -881,6 +900,7 @@ struct ScanKArgs {
   ChunkRecordLayout lay;
   int H, dv, T, nct;
   const int32_t *seq_tok0, *seq_chunk0;  // packed batch tables, or null
+  const int32_t *seq_order;              // packed: sequences longest first (unit u -> sequence seq_order[u / H])
   float scale;
   int n_units;                           // sequences * heads
   int wg_per_unit;                       // workgroups per unit (value tiles / waves per WG)
@@ -1217,7 +1237,7 @@ void chunk_scan_kernel(ScanKArgs a) {
     grp = slot % a.wg_per_unit;
   }
   if (u >= a.n_units) return;
-  const int n = u / a.H, h = u % a.H;
+  const int n = a.seq_order ? a.seq_order[u / a.H] : u / a.H, h = u % a.H;
   const int vwg = grp * (CW * VC);  // first value column of the workgroup
   const int H = a.H, DV = a.dv;
   const bool copier = w >= CW;
@@ -1602,7 +1622,7 @@ hipError_t run_prefill_overlap(const PrefillArgs &a, hipStream_t stream, PrepKAr
     sa.dv = a.dv;
     sa.T = a.T;
     sa.nct = nct;
-    sa.seq_tok0 = sa.seq_chunk0 = nullptr;
+    sa.seq_tok0 = sa.seq_chunk0 = sa.seq_order = nullptr;
     sa.scale = a.scale;
     sa.n_units = n_units;
     sa.wg_per_unit = a.dv / 32;  // two compute waves of 16 columns per workgroup
@@ -1644,7 +1664,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
   if (packed) {
     hipLaunchKernelGGL(varlen_index_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, P.n_seq, a.T,
                        tables + P.seq_tok0, tables + P.seq_chunk0, tables + P.chunk_t0, tables + P.chunk_len,
-                       P.max_chunks);
+                       P.max_chunks, tables + P.seq_order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1696,6 +1716,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     sa.nct = nct;
     sa.seq_tok0 = packed ? tables + P.seq_tok0 : nullptr;
     sa.seq_chunk0 = packed ? tables + P.seq_chunk0 : nullptr;
+    sa.seq_order = packed ? tables + P.seq_order : nullptr;
     sa.scale = a.scale;
     sa.n_units = P.n_seq * a.H;
     // compute waves per workgroup (CW) and 16-column tiles per wave (NT).
