@@ -1549,12 +1549,15 @@ OverlapCtx g_overlap[64];
 constexpr int kScanCUs = 128;
 
 // The current device's streams, or null if the schedule cannot run there
-// (caller holds g_overlap_mu).
-OverlapCtx *overlap_ctx() {
+// (caller holds g_overlap_mu).  They are not created while `stream` is being
+// captured into a graph (that call runs two-phase; a later one creates them).
+OverlapCtx *overlap_ctx(hipStream_t stream) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   OverlapCtx &c = g_overlap[dev];
   if (!c.tried) {
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
     c.tried = true;
     int ncu = 0;
     hipDeviceProp_t prop;
@@ -1691,7 +1694,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.ready_words = pa.n_units = 0;
     if (overlap_supported<DK, E>(a) && overlap_chosen(a, nct)) {
       std::lock_guard<std::mutex> lock(g_overlap_mu);
-      if (OverlapCtx *ov = overlap_ctx()) return run_prefill_overlap<DK, E>(a, stream, pa, lay, records, *ov);
+      if (OverlapCtx *ov = overlap_ctx(stream)) return run_prefill_overlap<DK, E>(a, stream, pa, lay, records, *ov);
     }
     const dim3 pg((unsigned)P.max_chunks, a.H);
     if (a.act & kActQK)

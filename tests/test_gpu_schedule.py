@@ -105,3 +105,47 @@ def test_overlap_repeated_calls_share_workspace():
         assert _error_word(ws, B, T, H) == 0
         o2, S2 = _run(inp, "two_phase")
         assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_overlap_in_graph_capture():
+    """The overlapped call captured into a HIP graph (its fork and join are
+    event nodes, its clear is a kernel): replays with new inputs copied in,
+    with eager work and synchronisation between them, match the eager
+    two-phase results bitwise."""
+    import linear_attention_kda_amd as kda
+    announce("schedule overlap captured in a graph: 3 replays vs eager two-phase, B=2 T=640 H=8")
+    B, T, H = 2, 640, 8
+    ws = _workspace(B, T, H)
+    static = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=0.02, seed=40))
+    o = torch.empty_like(static["v"])
+    S = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda")
+    prev = kda.set_schedule("overlap")
+    try:
+        def call():
+            kda.chunk_fwd(static["q"], static["k"], static["v"], static["alpha"], static["beta"], S0=static["S0"],
+                          out=o, S_final=S, workspace=ws)
+        call()  # eager once: creates the internal streams outside the capture
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        torch.cuda.synchronize()
+        for seed in (41, 42, 43):
+            new = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=0.02, seed=seed))
+            for name in ("q", "k", "v", "alpha", "beta", "S0"):
+                static[name].copy_(new[name])
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            o_g, S_g = o.clone(), S.clone()
+            assert _error_word(ws, B, T, H) == 0
+            o_e, S_e = _run(new, "two_phase")
+            assert torch.equal(o_g, o_e) and torch.equal(S_g, S_e)
+    finally:
+        kda.set_schedule(prev)
