@@ -35,9 +35,9 @@ NSETS = 4
 # Each figure belongs to the kernel source with the given sha256 prefix and is
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
-    "prefill": ("kda_prefill.hip", "53a0291cb62e9922", 464_175_104),
-    "decode": ("kda_decode.hip", "fab9d9aec69d4611", 1_086_896_640),
-    "decode_tokens": ("kda_decode.hip", "fab9d9aec69d4611", 1_125_209_088),
+    "prefill": ("kda_prefill.hip", "30e58532e63a2213", 464_084_275),
+    "decode": ("kda_decode.hip", "7a2611a8684364e9", 1_086_884_966),
+    "decode_tokens": ("kda_decode.hip", "7a2611a8684364e9", 1_125_189_632),
 }
 
 
