@@ -1722,35 +1722,17 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     sa.seq_order = packed ? tables + P.seq_order : nullptr;
     sa.scale = a.scale;
     sa.n_units = P.n_seq * a.H;
-    // compute waves per workgroup (CW) and 16-column tiles per wave (NT).
-    // Two tiles per wave halve the LDS reads per column but double each
-    // wave's serial chain of products; one tile and two compute waves per
-    // workgroup measured fastest at d_v = 128.
-    int nt = 1, cw = a.dv >= 32 ? 2 : 1, ncp = 3;
-    if (const char *env = std::getenv("KDA_SCAN_NT")) {
-      const int x = std::atoi(env);
-      if ((x == 1 || x == 2) && 16 * x <= a.dv) nt = x;
-    }
-    if (const char *env = std::getenv("KDA_SCAN_CW")) {
-      const int x = std::atoi(env);
-      if (x == 1 || x == 2) cw = x;
-    }
-    if (const char *env = std::getenv("KDA_SCAN_CP")) {
-      const int x = std::atoi(env);
-      if (x == 1 || x == 3) ncp = x;
-    }
-    while (cw > 1 && (16 * nt * cw > a.dv || !scan_stage_fits<DK, E>(nt, cw))) cw /= 2;
-    sa.wg_per_unit = a.dv / (16 * nt * cw);
+    // Two compute waves of one 16-column tile each per workgroup (one wave
+    // when d_v = 16 or two stages would not fit in LDS) and three copy
+    // waves: measured fastest at d_v = 128 against two tiles per wave
+    // (which halves the LDS reads per column but doubles each wave's serial
+    // chain of products) and against one copy wave.
+    int cw = a.dv >= 32 ? 2 : 1;
+    while (cw > 1 && !scan_stage_fits<DK, E>(1, cw)) cw /= 2;
+    sa.wg_per_unit = a.dv / (16 * cw);
     const long long slots = ((long long)sa.n_units + 7) / 8 * 8 * sa.wg_per_unit;
     const dim3 grid((unsigned)slots);
-    if (nt == 2 && ncp == 3)
-      launch_scan<DK, E, 2, 3>(cw, grid, stream, sa);
-    else if (nt == 2)
-      launch_scan<DK, E, 2, 1>(cw, grid, stream, sa);
-    else if (ncp == 3)
-      launch_scan<DK, E, 1, 3>(cw, grid, stream, sa);
-    else
-      launch_scan<DK, E, 1, 1>(cw, grid, stream, sa);
+    launch_scan<DK, E, 1, 3>(cw, grid, stream, sa);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
