@@ -167,6 +167,50 @@ def bench_long_context(args, torch, kda, inputs, steps=10, warmup=2):
                          "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
 
 
+def bench_varlen(args, torch, kda, inputs, steps=20, warmup=3):
+    """The packed-batch workload: 64 sequences of lognormal lengths in one
+    buffer with int32 offsets, 16 heads, per-sequence S0, the slow-gate and
+    beta = 1 head groups."""
+    w = inputs.WORKLOADS["varlen"]
+    H, dk, dv = w["H"], w["dk"], w["dv"]
+    dev = torch.device("cuda:0")
+    inp = inputs.workload("varlen", seed=0, device=dev)
+    T = int(inp["cu_seqlens"][-1])
+    N = int(inp["lengths"].numel())
+    o = torch.empty_like(inp["v"])
+    S = torch.empty((N, H, dv, dk), dtype=torch.float32, device=dev)
+    ws = torch.empty(kda.chunk_fwd_workspace_size(1, T, H, dk, dv, N, kda.KDA_BF16), dtype=torch.uint8,
+                     device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call():
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"],
+                      cu_seqlens=inp["cu_seqlens"], out=o, S_final=S, workspace=ws)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    lens = inp["lengths"]
+    # per token: q, k, v, o bf16, alpha fp32 per channel, beta fp32; S0 and
+    # S_final once per sequence
+    nbytes = T * H * ((2 * dk + 2 * dv) * 2 + dk * 4 + 4) + 2 * N * H * dv * dk * 4
+    ach = nbytes / (us * 1e-6) / 1e9
+    return {"workload": f"packed batch of {N} sequences (lengths {int(lens.min())}..{int(lens.max())}, "
+                        f"total {T} tokens) H={H} d_k=d_v={dk} bf16, S0 given",
+            "calls": steps, "call_us_mean": round(us, 1), "tokens": T,
+            "chunks": int(((lens + 63) // 64).sum()) * H,
+            "tokens_per_s": round(T / (us * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
+
+
 def decode_tokens_bytes(N, H, dk, dv, Tk, esize=2):
     """One multi-token launch: the state is read and written once, each of the
     Tk tokens brings its q, k, v, alpha, beta and writes its output row."""
@@ -290,6 +334,18 @@ def cpu_baseline(inputs, torch):
             "single_thread_value": round(tokens / dt1, 1)}
 
 
+def copy_calib(args, torch):
+    """One plain device copy of --copy-calib-mib MiB, whose counter readings
+    calibrate FETCH_SIZE and WRITE_SIZE."""
+    n = args.copy_calib_mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    return n
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -304,6 +360,10 @@ def main():
                     help="also time the long-context workload (B=1 H=32 T=65536) under both schedules")
     ap.add_argument("--long-only", action="store_true",
                     help="time only the long-context workload (for profiling); prints its object")
+    ap.add_argument("--varlen", action="store_true",
+                    help="also time the packed-batch workload (64 sequences, H=16)")
+    ap.add_argument("--varlen-only", action="store_true",
+                    help="time only the packed-batch workload (for profiling); prints its object")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -318,6 +378,12 @@ def main():
 
     if args.long_only:
         print(json.dumps({"long_context": bench_long_context(args, torch, kda, inputs)}), flush=True)
+        return
+    if args.varlen_only:
+        out = {"varlen": bench_varlen(args, torch, kda, inputs)}
+        if args.copy_calib_mib:
+            out["copy_calib_bytes"] = copy_calib(args, torch)
+        print(json.dumps(out), flush=True)
         return
     pf = bench_prefill(args, torch, kda, inputs)
     nbytes = prefill_bytes(pf["B"], pf["T"], pf["H"], pf["dk"], pf["dv"])
@@ -374,14 +440,10 @@ def main():
                              "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": sb}}
     if args.long_context:
         result["long_context"] = bench_long_context(args, torch, kda, inputs)
+    if args.varlen:
+        result["varlen"] = bench_varlen(args, torch, kda, inputs)
     if args.copy_calib_mib:
-        n = args.copy_calib_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        result["copy_calib_bytes"] = n
+        result["copy_calib_bytes"] = copy_calib(args, torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inputs, torch)
     print(json.dumps(result), flush=True)
