@@ -89,3 +89,33 @@ def test_decode_full_size_steps():
                                      sel(tok["beta"]), S_ref)
         check(f"o step {step}", o[nsel.cuda(), hsel.cuda()][:, None], o_ref, TOL[torch.bfloat16])
     check("S after 4 steps", S[nsel.cuda(), hsel.cuda()][:, None], S_ref, TOL[torch.bfloat16])
+
+
+def test_decode_tokens_full_size():
+    """The multi-token decode in the configuration the benchmark times: 256 x
+    32 heads, 512 MiB state updated in place, Tk = 4 tokens per launch, two
+    launches; the oracle follows 96 sampled (sequence, head) states."""
+    import linear_attention_kda_amd as kda
+    import oracle
+    announce("decode_tokens N256 H32 d128 bf16 Tk=4, 2 launches in place (oracle on 96 units)")
+    w = inputs.WORKLOADS["decode"]
+    N, H, dk, dv, Tk = w["N"], w["H"], w["dk"], w["dv"], 4
+    S = inputs.decode_state(N, H, dk, dv, w["s0_std"], seed=0, device="cuda")
+    g = torch.Generator().manual_seed(6)
+    units = torch.randperm(N * H, generator=g)[:96]
+    nsel, hsel = units.cuda() // H, units.cuda() % H
+    S_ref = S[nsel, hsel].double().cpu().numpy()[:, None]
+    for b in range(2):
+        toks = [inputs.decode_token(N, H, dk, dv, w["dtype"], w["alpha_lo"], step=b * Tk + t, device="cuda")
+                for t in range(Tk)]
+        blk = {key: torch.stack([t[key] for t in toks], 1).contiguous() for key in toks[0]}
+        o, S2 = kda.decode_tokens(blk["q"], blk["k"], blk["v"], blk["alpha"], blk["beta"], S, S_out=S)
+        torch.cuda.synchronize()
+        assert S2.data_ptr() == S.data_ptr()
+        for t in range(Tk):
+            sel = lambda x: x[nsel, hsel].cpu()[:, None]
+            o_ref, S_ref = oracle.decode(sel(toks[t]["q"]), sel(toks[t]["k"]), sel(toks[t]["v"]),
+                                         sel(toks[t]["alpha"]), sel(toks[t]["beta"]), S_ref)
+            check(f"o launch {b} token {t}", o[nsel, :, hsel][:, t][:, None], o_ref, TOL[torch.bfloat16])
+    check("S after 2 launches", S[nsel, hsel][:, None], S_ref, TOL[torch.bfloat16])
+    assert torch.isfinite(o).all()
