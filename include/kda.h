@@ -148,7 +148,8 @@ int kda_set_validation(int enable);
  *   KDA_SCHEDULE_TWO_PHASE: the preparation of every chunk, then the scan,
  *     on `stream`.
  *   KDA_SCHEDULE_OVERLAP: both at once on two internal streams confined to
- *     disjoint halves of the compute units, the scan copying each chunk's
+ *     disjoint sets of compute units (128 for the scan, 112 for the
+ *     preparation), the scan copying each chunk's
  *     record as soon as its preparation is published (ready bits in the
  *     workspace; producer and consumer of a record run on the same XCD, so
  *     the record is read from that XCD's L2).  The call forks from and joins

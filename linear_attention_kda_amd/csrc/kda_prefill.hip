@@ -1537,7 +1537,11 @@ void launch_scan(int cw, dim3 grid, hipStream_t stream, const ScanKArgs &sa) {
 // ================================================================ dispatch
 // CU-masked streams of the overlapped schedule, one set per device: the scan
 // on the first 128 CUs of the runtime's mask numbering (16 on each XCD) and
-// the prep on the other 128, so neither can hold the CUs the other needs.
+// the prep on the next 112 (14 on each XCD), so neither can hold the CUs the
+// other needs.  The last 16 CUs stay idle: on a 1024-chunk chain the prep,
+// which finishes well before the scan, slowed the scan less on 112 CUs (a
+// call of 1833-1839 us) than on 128 (1985 us) or 96 (1852 us); on 80 it
+// became the bound (2441 us).
 // Created on first use and kept for the life of the process.
 struct OverlapCtx {
   bool tried = false, ok = false;
@@ -1546,7 +1550,7 @@ struct OverlapCtx {
 };
 std::mutex g_overlap_mu;  // guards g_overlap and the event sequence of a launch
 OverlapCtx g_overlap[64];
-constexpr int kScanCUs = 128;
+constexpr int kScanCUs = 128, kPrepCUs = 112;
 // copy waves of the overlapped scan: four measured 4 % faster than three on
 // a 1024-chunk chain
 constexpr int kOverlapCopyWaves = 4;
@@ -1569,7 +1573,7 @@ OverlapCtx *overlap_ctx(hipStream_t stream) {
     // eight XCDs of 32 CUs (the whole MI355X as one device)
     if (ncu != 256 || std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return nullptr;
     uint32_t ms[8] = {0}, mp[8] = {0};
-    for (int i = 0; i < ncu; ++i) (i < kScanCUs ? ms : mp)[i / 32] |= 1u << (i % 32);
+    for (int i = 0; i < kScanCUs + kPrepCUs; ++i) (i < kScanCUs ? ms : mp)[i / 32] |= 1u << (i % 32);
     if (hipExtStreamCreateWithCUMask(&c.scan, 8, ms) != hipSuccess) return nullptr;
     if (hipExtStreamCreateWithCUMask(&c.prep, 8, mp) != hipSuccess) return nullptr;
     if (hipEventCreateWithFlags(&c.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
