@@ -163,10 +163,11 @@ int kda_set_validation(int enable);
  *     a second (another process holding its compute units), the scan stops
  *     waiting and its results are wrong; the schedule's error word in the
  *     workspace records that.
- *   KDA_SCHEDULE_AUTO (default): overlap when supported and the scan's
- *     workgroups (B * H * d_v / 32) fit on half of the chip, with at least 8
- *     chunks per sequence (long sequences over few heads, where the two-phase
- *     scan leaves half of the chip idle); else two-phase.
+ *   KDA_SCHEDULE_AUTO (default): overlap when supported, the scan's
+ *     workgroups (B * H * d_v / 32) fit on 128 compute units, and the batch
+ *     holds at least 4096 chunks over all sequences and heads
+ *     (B * H * ceil(T / 64); long sequences over few heads, whose records
+ *     overflow the Infinity Cache); else two-phase.
  * The initial value is taken from the environment variable KDA_SCHEDULE
  * (0, 1 or 2) at load time.  Process-wide; returns the previous setting, or
  * -1 (nothing changed) for an unknown value.

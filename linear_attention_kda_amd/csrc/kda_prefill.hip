@@ -1590,13 +1590,20 @@ template <int DK, typename E> bool overlap_supported(const PrefillArgs &a) {
   return DK == 128 && a.dv == 128 && sizeof(E) == 2 && !a.cu_seqlens && a.plan.sched_bytes > 0;
 }
 
-// Automatic choice: the overlap pays when the scan's workgroups (four per
-// unit at d_v = 128) fit on half of the chip, which the two-phase scan would
-// leave idle, and the chain is long enough to amortise the fork and join.
+// Automatic choice: the overlap needs the scan's workgroups (four per unit at
+// d_v = 128) to fit on its 128 CUs, and it pays once the batch holds at least
+// 4096 chunk records (256 MB at d = 128, the size of the Infinity Cache):
+// the two-phase scan then fetches its records from HBM while the overlapped
+// one reads them soon after they are written, and the fork and join (about
+// 50 us) are amortised.  Measured (two-phase / overlap, us): 8 units x 256
+// chunks 300 / 380, 8 x 512 800 / 759, 16 x 192 293 / 336, 16 x 256 477 /
+// 419, 32 x 128 310 / 315, 32 x 192 473 / 416, 32 x 1024 2430 / 1800.
+constexpr long long kOverlapMinRecords = 4096;
 bool overlap_chosen(const PrefillArgs &a, int nct) {
   if (a.schedule == kScheduleTwoPhase) return false;
   if (a.schedule == kScheduleOverlap) return true;
-  return (long long)a.B * a.H * (a.dv / 32) <= kScanCUs && nct >= 8;
+  const long long units = (long long)a.B * a.H;
+  return units * (a.dv / 32) <= kScanCUs && units * nct >= kOverlapMinRecords;
 }
 
 // Overlapped schedule: clear the ready words on the caller's stream, then
