@@ -35,7 +35,7 @@ NSETS = 4
 # Each figure belongs to the kernel source with the given sha256 prefix and is
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
-    "prefill": ("kda_prefill.hip", "b99355fe448b16d5", 464_307_126),
+    "prefill": ("kda_prefill.hip", "69fe437b5e7ed77c", 464_490_841),
     "decode": ("kda_decode.hip", "7a2611a8684364e9", 1_086_884_966),
     "decode_tokens": ("kda_decode.hip", "7a2611a8684364e9", 1_125_189_632),
 }
