@@ -62,12 +62,13 @@ __device__ __forceinline__ void load4<float>(const float *p, float *out) {
 }
 
 // Work split: a unit's state is NACC wave-wide KiB accesses.  A workgroup of
-// four waves takes APW = min(NACC, 8) of them (two per wave), so a d = 128
-// unit spreads over 8 workgroups; fewer accesses in flight per wave and more
-// workgroups measured closer to the copy bandwidth of the part.
-template <int DK, int DV> struct DecodeShape {
+// four waves takes APW = min(NACC, MAXAPW) of them.  With one token per launch
+// MAXAPW = 8 (two per wave), so a d = 128 unit spreads over 8 workgroups;
+// fewer accesses in flight per wave and more workgroups measured closer to the
+// copy bandwidth of the part.
+template <int DK, int DV, int MAXAPW = 8> struct DecodeShape {
   static constexpr int NACC = DV * DK / 256;
-  static constexpr int APW = NACC < 8 ? NACC : 8;
+  static constexpr int APW = NACC < MAXAPW ? NACC : MAXAPW;
   static constexpr int SPLIT = NACC / APW;        // workgroups per unit
   static constexpr int NI = (APW + 3) / 4;        // accesses per wave
 };
@@ -89,9 +90,19 @@ __device__ __forceinline__ void consume(const TokIn<NI> &x) {
   asm volatile("" ::"v"(x.beta));
 }
 
+// Several tokens per launch are bound by vector issue, not by the state
+// traffic: each token's own work per lane (its loads and conversions, the k.q
+// sum, the decayed gates) is shared by the lane's rows, so the multi-token
+// kernel gives each workgroup 32 KiB of state (eight rows per lane, two
+// workgroups per d = 128 unit).  Four-token launches on 256 x 32 units took
+// 265 us with 8 KiB per workgroup, 229 with 16, 221-227 with 32 and 272 with
+// 64 (occupancy two waves per SIMD).
+constexpr int kMultiAPW = 32;
+template <int DK, int DV, int G> using DecodeShapeG = DecodeShape<DK, DV, G == 1 ? 8 : kMultiAPW>;
+
 template <int DK, int DV, typename E, int GATE, int G>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
-  typedef DecodeShape<DK, DV> SH;
+  typedef DecodeShapeG<DK, DV, G> SH;
   constexpr int LPR = DK / 4;                 // lanes per state row
   constexpr int RPA = 64 / LPR;               // rows per wave-wide KiB access
   constexpr int NI = SH::NI;                  // accesses per wave
@@ -237,21 +248,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 }
 
 // tokens whose inputs are requested together: two measured faster than four
-// (72 VGPRs and seven waves per SIMD instead of 106 and four; 261 against
-// 283 us per four-token launch on the decode workload)
+// (with eight rows per lane: 125 VGPRs and four waves per SIMD against 171
+// and two; 221-227 against 263 us per four-token launch on the decode
+// workload)
 constexpr int kTokGroup = 2;
 
 template <int DK, typename E, int GATE>
 hipError_t run_decode_dv(const DecodeArgs &a, const DecodeKArgs &ka, hipStream_t s) {
   const size_t units = (size_t)a.N * a.H;
   if ((units + 7) / 8 * 8 * DecodeShape<DK, 128>::SPLIT > 0x7fffffffull) return hipErrorInvalidConfiguration;
-#define KDA_DECODE_LAUNCH(DV)                                                                         \
-  {                                                                                                   \
-    const dim3 grid((unsigned)((units + 7) / 8 * 8 * DecodeShape<DK, DV>::SPLIT));                    \
-    if (a.Tk == 1)                                                                                    \
-      hipLaunchKernelGGL((decode_kernel<DK, DV, E, GATE, 1>), grid, dim3(kThreads), 0, s, ka);         \
-    else                                                                                              \
-      hipLaunchKernelGGL((decode_kernel<DK, DV, E, GATE, kTokGroup>), grid, dim3(kThreads), 0, s, ka); \
+#define KDA_DECODE_LAUNCH(DV)                                                                          \
+  {                                                                                                    \
+    if (a.Tk == 1) {                                                                                   \
+      const dim3 grid((unsigned)((units + 7) / 8 * 8 * DecodeShapeG<DK, DV, 1>::SPLIT));               \
+      hipLaunchKernelGGL((decode_kernel<DK, DV, E, GATE, 1>), grid, dim3(kThreads), 0, s, ka);          \
+    } else {                                                                                           \
+      const dim3 grid((unsigned)((units + 7) / 8 * 8 * DecodeShapeG<DK, DV, kTokGroup>::SPLIT));       \
+      hipLaunchKernelGGL((decode_kernel<DK, DV, E, GATE, kTokGroup>), grid, dim3(kThreads), 0, s, ka);  \
+    }                                                                                                  \
   }
   switch (a.dv) {
     case 16: KDA_DECODE_LAUNCH(16); break;
