@@ -36,8 +36,8 @@ NSETS = 4
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
     "prefill": ("kda_prefill.hip", "69fe437b5e7ed77c", 464_490_841),
-    "decode": ("kda_decode.hip", "7a2611a8684364e9", 1_086_884_966),
-    "decode_tokens": ("kda_decode.hip", "7a2611a8684364e9", 1_125_189_632),
+    "decode": ("kda_decode.hip", "278dd0ca3f70dd05", 1_086_895_866),
+    "decode_tokens": ("kda_decode.hip", "278dd0ca3f70dd05", 1_125_438_808),
 }
 
 
