@@ -1628,7 +1628,7 @@ hipError_t run_prefill_overlap(const PrefillArgs &a, hipStream_t stream, PrepKAr
   if ((e = hipStreamWaitEvent(ov.prep, ov.fork, 0)) != hipSuccess) return e;
 
   if constexpr (DK == 128 && sizeof(E) == 2) {
-    ScanKArgs sa;
+    ScanKArgs sa{};
     sa.v = a.v;
     sa.S0 = a.S0;
     sa.o = a.o;
@@ -1688,7 +1688,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
   }
 
   if (P.max_chunks > 0) {
-    PrepKArgs pa;
+    PrepKArgs pa{};
     pa.q = a.q;
     pa.k = a.k;
     pa.alpha = a.alpha;
@@ -1721,7 +1721,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
   }
 
   if (P.n_seq > 0) {
-    ScanKArgs sa;
+    ScanKArgs sa{};
     sa.v = a.v;
     sa.S0 = a.S0;
     sa.o = a.o;
