@@ -35,7 +35,7 @@ NSETS = 4
 # Each figure belongs to the kernel source with the given sha256 prefix and is
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
-    "prefill": ("kda_prefill.hip", "69fe437b5e7ed77c", 464_490_841),
+    "prefill": ("kda_prefill.hip", "20c75a744eded799", 464_174_125),
     "decode": ("kda_decode.hip", "278dd0ca3f70dd05", 1_086_895_866),
     "decode_tokens": ("kda_decode.hip", "278dd0ca3f70dd05", 1_125_438_808),
 }
