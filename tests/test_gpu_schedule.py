@@ -48,7 +48,7 @@ def _error_word(ws, B, T, H):
     (1, 65, 2, 0.02),        # a ragged second chunk
     (2, 700, 3, 0.02),       # units not a multiple of eight
     (4, 2048, 16, None),     # the prefill workload's shape, 64 units
-    (3, 1000, 32, 0.02),     # 96 units: more than the 64 scan CUs, so units take turns
+    (3, 1000, 32, 0.02),     # 96 units: 384 scan workgroups on 128 CUs, so units take turns
 ])
 def test_overlap_equals_two_phase(B, T, H, s0):
     announce(f"schedule overlap vs two-phase, dense bf16 d=128 B={B} T={T} H={H} S0={s0}")
@@ -149,3 +149,24 @@ def test_overlap_in_graph_capture():
             assert torch.equal(o_g, o_e) and torch.equal(S_g, S_e)
     finally:
         kda.set_schedule(prev)
+
+
+@pytest.mark.parametrize("T,overlap", [(8192, True), (8128, False)])
+def test_auto_schedule_threshold(T, overlap):
+    """The automatic schedule overlaps from 4096 chunk records (B * H *
+    ceil(T / 64)): 32 heads x 128 chunks do, 32 x 127 do not.  Only the
+    overlapped schedule touches the prep's per-XCD task counters, so in a
+    workspace that starts zeroed they show which schedule ran; the results
+    equal the two-phase schedule's bit for bit either way."""
+    B, H = 1, 32
+    announce(f"schedule auto at the overlap threshold, B={B} T={T} H={H} (overlap expected: {overlap})")
+    inp = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, seed=23))
+    ws = _workspace(B, T, H)
+    o1, S1 = _run(inp, "auto", ws=ws)
+    nrec = B * ((T + 63) // 64) * H
+    off = nrec * REC_BYTES + nrec * 4            # the control words follow the ready words
+    prep_tickets = ws[off:off + 32].cpu().numpy().view(np.int32)
+    assert (int(prep_tickets.sum()) > 0) == overlap
+    assert _error_word(ws, B, T, H) == 0
+    o2, S2 = _run(inp, "two_phase")
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
