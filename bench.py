@@ -9,8 +9,10 @@ from HBM rather than from a cache warmed by the previous call.
 
 Printed: ONE JSON line with the headline prefill rate, the roofline of the
 prefill call (compulsory HBM bytes / measured call time against 8 TB/s), the
-decode workload (256 sequences x 32 heads, 512 MiB fp32 state, 1024 steps)
-with its own roofline, and the fp64 CPU oracle timed on this host.
+decode workload (256 sequences x 32 heads, 512 MiB fp32 state, 1024 steps),
+the long-context workload (B=1 H=32 T=65536) and the packed-batch workload
+(64 sequences, H=16), each with its own roofline, and the fp64 CPU oracle
+timed on this host.
 """
 from __future__ import annotations
 
@@ -38,12 +40,16 @@ MEASURED_TRAFFIC = {
     "prefill": ("kda_prefill.hip", "20c75a744eded799", 464_174_125),
     "decode": ("kda_decode.hip", "278dd0ca3f70dd05", 1_086_895_866),
     "decode_tokens": ("kda_decode.hip", "278dd0ca3f70dd05", 1_125_438_808),
+    "long_context": ("kda_prefill.hip", "0", None),
+    "varlen": ("kda_prefill.hip", "0", None),
 }
 
 
 def measured_traffic(key):
     import hashlib
     fname, sha, nbytes = MEASURED_TRAFFIC[key]
+    if nbytes is None:
+        return None
     path = os.path.join(ROOT, "linear_attention_kda_amd", "csrc", fname)
     with open(path, "rb") as f:
         cur = hashlib.sha256(f.read()).hexdigest()
@@ -66,6 +72,13 @@ def prefill_flops(B, T, H, dk, dv, C=64):
     """Algorithmic flops of the chunked form per head-token, as executed:
     6 dk dv + 2C(3dk + 2dv) + C^2/3."""
     return B * T * H * (6 * dk * dv + 2 * C * (3 * dk + 2 * dv) + C * C / 3)
+
+
+def packed_bytes(T, N, H, dk, dv, esize=2):
+    """Compulsory bytes of one packed-batch call of T tokens in N sequences:
+    per head-token q, k, v, o at their dtype, alpha fp32 per key channel and
+    beta fp32; S0 and S_final fp32 once per (sequence, head)."""
+    return T * H * ((2 * dk + 2 * dv) * esize + dk * 4 + 4) + 2 * N * H * dv * dk * 4
 
 
 def decode_bytes(N, H, dk, dv, esize=2):
@@ -141,7 +154,7 @@ def bench_long_context(args, torch, kda, inputs, steps=10, warmup=2):
     ws = torch.empty(kda.chunk_fwd_workspace_size(B, T, H, dk, dv, -1, kda.KDA_BF16), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream(dev)
-    out = {}
+    out, status = {}, {}
     for sched in ("auto", "two_phase"):
         prev = kda.set_schedule(sched)
         for _ in range(warmup):
@@ -157,14 +170,20 @@ def bench_long_context(args, torch, kda, inputs, steps=10, warmup=2):
         torch.cuda.synchronize()
         kda.set_schedule(prev)
         out[sched] = e0.elapsed_time(e1) * 1e3 / steps
+        # which schedule the timed calls ran, and that none reported an error
+        status[sched] = kda.chunk_fwd_status(ws)
+        if status[sched][1]:
+            raise RuntimeError(f"long-context {sched}: schedule error bits {status[sched][1]:#x}")
     nbytes = prefill_bytes(B, T, H, dk, dv, s0=True)
     ach = nbytes / (out["auto"] * 1e-6) / 1e9
     return {"workload": f"long-context prefill B={B} H={H} T={T} d_k=d_v={dk} bf16, S0 given",
             "calls": steps, "call_us_mean": round(out["auto"], 1),
+            "schedule": status["auto"][0],
             "call_us_two_phase": round(out["two_phase"], 1),
             "tokens_per_s": round(B * T / (out["auto"] * 1e-6), 1),
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic("long_context"),
+                         "algorithmic_bytes": nbytes}}
 
 
 def bench_varlen(args, torch, kda, inputs, steps=20, warmup=3):
@@ -198,9 +217,7 @@ def bench_varlen(args, torch, kda, inputs, steps=20, warmup=3):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     lens = inp["lengths"]
-    # per token: q, k, v, o bf16, alpha fp32 per channel, beta fp32; S0 and
-    # S_final once per sequence
-    nbytes = T * H * ((2 * dk + 2 * dv) * 2 + dk * 4 + 4) + 2 * N * H * dv * dk * 4
+    nbytes = packed_bytes(T, N, H, dk, dv)
     ach = nbytes / (us * 1e-6) / 1e9
     return {"workload": f"packed batch of {N} sequences (lengths {int(lens.min())}..{int(lens.max())}, "
                         f"total {T} tokens) H={H} d_k=d_v={dk} bf16, S0 given",
@@ -208,7 +225,8 @@ def bench_varlen(args, torch, kda, inputs, steps=20, warmup=3):
             "chunks": int(((lens + 63) // 64).sum()) * H,
             "tokens_per_s": round(T / (us * 1e-6), 1),
             "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": nbytes}}
+                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic("varlen"),
+                         "algorithmic_bytes": nbytes}}
 
 
 def decode_tokens_bytes(N, H, dk, dv, Tk, esize=2):
@@ -356,12 +374,12 @@ def main():
     ap.add_argument("--no-gate-forms", action="store_true",
                     help="skip the scalar-gate prefill line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--long-context", action="store_true",
-                    help="also time the long-context workload (B=1 H=32 T=65536) under both schedules")
+    ap.add_argument("--no-long-context", action="store_true",
+                    help="skip the long-context workload (B=1 H=32 T=65536, timed under both schedules)")
     ap.add_argument("--long-only", action="store_true",
                     help="time only the long-context workload (for profiling); prints its object")
-    ap.add_argument("--varlen", action="store_true",
-                    help="also time the packed-batch workload (64 sequences, H=16)")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed-batch workload (64 sequences, H=16)")
     ap.add_argument("--varlen-only", action="store_true",
                     help="time only the packed-batch workload (for profiling); prints its object")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
@@ -438,9 +456,9 @@ def main():
                 "call_us_mean": round(sg["call_ms_mean"] * 1e3, 2),
                 "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": sb}}
-    if args.long_context:
+    if not args.no_long_context:
         result["long_context"] = bench_long_context(args, torch, kda, inputs)
-    if args.varlen:
+    if not args.no_varlen:
         result["varlen"] = bench_varlen(args, torch, kda, inputs)
     if args.copy_calib_mib:
         result["copy_calib_bytes"] = copy_calib(args, torch)

@@ -20,7 +20,11 @@
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are DEVICE pointers, owned by the caller.  The
- *    library allocates nothing and keeps no pointer after a call returns.
+ *    library allocates no device memory and keeps no pointer to caller
+ *    memory after a call returns.  The one thing it keeps is per device:
+ *    the first call that takes the overlapped prefill schedule (see
+ *    kda_set_schedule) creates two internal streams and three events there,
+ *    which stay until kda_release() (registered to run at process exit).
  *  - Layouts are dense row-major with the last dimension contiguous; every
  *    tensor pointer must be 16-byte aligned.
  *  - Calls are asynchronous on `stream` (0 = the null stream); results are
@@ -59,11 +63,15 @@ typedef enum {
   KDA_ERR_MISALIGNED = 5,          /* a tensor pointer is not 16-B aligned   */
   KDA_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the query result */
   KDA_ERR_VARLEN_REQUIRES_B1 = 7,  /* cu_seqlens given with B != 1           */
-  KDA_ERR_ALIAS = 8,               /* o overlaps an input                    */
+  KDA_ERR_ALIAS = 8,               /* an output overlaps an input, another
+                                      output or the workspace                */
   KDA_ERR_HIP = 9,                 /* the HIP runtime reported an error      */
   KDA_ERR_UNSUPPORTED_GATE = 10,   /* gate is not a kda_gate value           */
   KDA_ERR_INVALID_VALUE = 11,      /* a value check failed (validation on)   */
-  KDA_ERR_UNSUPPORTED_ACT = 12     /* input_act has bits no kda_input_act has */
+  KDA_ERR_UNSUPPORTED_ACT = 12,    /* input_act has bits no kda_input_act has */
+  KDA_ERR_STREAM_CAPTURE = 13      /* the call has to wait for the device
+                                      (value checks, status query) but the
+                                      stream is being captured into a graph  */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -134,9 +142,12 @@ const char *kda_status_string(kda_status s);
  *     the value": the write replaces the value stored along k when |k| = 1),
  *   - cu_seqlens does not start at 0, decreases, or does not end at T.
  * The check reads every input once more and then SYNCHRONISES `stream`
- * (the only case in which a call waits for the device).  The initial state
- * is on when the environment variable KDA_VALIDATE holds a nonzero integer
- * at load time.  Process-wide; returns the previous setting.
+ * (with kda_chunk_fwd_status, the only cases in which a call waits for the
+ * device), so on a stream being captured into a graph a call with checks on
+ * returns KDA_ERR_STREAM_CAPTURE.  Checks from several host threads run one
+ * at a time.  The initial state is on when the environment variable
+ * KDA_VALIDATE holds a nonzero integer at load time.  Process-wide; returns
+ * the previous setting (enable < 0 only returns the current one).
  */
 int kda_set_validation(int enable);
 
@@ -155,14 +166,17 @@ int kda_set_validation(int enable);
  *     the record is read from that XCD's L2).  The call forks from and joins
  *     back to `stream` with events, so it stays asynchronous and ordered on
  *     `stream`.  Used for dense bf16 batches with d_k = d_v = 128 on a full
- *     MI355X (256 CUs); other calls run two-phase.  Both schedules give
- *     bitwise identical results.  Calls from several host threads are
- *     serialised around the internal streams, which are created on the first
- *     overlapped call (if that fails, e.g. under stream capture, the device
- *     stays on two-phase).  If the preparation cannot run for more than about
- *     a second (another process holding its compute units), the scan stops
- *     waiting and its results are wrong; the schedule's error word in the
- *     workspace records that.
+ *     MI355X (256 CUs); other calls run two-phase, and so does every call
+ *     made while `stream` is being captured into a graph (a replay keeps
+ *     neither the compute-unit masks nor the concurrency the scan waits
+ *     on).  Both schedules give bitwise identical results.  Calls from
+ *     several host threads are serialised around the internal streams,
+ *     which are created on the first overlapped call on a device (if that
+ *     fails, the device stays on two-phase) and released by kda_release().
+ *     If the preparation cannot run for more than about a second (another
+ *     process holding its compute units), the scan stops waiting and its
+ *     results are wrong: kda_chunk_fwd_status then reports
+ *     KDA_SCHED_ERR_TIMEOUT for that workspace.
  *   KDA_SCHEDULE_AUTO (default): overlap when supported, the scan's
  *     workgroups (B * H * d_v / 32) fit on 128 compute units, and the batch
  *     holds at least 4096 chunks over all sequences and heads
@@ -178,6 +192,41 @@ typedef enum {
   KDA_SCHEDULE_OVERLAP = 2
 } kda_schedule;
 int kda_set_schedule(int schedule);
+
+/*
+ * What the last kda_chunk_fwd call that launched work with this workspace
+ * did: *schedule receives the schedule it ran (KDA_SCHEDULE_TWO_PHASE or
+ * KDA_SCHEDULE_OVERLAP) and *errors the overlapped schedule's error bits
+ * (0 for a clean call; KDA_SCHED_ERR_TIMEOUT: a wait for a chunk record gave
+ * up, so that call's o and S_final are wrong; KDA_SCHED_ERR_XCD: a record
+ * was read on another XCD than the one that wrote it).  The workspace keeps
+ * these words in its first 256 bytes.  Reads them with a copy on `stream`
+ * and SYNCHRONISES the stream (so returns KDA_ERR_STREAM_CAPTURE while it
+ * is being captured).  Either output pointer may be NULL.  Before any call
+ * has used the workspace the words are whatever it held.
+ */
+enum { KDA_SCHED_ERR_TIMEOUT = 1, KDA_SCHED_ERR_XCD = 2 };
+kda_status kda_chunk_fwd_status(const void *workspace, hipStream_t stream,
+                                int *schedule, unsigned *errors);
+
+/*
+ * Destroys the internal streams and events the overlapped schedule created
+ * (after the work queued on them finishes), on every device.  Idempotent;
+ * a later overlapped call creates them again.  Also registered with atexit
+ * by the first call that creates them.
+ */
+void kda_release(void);
+
+/*
+ * The bound on one wait of the overlapped schedule's scan for a chunk
+ * record, in ticks of the GPU's 100 MHz real-time counter (default 2^27,
+ * about 1.3 s); a wait that reaches it gives up, so the kernel always ends,
+ * and sets KDA_SCHED_ERR_TIMEOUT.  0 gives up at once without waiting: the
+ * way to exercise that error path on purpose (the call's results are then
+ * wrong).  Process-wide; returns the previous value (ticks < 0 only returns
+ * the current one).
+ */
+long long kda_set_sched_wait_limit(long long ticks);
 
 /*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes (host-only
@@ -207,8 +256,10 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v,
  *  S_final  [N, H, d_v, d_k] fp32      final states; may be the same buffer
  *           as S0 (in-place update)
  *  workspace / workspace_bytes: device scratch of at least
- *           kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, N, dtype) bytes,
- *           16-B aligned; its contents on entry do not matter.
+ *           kda_chunk_fwd_workspace_size(B, T, H, d_k, d_v, N, dtype) bytes
+ *           (at least 256 for any shape), 16-B aligned; its contents on
+ *           entry do not matter.  It must not overlap any other argument;
+ *           S_final must not overlap an input unless it is exactly S0.
  *
  * T = 0 (or an empty packed batch) copies S0 (or zeros) to S_final.
  */

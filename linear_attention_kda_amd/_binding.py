@@ -8,11 +8,14 @@ fallback: if the library is missing the import fails loudly.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libkda.so")
+# KDA_LIBRARY loads another build of the same ABI (the CPU sanitizer job's
+# host-only build of the argument checks); by default the in-tree library
+LIB_PATH = os.environ.get("KDA_LIBRARY") or os.path.join(PKG_DIR, "libkda.so")
 
 KDA_F32 = 0
 KDA_BF16 = 1
@@ -40,12 +43,17 @@ KDA_SCHEDULE_TWO_PHASE = 1
 KDA_SCHEDULE_OVERLAP = 2
 SCHEDULES = {"auto": KDA_SCHEDULE_AUTO, "two_phase": KDA_SCHEDULE_TWO_PHASE, "overlap": KDA_SCHEDULE_OVERLAP}
 
+# error bits of kda_chunk_fwd_status
+KDA_SCHED_ERR_TIMEOUT = 1
+KDA_SCHED_ERR_XCD = 2
+
 # names exported by include/kda.h
-EXPORTED = ("kda_status_string", "kda_set_validation", "kda_set_schedule", "kda_chunk_fwd_workspace_size",
-            "kda_chunk_fwd",
+EXPORTED = ("kda_status_string", "kda_set_validation", "kda_set_schedule", "kda_chunk_fwd_status",
+            "kda_release", "kda_set_sched_wait_limit", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_decode_step", "kda_decode_step_gated",
             "kda_decode_tokens", "kda_decode_tokens_ex")
 KDA_ERR_INVALID_VALUE = 11
+KDA_ERR_STREAM_CAPTURE = 13
 
 
 class KdaError(RuntimeError):
@@ -90,10 +98,19 @@ def _load() -> ctypes.CDLL:
     lib.kda_set_validation.argtypes = [i32]
     lib.kda_set_schedule.restype = i32
     lib.kda_set_schedule.argtypes = [i32]
+    lib.kda_chunk_fwd_status.restype = i32
+    lib.kda_chunk_fwd_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_uint)]
+    lib.kda_release.restype = None
+    lib.kda_release.argtypes = []
+    lib.kda_set_sched_wait_limit.restype = ctypes.c_longlong
+    lib.kda_set_sched_wait_limit.argtypes = [ctypes.c_longlong]
     return lib
 
 
 lib = _load()
+# the overlapped schedule's internal streams go before the interpreter (and
+# the HIP runtime under it) shuts down
+atexit.register(lib.kda_release)
 
 
 def status_string(status: int) -> str:
@@ -106,6 +123,34 @@ def set_validation(enable: bool) -> bool:
     stream and raises KdaError (status KDA_ERR_INVALID_VALUE) on inputs
     outside the method's domain."""
     return bool(lib.kda_set_validation(1 if enable else 0))
+
+
+def validation_enabled() -> bool:
+    return bool(lib.kda_set_validation(-1))
+
+
+def chunk_fwd_status(workspace, stream=None):
+    """(schedule name, error bits) of the last chunk_fwd call that launched
+    work with this workspace tensor (see kda_chunk_fwd_status; synchronises
+    the stream)."""
+    sched, errs = ctypes.c_int(0), ctypes.c_uint(0)
+    st = lib.kda_chunk_fwd_status(_ptr(workspace), stream if stream is not None else _stream(workspace.device),
+                                  ctypes.byref(sched), ctypes.byref(errs))
+    if st != 0:
+        raise KdaError("kda_chunk_fwd_status", st)
+    names = {v: k for k, v in SCHEDULES.items()}
+    return names.get(sched.value, str(sched.value)), int(errs.value)
+
+
+def set_sched_wait_limit(ticks: int) -> int:
+    """Bound on one ready-flag wait of the overlapped scan, in 100 MHz ticks
+    (kda_set_sched_wait_limit; 0 gives up at once).  Returns the previous."""
+    return int(lib.kda_set_sched_wait_limit(int(ticks)))
+
+
+def release() -> None:
+    """Destroy the library's internal streams and events (kda_release)."""
+    lib.kda_release()
 
 
 def set_schedule(schedule: str) -> str:
@@ -227,6 +272,13 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gat
                               _ptr(workspace), workspace.numel(), _stream(dev))
     if st != 0:
         raise KdaError("kda_chunk_fwd_ex", st)
+    if validation_enabled():
+        # with value checks on the call has already waited for the device;
+        # a schedule error (a record wait that gave up) means wrong results
+        sched, errs = chunk_fwd_status(workspace)
+        if errs:
+            raise RuntimeError(f"kda_chunk_fwd: the {sched} schedule reported error bits {errs:#x} "
+                               "(results are wrong)")
     return out, S_final
 
 

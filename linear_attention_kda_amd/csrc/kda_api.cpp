@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "kda_launch.h"
 
@@ -51,16 +52,31 @@ std::atomic<int> g_schedule{[] {
   return v == kda::kScheduleTwoPhase || v == kda::kScheduleOverlap ? v : kda::kScheduleAuto;
 }()};
 
+// Bound on the overlapped scan's ready-flag waits (kda_set_sched_wait_limit).
+std::atomic<long long> g_wait_ticks{kda::kDefaultWaitTicks};
+
+// One value check at a time in the process: the kernel reports through one
+// device word per device, cleared before and read back after the check.
+std::mutex g_validate_mu;
+
+bool capturing(hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
+}
+
 // Runs the device checks when they are on.  KDA_OK when off or clean.
 kda_status check_values(const float *alpha, size_t n_alpha, kda_gate gate, const float *beta, size_t n_beta,
                         unsigned act, const void *k, size_t n_krows, int d_k, kda_dtype dtype, const int32_t *cu,
                         int n_seq, int total, hipStream_t stream) {
   if (!g_validate.load(std::memory_order_relaxed)) return KDA_OK;
+  // the check waits for the stream, which a stream being captured cannot do
+  if (capturing(stream)) return KDA_ERR_STREAM_CAPTURE;
   const int range = kda::gate_is_log(gate) ? 1 : kda::gate_is_softplus(gate) ? 2 : 0;
   // keys normalised on load need no unit norm
   kda::ValidateArgs v{alpha, alpha ? n_alpha : 0, range, beta, n_beta, (act & kda::kActBeta) != 0, k,
                       (act & kda::kActQK) ? 0 : n_krows, d_k, dtype == KDA_BF16, cu, n_seq, total};
   unsigned bits = 0;
+  std::lock_guard<std::mutex> lock(g_validate_mu);
   if (kda::run_validation(v, stream, &bits) != hipSuccess) return KDA_ERR_HIP;
   return bits ? KDA_ERR_INVALID_VALUE : KDA_OK;
 }
@@ -79,18 +95,42 @@ const char *kda_status_string(kda_status s) {
     case KDA_ERR_MISALIGNED: return "a tensor pointer is not 16-byte aligned";
     case KDA_ERR_WORKSPACE_TOO_SMALL: return "workspace is smaller than kda_chunk_fwd_workspace_size()";
     case KDA_ERR_VARLEN_REQUIRES_B1: return "cu_seqlens requires B == 1";
-    case KDA_ERR_ALIAS: return "the output overlaps an input";
+    case KDA_ERR_ALIAS: return "an output overlaps an input, another output or the workspace";
     case KDA_ERR_HIP: return "the HIP runtime reported an error";
     case KDA_ERR_UNSUPPORTED_GATE: return "gate must be a kda_gate value (channel, scalar, none, log channel, log scalar)";
     case KDA_ERR_INVALID_VALUE:
       return "an input value is out of range (gate or beta outside [0, 1], a key of norm not 1, or bad cu_seqlens)";
     case KDA_ERR_UNSUPPORTED_ACT: return "input_act has bits that are not kda_input_act flags";
+    case KDA_ERR_STREAM_CAPTURE:
+      return "the stream is being captured into a graph, and this call has to wait for the device";
   }
   return "unknown status";
 }
 
 int kda_set_validation(int enable) {
+  if (enable < 0) return g_validate.load();
   return g_validate.exchange(enable ? 1 : 0);
+}
+
+kda_status kda_chunk_fwd_status(const void *workspace, hipStream_t stream, int *schedule, unsigned *errors) {
+  if (!workspace) return KDA_ERR_NULL_ARG;
+  if (!aligned16(workspace)) return KDA_ERR_MISALIGNED;
+  if (capturing(stream)) return KDA_ERR_STREAM_CAPTURE;
+  int32_t words[2] = {0, 0};
+  static_assert(kda::kCtlSchedule == 0 && kda::kCtlError == 1, "status words first");
+  if (hipMemcpyAsync(words, workspace, sizeof(words), hipMemcpyDeviceToHost, stream) != hipSuccess)
+    return KDA_ERR_HIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return KDA_ERR_HIP;
+  if (schedule) *schedule = words[0];
+  if (errors) *errors = (unsigned)words[1];
+  return KDA_OK;
+}
+
+void kda_release(void) { kda::release_overlap(); }
+
+long long kda_set_sched_wait_limit(long long ticks) {
+  if (ticks < 0) return g_wait_ticks.load();
+  return g_wait_ticks.exchange(ticks);
 }
 
 int kda_set_schedule(int schedule) {
@@ -161,14 +201,21 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const f
   const kda::WorkspacePlan plan = kda::plan_workspace(packed, B, T, H, d_k, N, (int)es);
   if (plan.total > 0 && (!workspace || workspace_bytes < plan.total)) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
-  if (ntok > 0) {
-    const Range ro = range_of(o, ntok * H * d_v * es);
-    const Range ins[] = {range_of(q, qk_bytes), range_of(k, qk_bytes), range_of(v, v_bytes),
-                         range_of(alpha, alpha ? a_bytes : 0), range_of(beta, b_bytes),
-                         range_of(S0, S0 ? s_bytes : 0), range_of(S_final, s_bytes),
-                         range_of(workspace, plan.total)};
+  {
+    // Every output (o, S_final) and the workspace must be disjoint from each
+    // other and from every input; S_final may only be S0 itself (in place).
+    const Range ro = range_of(o, ntok > 0 ? ntok * H * d_v * es : 0);
+    const Range rs = range_of(S_final, s_bytes), rw = range_of(workspace, plan.total);
+    const Range ins[] = {range_of(q, ntok > 0 ? qk_bytes : 0), range_of(k, ntok > 0 ? qk_bytes : 0),
+                         range_of(v, ntok > 0 ? v_bytes : 0), range_of(alpha, alpha && ntok > 0 ? a_bytes : 0),
+                         range_of(beta, ntok > 0 ? b_bytes : 0),
+                         range_of(cu_seqlens, packed ? ((size_t)N + 1) * sizeof(int32_t) : 0)};
     for (const Range &r : ins)
-      if (overlaps(ro, r)) return KDA_ERR_ALIAS;
+      if (overlaps(ro, r) || overlaps(rs, r) || overlaps(rw, r)) return KDA_ERR_ALIAS;
+    const Range rs0 = range_of(S0, S0 ? s_bytes : 0);
+    if (overlaps(ro, rs) || overlaps(ro, rw) || overlaps(rs, rw) || overlaps(ro, rs0) || overlaps(rw, rs0))
+      return KDA_ERR_ALIAS;
+    if (S0 && S0 != S_final && overlaps(rs, rs0)) return KDA_ERR_ALIAS;
   }
   if (N == 0) return KDA_OK;
   if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, ntok * H, input_act, k,
@@ -177,6 +224,7 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const f
 
   kda::PrefillArgs a;
   a.schedule = g_schedule.load(std::memory_order_relaxed);
+  a.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
   a.q = q;
   a.k = k;
   a.v = v;
@@ -224,12 +272,14 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, co
                          : kda::gate_per_token(gate) ? units * sizeof(float) : 0;
   if (units > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
   const size_t es = dtype == KDA_BF16 ? 2 : 4;
-  const Range ro = range_of(o, units * d_v * es);
+  // o and the state S (read and written) must not overlap each other or an input
+  const Range ro = range_of(o, units * d_v * es), rs = range_of(S, units * d_v * d_k * sizeof(float));
   const Range ins[] = {range_of(q, units * d_k * es), range_of(k, units * d_k * es),
                        range_of(v, units * d_v * es), range_of(alpha, alpha ? a_bytes : 0),
-                       range_of(beta, units * sizeof(float)), range_of(S, units * d_v * d_k * sizeof(float))};
+                       range_of(beta, units * sizeof(float))};
   for (const Range &r : ins)
-    if (overlaps(ro, r)) return KDA_ERR_ALIAS;
+    if (overlaps(ro, r) || overlaps(rs, r)) return KDA_ERR_ALIAS;
+  if (overlaps(ro, rs)) return KDA_ERR_ALIAS;
   if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, units, 0, k, units, d_k,
                                          dtype, nullptr, 0, 0, stream))
     return st;
@@ -288,12 +338,15 @@ kda_status kda_decode_tokens_ex(const void *q, const void *k, const void *v, con
   // the state is updated in place or written to a disjoint buffer
   if (S_in != S_out && overlaps(range_of(S_in, s_bytes), range_of(S_out, s_bytes))) return KDA_ERR_ALIAS;
   if (toks > 0) {
-    const Range ro = range_of(o, toks * d_v * es);
+    // o and S_out must not overlap each other or an input (S_out == S_in is
+    // the in-place update, checked above)
+    const Range ro = range_of(o, toks * d_v * es), rso = range_of(S_out, s_bytes);
     const Range ins[] = {range_of(q, toks * d_k * es), range_of(k, toks * d_k * es),
                          range_of(v, toks * d_v * es), range_of(alpha, alpha ? a_bytes : 0),
-                         range_of(beta, toks * sizeof(float)), range_of(S_in, s_bytes), range_of(S_out, s_bytes)};
+                         range_of(beta, toks * sizeof(float))};
     for (const Range &r : ins)
-      if (overlaps(ro, r)) return KDA_ERR_ALIAS;
+      if (overlaps(ro, r) || overlaps(rso, r)) return KDA_ERR_ALIAS;
+    if (overlaps(ro, range_of(S_in, s_bytes)) || overlaps(ro, rso)) return KDA_ERR_ALIAS;
     if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, toks, input_act, k, toks,
                                            d_k, dtype, nullptr, 0, 0, stream))
       return st;

@@ -49,23 +49,28 @@ inline ChunkRecordLayout chunk_record_layout(int dk, int esize) {
   return L;
 }
 
-// Control words of the overlapped schedule (int32, after one ready flag per
-// record): per-XCD task counters of the prep and of the scan, and an error word.
-constexpr int kSchedPrepNext = 0, kSchedScanNext = 8, kSchedError = 16, kSchedWords = 64;
-// kSchedError values: a flag wait timed out / a record came from another XCD
+// Control words at the start of every prefill workspace (kCtlWords int32):
+// the schedule the last call ran (a kSchedule* value other than auto) and
+// the overlapped schedule's error bits, read back by kda_chunk_fwd_status,
+// then that schedule's per-XCD task counters of the prep and of the scan.
+constexpr int kCtlSchedule = 0, kCtlError = 1, kCtlPrepNext = 8, kCtlScanNext = 16, kCtlWords = 64;
+constexpr size_t kCtlBytes = kCtlWords * sizeof(int32_t);
+// error bits: a ready-flag wait timed out / a record came from another XCD
 constexpr int kSchedErrTimeout = 1, kSchedErrXcd = 2;
 
-// Workspace = [index tables (packed batches only)] [chunk records]
-//             [ready flags + control words (dense batches only)].
+// Workspace = [control words] [index tables (packed batches only)]
+//             [chunk records] [ready flags (dense batches only)].
 struct WorkspacePlan {
   int n_seq;           // sequences
   long long max_chunks;// chunk slots (dense: exact count)
+  size_t tables;       // byte offset of the index tables
   size_t tables_bytes; // 0 for dense batches
+  size_t records;      // byte offset of the chunk records
   size_t record_bytes;
-  size_t sched;        // byte offset of the flags (dense only; 0 bytes for packed)
-  size_t sched_bytes;
+  size_t ready;        // byte offset of the ready flags (dense only)
+  size_t ready_bytes;  // one int32 per record slot, 0 for packed batches
   size_t total;
-  // int32 table offsets (in elements from the workspace start), packed only
+  // int32 table offsets (in elements from `tables`), packed only
   size_t seq_tok0, seq_chunk0, chunk_t0, chunk_len, seq_order;
 };
 
@@ -74,6 +79,7 @@ inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
   WorkspacePlan P{};
   ChunkRecordLayout L = chunk_record_layout(dk, esize);
   P.record_bytes = L.bytes;
+  P.tables = kCtlBytes;
   if (packed) {
     P.n_seq = N;
     P.max_chunks = ((long long)T + kChunkTokens - 1) / kChunkTokens + N;
@@ -89,10 +95,10 @@ inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
     P.max_chunks = (long long)B * (((long long)T + kChunkTokens - 1) / kChunkTokens);
     P.tables_bytes = 0;
   }
-  P.sched = P.tables_bytes + (size_t)P.max_chunks * H * P.record_bytes;
-  P.sched_bytes = packed || P.max_chunks == 0 ? 0
-                  : (((size_t)P.max_chunks * H + kSchedWords) * sizeof(int32_t) + 255) / 256 * 256;
-  P.total = P.sched + P.sched_bytes;
+  P.records = P.tables + P.tables_bytes;
+  P.ready = P.records + (size_t)P.max_chunks * H * P.record_bytes;
+  P.ready_bytes = packed ? 0 : ((size_t)P.max_chunks * H * sizeof(int32_t) + 255) / 256 * 256;
+  P.total = P.ready + P.ready_bytes;
   return P;
 }
 
@@ -116,8 +122,13 @@ constexpr unsigned kActBeta = 2;  // beta <- sigmoid(beta)
 // prep and scan overlapped whenever the shapes allow it.
 constexpr int kScheduleAuto = 0, kScheduleTwoPhase = 1, kScheduleOverlap = 2;
 
+// Default bound on one ready-flag wait of the overlapped scan: 2^27 ticks of
+// the 100 MHz real-time counter, about 1.3 s.
+constexpr long long kDefaultWaitTicks = 1ll << 27;
+
 struct PrefillArgs {
   int schedule;               // kSchedule*
+  long long wait_ticks;       // bound on one ready-flag wait (overlapped schedule)
   const void *q, *k, *v;
   const float *alpha, *beta, *S0;
   int gate;
@@ -133,6 +144,10 @@ struct PrefillArgs {
 };
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
+
+// Destroys the internal streams and events of the overlapped schedule on
+// every device (kda_release); idempotent.
+void release_overlap();
 
 // Optional value checks (see kda_set_validation).  Bits of the result:
 constexpr unsigned kValidateAlpha = 1, kValidateBeta = 2, kValidateKey = 4, kValidateOffsets = 8;

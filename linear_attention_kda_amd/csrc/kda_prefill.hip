@@ -211,7 +211,7 @@ struct PrepKArgs {
   char *ws_records;
   ChunkRecordLayout lay;
   // overlapped schedule (null otherwise): the ready words (ready_words per
-  // unit), the control words (kSchedWords) and the number of units
+  // unit), the control words (kCtlWords) and the number of units
   int *ready, *ctl;
   int ready_words, n_units;
 };
@@ -876,13 +876,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int x = xcd_id();
   const int nux = a.n_units > x ? (a.n_units - x + 7) / 8 : 0;
   if (threadIdx.x == 0)
-    sTask = __hip_atomic_fetch_add(a.ctl + kSchedPrepNext + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sTask = __hip_atomic_fetch_add(a.ctl + kCtlPrepNext + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
   const int t = sTask;
   if (t >= nux * a.src.nct) return;
   const int u = x + 8 * (t % nux), ci = t / nux;
   const long long slot = (long long)(u / a.H) * a.src.nct + ci;
   prep_one(slot, u % a.H);
+  // the producing XCD, in the record's padding after D_{0:63}; the scan
+  // checks it against its own (the record is read through this XCD's L2)
+  if (threadIdx.x == 0)
+    *reinterpret_cast<int *>(a.ws_records + ((size_t)slot * a.H + u % a.H) * a.lay.bytes + a.lay.p63 + DK * 4) = x;
   __builtin_amdgcn_s_waitcnt(0);  // this thread's record stores are done
   __syncthreads();
   if (threadIdx.x == 0)
@@ -904,11 +908,13 @@ struct ScanKArgs {
   float scale;
   int n_units;                           // sequences * heads
   int wg_per_unit;                       // workgroups per unit (value tiles / waves per WG)
-  // overlapped schedule only: ready words (ready_words per unit, bit c % 32
-  // of word c / 32 set once chunk c's record is in L2) and control words
+  // control words (both schedules: the two-phase scan records its schedule
+  // there); overlapped schedule only: ready words (ready_words per unit, bit
+  // c % 32 of word c / 32 set once chunk c's record is in L2)
   const int *ready;
   int ready_words;
   int *ctl;
+  long long wait_ticks;  // bound on one ready-flag wait (100 MHz ticks; 0: give up at once)
 };
 
 // B operands built from accumulator tiles.  Tile q of a K x 16 operand holds
@@ -1221,13 +1227,13 @@ void chunk_scan_kernel(ScanKArgs a) {
 
   const int w = wave_id(), l = lane_id(), col = l & 15, g = l >> 4;
   int u, grp;  // unit and value-column group of this workgroup
+  const int x = SCHED ? xcd_id() : 0;
   if constexpr (SCHED) {
     // overlapped schedule: the next (unit, group) ticket of this XCD, whose
     // prep workers produce the records of units u = x (mod 8)
     __shared__ int sTicket;
-    const int x = xcd_id();
     if (threadIdx.x == 0)
-      sTicket = __hip_atomic_fetch_add(a.ctl + kSchedScanNext + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sTicket = __hip_atomic_fetch_add(a.ctl + kCtlScanNext + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __syncthreads();
     u = x + 8 * (sTicket / a.wg_per_unit);
     grp = sTicket % a.wg_per_unit;
@@ -1235,6 +1241,11 @@ void chunk_scan_kernel(ScanKArgs a) {
     const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
     u = (slot / a.wg_per_unit) * 8 + xcd;
     grp = slot % a.wg_per_unit;
+    // the schedule this call ran, and no schedule errors
+    if (bid == 0 && threadIdx.x == 0) {
+      a.ctl[kCtlSchedule] = kScheduleTwoPhase;
+      a.ctl[kCtlError] = 0;
+    }
   }
   if (u >= a.n_units) return;
   const int n = a.seq_order ? a.seq_order[u / a.H] : u / a.H, h = u % a.H;
@@ -1319,9 +1330,9 @@ void chunk_scan_kernel(ScanKArgs a) {
   // Overlapped schedule: chunk ci's record may be copied once bit ci % 32 of
   // the unit's ready word ci / 32 is set.  Lane 0 reads the word (bypassing
   // the CU's L1: agent-scope load) only when the bit is not known yet; a wait
-  // longer than 1.3 s (the prep could not run) sets kSchedErrTimeout and the
-  // wave stops waiting: the results are then wrong, but the kernel always
-  // finishes.
+  // longer than a.wait_ticks (1.3 s by default: the prep could not run) sets
+  // kSchedErrTimeout and the wave stops waiting: the results are then wrong,
+  // but the kernel always finishes.  A bound of 0 gives up without reading.
   unsigned known = 0;
   int known_word = -1;
   bool gave_up = false;
@@ -1334,6 +1345,12 @@ void chunk_scan_kernel(ScanKArgs a) {
         known = 0;
       }
       if ((known & bit) || gave_up) return;
+      if (a.wait_ticks <= 0) {
+        if (l == 0) __hip_atomic_fetch_or(a.ctl + kCtlError, kSchedErrTimeout, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        gave_up = true;
+        return;
+      }
       const int *word = a.ready + (size_t)u * a.ready_words + wd;
       const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
       for (;;) {
@@ -1341,8 +1358,8 @@ void chunk_scan_kernel(ScanKArgs a) {
         if (l == 0) v = (unsigned)__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         known = __builtin_amdgcn_readfirstlane(v);
         if (known & bit) break;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > (1ull << 27)) {  // 100 MHz ticks
-          if (l == 0) __hip_atomic_fetch_or(a.ctl + kSchedError, kSchedErrTimeout, __ATOMIC_RELAXED,
+        if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)a.wait_ticks) {  // 100 MHz ticks
+          if (l == 0) __hip_atomic_fetch_or(a.ctl + kCtlError, kSchedErrTimeout, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
           gave_up = true;
           break;
@@ -1408,6 +1425,12 @@ void chunk_scan_kernel(ScanKArgs a) {
                         : zero4();
 
   auto compute = [&](const char *recb, const E *vs, f32x4 (*ov)[NT]) {
+    if constexpr (SCHED) {
+      // the record must come from this XCD's prep workers (stamped by them)
+      static_assert(RS::p63 + DK * 4 + 4 <= RS::bytes, "room for the XCD stamp");
+      if (w == 0 && l == 0 && *reinterpret_cast<const int *>(recb + RS::p63 + DK * 4) != x)
+        __hip_atomic_fetch_or(a.ctl + kCtlError, kSchedErrXcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     scan_chunk<DK, E, NT, WC>(recb, vs + w * VC, st, ov);
   };
 
@@ -1485,9 +1508,12 @@ void chunk_scan_kernel(ScanKArgs a) {
       *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
 }
 
-// Zeroes the ready words and control words of the overlapped schedule.
-__global__ void sched_clear_kernel(int *p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+// Zeroes the control words and the ready words of the overlapped schedule
+// and records that schedule as the one this call runs.
+__global__ void sched_clear_kernel(int *ctl, int *ready, int n_ready) {
+  const int tid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (tid < kCtlWords) ctl[tid] = tid == kCtlSchedule ? kScheduleOverlap : 0;
+  for (int i = tid; i < n_ready; i += gridDim.x * blockDim.x) ready[i] = 0;
 }
 
 // The prep kernel for a gate form, with or without the q, k activation.
@@ -1542,7 +1568,11 @@ void launch_scan(int cw, dim3 grid, hipStream_t stream, const ScanKArgs &sa) {
 // which finishes well before the scan, slowed the scan less on 112 CUs (a
 // call of 1833-1839 us) than on 128 (1985 us) or 96 (1852 us); on 80 it
 // became the bound (2441 us).
-// Created on first use and kept for the life of the process.
+// Created on the first overlapped call on a device; released by
+// kda_release() (also run at process exit, before the HIP runtime and any
+// profiler attached to it are torn down: streams still alive at that point
+// were destroyed by the runtime's own teardown after the profiler had
+// finalised, and the process then crashed in __cxa_finalize).
 struct OverlapCtx {
   bool tried = false, ok = false;
   hipStream_t scan = nullptr, prep = nullptr;
@@ -1550,21 +1580,37 @@ struct OverlapCtx {
 };
 std::mutex g_overlap_mu;  // guards g_overlap and the event sequence of a launch
 OverlapCtx g_overlap[64];
+bool g_atexit_registered = false;  // guarded by g_overlap_mu
 constexpr int kScanCUs = 128, kPrepCUs = 112;
 // copy waves of the overlapped scan: four measured 4 % faster than three on
 // a 1024-chunk chain
 constexpr int kOverlapCopyWaves = 4;
 
+// Destroys what one device's context holds (caller holds g_overlap_mu and
+// has made that device current).
+void destroy_ctx(OverlapCtx &c) {
+  if (c.scan) (void)hipStreamDestroy(c.scan);
+  if (c.prep) (void)hipStreamDestroy(c.prep);
+  if (c.fork) (void)hipEventDestroy(c.fork);
+  if (c.done_scan) (void)hipEventDestroy(c.done_scan);
+  if (c.done_prep) (void)hipEventDestroy(c.done_prep);
+  c = OverlapCtx{};
+}
+
+void release_at_exit() { release_overlap(); }
+
 // The current device's streams, or null if the schedule cannot run there
-// (caller holds g_overlap_mu).  They are not created while `stream` is being
-// captured into a graph (that call runs two-phase; a later one creates them).
+// (caller holds g_overlap_mu).  A call whose stream is being captured into a
+// graph never takes the overlapped schedule: a graph replay keeps neither
+// the compute-unit masks nor the guarantee that the prep runs beside the
+// scan, whose waits would then time out.
 OverlapCtx *overlap_ctx(hipStream_t stream) {
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
   OverlapCtx &c = g_overlap[dev];
   if (!c.tried) {
-    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return nullptr;
     c.tried = true;
     int ncu = 0;
     hipDeviceProp_t prop;
@@ -1572,13 +1618,18 @@ OverlapCtx *overlap_ctx(hipStream_t stream) {
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return nullptr;
     // eight XCDs of 32 CUs (the whole MI355X as one device)
     if (ncu != 256 || std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return nullptr;
+    if (!g_atexit_registered) g_atexit_registered = std::atexit(release_at_exit) == 0;
     uint32_t ms[8] = {0}, mp[8] = {0};
     for (int i = 0; i < kScanCUs + kPrepCUs; ++i) (i < kScanCUs ? ms : mp)[i / 32] |= 1u << (i % 32);
-    if (hipExtStreamCreateWithCUMask(&c.scan, 8, ms) != hipSuccess) return nullptr;
-    if (hipExtStreamCreateWithCUMask(&c.prep, 8, mp) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&c.fork, hipEventDisableTiming) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&c.done_scan, hipEventDisableTiming) != hipSuccess) return nullptr;
-    if (hipEventCreateWithFlags(&c.done_prep, hipEventDisableTiming) != hipSuccess) return nullptr;
+    if (hipExtStreamCreateWithCUMask(&c.scan, 8, ms) != hipSuccess ||
+        hipExtStreamCreateWithCUMask(&c.prep, 8, mp) != hipSuccess ||
+        hipEventCreateWithFlags(&c.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c.done_scan, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c.done_prep, hipEventDisableTiming) != hipSuccess) {
+      destroy_ctx(c);
+      c.tried = true;  // stay on two-phase on this device
+      return nullptr;
+    }
     c.ok = true;
   }
   return c.ok ? &c : nullptr;
@@ -1587,7 +1638,7 @@ OverlapCtx *overlap_ctx(hipStream_t stream) {
 // Shapes the overlapped schedule supports: dense bf16 batches at
 // d_k = d_v = 128 (two records and two value tiles fill the scan's LDS).
 template <int DK, typename E> bool overlap_supported(const PrefillArgs &a) {
-  return DK == 128 && a.dv == 128 && sizeof(E) == 2 && !a.cu_seqlens && a.plan.sched_bytes > 0;
+  return DK == 128 && a.dv == 128 && sizeof(E) == 2 && !a.cu_seqlens && a.plan.ready_bytes > 0;
 }
 
 // Automatic choice: the overlap needs the scan's workgroups (four per unit at
@@ -1616,11 +1667,11 @@ hipError_t run_prefill_overlap(const PrefillArgs &a, hipStream_t stream, PrepKAr
   const int nct = (a.T + kChunk - 1) / kChunk;
   const int n_units = a.B * a.H;
   const int words = (nct + 31) / 32;  // ready words per unit
-  int *ready = reinterpret_cast<int *>(a.ws + P.sched);
-  int *ctl = ready + P.max_chunks * a.H;  // n_units * words <= chunk slots * heads
-  const int nclear = (int)(P.max_chunks * a.H) + kSchedWords;
-  hipLaunchKernelGGL(sched_clear_kernel, dim3((unsigned)min(64, (nclear + 255) / 256)), dim3(256), 0, stream, ready,
-                     nclear);
+  int *ready = reinterpret_cast<int *>(a.ws + P.ready);  // n_units * words <= chunk slots * heads
+  int *ctl = reinterpret_cast<int *>(a.ws);
+  const int nclear = (int)(P.max_chunks * a.H);
+  hipLaunchKernelGGL(sched_clear_kernel, dim3((unsigned)min(64, (nclear + 255) / 256)), dim3(256), 0, stream, ctl,
+                     ready, nclear);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if ((e = hipEventRecord(ov.fork, stream)) != hipSuccess) return e;
@@ -1646,6 +1697,7 @@ hipError_t run_prefill_overlap(const PrefillArgs &a, hipStream_t stream, PrepKAr
     sa.ready = ready;
     sa.ready_words = words;
     sa.ctl = ctl;
+    sa.wait_ticks = a.wait_ticks;
     // a ticket per (unit, group): eight times those of the XCD with most units
     const dim3 sg((unsigned)(8 * ((n_units + 7) / 8) * sa.wg_per_unit));
     hipLaunchKernelGGL((chunk_scan_kernel<DK, E, 1, 2, kOverlapCopyWaves, true>), sg, dim3(64 * (2 + kOverlapCopyWaves)),
@@ -1674,8 +1726,9 @@ template <int DK, typename E>
 hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
   const WorkspacePlan &P = a.plan;
   const ChunkRecordLayout lay = chunk_record_layout(DK, (int)sizeof(E));
-  char *records = a.ws + P.tables_bytes;
-  int32_t *tables = reinterpret_cast<int32_t *>(a.ws);
+  char *records = a.ws + P.records;
+  int32_t *tables = reinterpret_cast<int32_t *>(a.ws + P.tables);
+  int *ctl = reinterpret_cast<int *>(a.ws);
   const bool packed = a.cu_seqlens != nullptr;
   const int nct = (a.T + kChunk - 1) / kChunk;
 
@@ -1737,6 +1790,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     sa.seq_order = packed ? tables + P.seq_order : nullptr;
     sa.scale = a.scale;
     sa.n_units = P.n_seq * a.H;
+    sa.ctl = ctl;
     // Two compute waves of one 16-column tile each per workgroup (one wave
     // when d_v = 16 or two stages would not fit in LDS) and four copy
     // waves: measured fastest at d_v = 128 against two tiles per wave
@@ -1766,6 +1820,30 @@ template <typename E> hipError_t run_prefill_dk(const PrefillArgs &a, hipStream_
 }
 
 }  // namespace
+
+void release_overlap() {
+  std::lock_guard<std::mutex> lock(g_overlap_mu);
+  auto holds = [](const OverlapCtx &c) { return c.scan || c.prep || c.fork || c.done_scan || c.done_prep; };
+  bool any = false;
+  for (const OverlapCtx &c : g_overlap) any = any || holds(c);
+  if (!any) {  // nothing was created: no runtime call at all
+    for (OverlapCtx &c : g_overlap) c = OverlapCtx{};
+    return;
+  }
+  int cur = -1;
+  const bool have_cur = hipGetDevice(&cur) == hipSuccess;
+  for (int dev = 0; dev < 64; ++dev) {
+    OverlapCtx &c = g_overlap[dev];
+    if (holds(c) && hipSetDevice(dev) == hipSuccess) {
+      // work still queued on the streams finishes before they go
+      if (c.scan) (void)hipStreamSynchronize(c.scan);
+      if (c.prep) (void)hipStreamSynchronize(c.prep);
+      destroy_ctx(c);
+    }
+    c = OverlapCtx{};
+  }
+  if (have_cur) (void)hipSetDevice(cur);
+}
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   return a.bf16 ? run_prefill_dk<bf16>(a, stream) : run_prefill_dk<float>(a, stream);

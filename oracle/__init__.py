@@ -15,13 +15,16 @@ from __future__ import annotations
 
 import ctypes
 import os
+import shlex
 import subprocess
 
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "kda_oracle.c")
-LIB_PATH = os.path.join(_HERE, "libkda_oracle.so")
+# KDA_ORACLE_LIB and KDA_ORACLE_CFLAGS let a test job build and load the
+# oracle elsewhere and with extra compiler flags (the sanitizer job does)
+LIB_PATH = os.environ.get("KDA_ORACLE_LIB") or os.path.join(_HERE, "libkda_oracle.so")
 
 _DP = ctypes.POINTER(ctypes.c_double)
 _I64P = ctypes.POINTER(ctypes.c_int64)
@@ -31,7 +34,7 @@ def compile_oracle(source: str = SOURCE, out: str = LIB_PATH) -> str:
     """Compile the oracle C source into a shared library with gcc."""
     tmp = out + ".tmp"
     cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
-           "-o", tmp, source, "-lm"]
+           *shlex.split(os.environ.get("KDA_ORACLE_CFLAGS", "")), "-o", tmp, source, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -166,3 +169,41 @@ def rel_l2(x, ref) -> float:
     if den == 0.0:
         return num
     return num / den
+
+
+def unit_rel_l2(x, ref, unit_axes=(0, 1), cu_seqlens=None) -> np.ndarray:
+    """Relative L2 error of every (sequence, head) unit, in fp64.
+
+    Dense layout: ``unit_axes`` names the sequence axis and the head axis;
+    the error and the reference norm are summed over every other axis.
+    Packed layout (``cu_seqlens`` given, length N+1): axis 0 is the packed
+    token axis and axis 1 the head axis; sequence n owns tokens
+    [cu[n], cu[n+1]).  Returns an array [sequences, heads]; a unit whose
+    reference is all zero reports its absolute error, as rel_l2 does."""
+    x = _to_f64(x)
+    ref = _to_f64(ref)
+    if x.shape != ref.shape:
+        raise ValueError(f"shapes differ: {x.shape} vs {ref.shape}")
+    d2 = (x - ref) ** 2
+    r2 = ref ** 2
+    if cu_seqlens is not None:
+        cu = np.asarray(cu_seqlens.cpu() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+                        dtype=np.int64)
+        rest = tuple(range(2, x.ndim))
+        d2t, r2t = d2.sum(axis=rest), r2.sum(axis=rest)      # [tokens, heads]
+        N = cu.shape[0] - 1
+        num = np.zeros((N, x.shape[1]))
+        den = np.zeros((N, x.shape[1]))
+        for n in range(N):
+            a, b = int(cu[n]), int(cu[n + 1])
+            num[n] = d2t[a:b].sum(axis=0)
+            den[n] = r2t[a:b].sum(axis=0)
+    else:
+        a0, a1 = unit_axes
+        rest = tuple(i for i in range(x.ndim) if i not in (a0, a1))
+        num = d2.sum(axis=rest)
+        den = r2.sum(axis=rest)
+        if a0 > a1:
+            num, den = num.T, den.T
+    num, den = np.sqrt(num), np.sqrt(den)
+    return np.where(den > 0.0, num / np.where(den > 0.0, den, 1.0), num)

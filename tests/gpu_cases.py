@@ -53,8 +53,33 @@ def rel(x, ref) -> float:
     return oracle.rel_l2(x, ref)
 
 
-def check(name, got, ref, tol):
+def unit_axes(name: str, ndim: int):
+    """The (sequence, head) axes of a checked tensor, from its name and rank:
+    states S [N, H, d_v, d_k] -> (0, 1); outputs o [B, T, H, d_v] (dense
+    prefill, or [N, Tk, H, d_v] for several decode tokens) -> (0, 2); outputs
+    o [N, H, d_v] of a decode step -> (0, 1).  Packed outputs [T, H, d_v]
+    need their offsets (check(..., cu=...))."""
+    if name.startswith("S"):
+        return (0, 1)
+    if ndim == 4:
+        return (0, 2)
+    if ndim == 3:
+        return (0, 1)
+    raise ValueError(f"no unit axes for {name} of rank {ndim}")
+
+
+def check(name, got, ref, tol, cu=None):
+    """Relative L2 error against the oracle, over the whole tensor and per
+    (sequence, head) unit; both must be within tol, so one wrong unit among
+    many cannot hide in the whole-tensor figure."""
     r = rel(got, ref)
-    print(f"    {name}: rel_l2 = {r:.3e} (tol {tol:.0e})", flush=True)
+    if cu is not None:
+        per = oracle.unit_rel_l2(got, ref, cu_seqlens=cu)
+    else:
+        per = oracle.unit_rel_l2(got, ref, unit_axes(name, got.ndim))
+    worst = float(per.max()) if per.size else 0.0
+    at = tuple(int(i) for i in np.unravel_index(int(per.argmax()), per.shape)) if per.size else ()
+    print(f"    {name}: rel_l2 = {r:.3e}, worst (seq, head) {at} = {worst:.3e} (tol {tol:.0e})", flush=True)
     assert np.isfinite(r) and r <= tol, f"{name}: rel_l2 {r:.3e} > {tol:.0e}"
+    assert np.isfinite(worst) and worst <= tol, f"{name}: unit {at} rel_l2 {worst:.3e} > {tol:.0e}"
     return r

@@ -1,0 +1,77 @@
+// host_stubs.cpp -- host-only stand-ins for the kernel launchers and for the
+// three HIP runtime calls that kda_api.cpp makes, so the C ABI's argument
+// checks and workspace planning can be built with the address and
+// undefined-behaviour sanitizers and run on a machine without a GPU.  Test
+// infrastructure only: never linked into libkda.so.
+//
+// The launch stand-ins check that what the ABI layer hands the launchers is
+// consistent (the workspace plan fits the workspace it was checked against,
+// the shapes are the ones the call was made with) and count the calls; the
+// counts are read back through kda_stub_calls().
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+
+#include "kda_launch.h"
+
+namespace {
+int g_calls[3];        // prefill, decode, validation
+int g_bad_plans;       // plans that failed a consistency check
+}  // namespace
+
+namespace kda {
+
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t) {
+  ++g_calls[0];
+  const WorkspacePlan &P = a.plan;
+  const bool ok = P.tables == kCtlBytes && P.records == P.tables + P.tables_bytes &&
+                  P.ready == P.records + (size_t)P.max_chunks * a.H * P.record_bytes &&
+                  P.total == P.ready + P.ready_bytes && P.record_bytes % 1024 == 0 && a.ws != nullptr &&
+                  (a.cu_seqlens ? P.ready_bytes == 0 : P.n_seq == a.B) && a.scale > 0.f &&
+                  (a.dk == 16 || a.dk == 32 || a.dk == 64 || a.dk == 128);
+  if (!ok) ++g_bad_plans;
+  return hipSuccess;
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t) {
+  ++g_calls[1];
+  if (a.N <= 0 || a.H <= 0 || a.Tk < 0 || !a.S || !a.S_in || a.scale <= 0.f) ++g_bad_plans;
+  return hipSuccess;
+}
+
+hipError_t run_validation(const ValidateArgs &, hipStream_t, unsigned *bits) {
+  ++g_calls[2];
+  *bits = 0;
+  return hipSuccess;
+}
+
+void release_overlap() {}
+
+}  // namespace kda
+
+extern "C" {
+
+// which: 0 prefill launches, 1 decode launches, 2 validation runs, 3 plans
+// that failed a consistency check; -1 resets every count
+int kda_stub_calls(int which) {
+  if (which < 0) {
+    std::memset(g_calls, 0, sizeof(g_calls));
+    g_bad_plans = 0;
+    return 0;
+  }
+  return which < 3 ? g_calls[which] : g_bad_plans;
+}
+
+hipError_t hipStreamIsCapturing(hipStream_t, hipStreamCaptureStatus *s) {
+  *s = hipStreamCaptureStatusNone;
+  return hipSuccess;
+}
+
+hipError_t hipMemcpyAsync(void *dst, const void *, size_t n, hipMemcpyKind, hipStream_t) {
+  std::memset(dst, 0, n);  // no device: the status words read back as zero
+  return hipSuccess;
+}
+
+hipError_t hipStreamSynchronize(hipStream_t) { return hipSuccess; }
+
+}  // extern "C"

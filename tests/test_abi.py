@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(kda):
 
 
 def test_status_strings(kda):
-    for s in range(13):
+    for s in range(14):
         assert kda.status_string(s) and kda.status_string(s) != "unknown status"
     assert kda.status_string(99) == "unknown status"
 
@@ -43,12 +43,14 @@ def test_workspace_size(kda):
     # k-slabs that reach the diagonal (6 slabs of 32 columns in bf16) and d_k
     # floats, rounded up to 1 KiB
     rec = (3 * 64 * 128 * 2 + 2 * 6 * 1024 + 128 * 4 + 1023) // 1024 * 1024
-    # then one int32 ready flag per record and 64 control words of the
-    # overlapped schedule, rounded up to 256 bytes
+    # after 64 control words (256 bytes: the status of the last call and the
+    # overlapped schedule's counters), then one int32 ready flag per record,
+    # rounded up to 256 bytes
     nrec = 4 * 32 * 16
-    sched = ((nrec + 64) * 4 + 255) // 256 * 256
-    assert kda.chunk_fwd_workspace_size(4, 2048, 16, 128, 128, -1, kda.KDA_BF16) == nrec * rec + sched
-    assert kda.chunk_fwd_workspace_size(2, 0, 3, 32, 32, -1, kda.KDA_F32) == 0
+    ready = (nrec * 4 + 255) // 256 * 256
+    assert kda.chunk_fwd_workspace_size(4, 2048, 16, 128, 128, -1, kda.KDA_BF16) == 256 + nrec * rec + ready
+    # no tokens: the control words alone
+    assert kda.chunk_fwd_workspace_size(2, 0, 3, 32, 32, -1, kda.KDA_F32) == 256
     # packed: tables plus (ceil(T/64) + N) chunk slots
     packed = kda.chunk_fwd_workspace_size(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)
     rec64 = (3 * 64 * 64 * 2 + 2 * 6 * 1024 + 64 * 4 + 1023) // 1024 * 1024
@@ -87,6 +89,14 @@ def test_chunk_fwd_validation(kda):
     assert _fwd(kda, ws=None) == 6
     assert _fwd(kda, o=P(0x30000)) == 8              # o aliases v
     assert _fwd(kda, o=P(0x80000)) == 8              # o aliases the workspace
+    assert _fwd(kda, S_final=P(0x10000)) == 8        # S_final aliases q
+    assert _fwd(kda, S_final=P(0x80000)) == 8        # S_final aliases the workspace
+    assert _fwd(kda, ws=P(0x30000)) == 8             # the workspace aliases v
+    assert _fwd(kda, ws=P(0x50000)) == 8             # ... beta
+    assert _fwd(kda, S0=P(0x70000 + 256)) == 8       # S0 overlaps S_final without being it
+    assert _fwd(kda, S0=P(0x60000)) == 8             # S0 overlaps o
+    assert _fwd(kda, S0=P(0x80000)) == 8             # S0 overlaps the workspace
+    assert _fwd(kda, cu=P(0x70000), B=1) == 8        # the offsets overlap S_final
 
 
 def test_decode_validation(kda):
@@ -105,6 +115,8 @@ def test_decode_validation(kda):
     assert call(S=None) == 1
     assert call(beta=P(0x50008)) == 5
     assert call(o=P(0x60000)) == 8                   # o aliases S
+    assert call(S=P(0x10000)) == 8                   # the state overlaps q
+    assert call(S=P(0x50000)) == 8                   # ... beta
 
 
 def _fwd_gated(kda, gate, **kw):
@@ -168,6 +180,7 @@ def test_decode_tokens_validation(kda):
     assert call(Si=None) == 1
     assert call(So=P(0x100000 + 256)) == 8          # partial overlap of the two states
     assert call(o=P(0x100000)) == 8                 # o overlaps a state
+    assert call(So=P(0x30000)) == 8                 # the output state overlaps v
     assert call(gate=kda.KDA_GATE_SCALAR, alpha=None) == 1
     assert call(N=0) == 0
 
@@ -193,5 +206,29 @@ def test_set_validation_toggles(kda):
         assert kda.set_validation(True) is True
         assert kda.set_validation(False) is True
         assert kda.set_validation(False) is False
+    finally:
+        kda.set_validation(prev)
+
+
+def test_status_query_and_release_host_checks(kda):
+    # rejected before any device access
+    P = ctypes.c_void_p
+    sched, errs = ctypes.c_int(-7), ctypes.c_uint(7)
+    assert kda.lib.kda_chunk_fwd_status(None, None, ctypes.byref(sched), ctypes.byref(errs)) == 1
+    assert kda.lib.kda_chunk_fwd_status(P(0x80004), None, ctypes.byref(sched), ctypes.byref(errs)) == 5
+    assert sched.value == -7 and errs.value == 7            # outputs untouched on error
+    # nothing was created: release is a no-op, and may run any number of times
+    kda.release()
+    kda.release()
+
+
+def test_set_validation_query(kda):
+    prev = kda.set_validation(False)
+    try:
+        assert kda.lib.kda_set_validation(-1) == 0
+        assert kda.validation_enabled() is False
+        kda.set_validation(True)
+        assert kda.lib.kda_set_validation(-1) == 1      # a query changes nothing
+        assert kda.validation_enabled() is True
     finally:
         kda.set_validation(prev)

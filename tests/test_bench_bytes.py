@@ -32,6 +32,15 @@ def test_long_context_bytes():
     assert bench.prefill_bytes(B, T, H, d, d, s0=True) == total
 
 
+def test_packed_bytes():
+    # the seeded draw of the packed-batch workload: 274,797 tokens, 64 sequences
+    T, N, H, d = 274_797, 64, 16, 128
+    per_tok = 4 * d * BF16 + d * F32 + F32
+    total = T * H * per_tok + 2 * N * H * d * d * F32
+    assert total == 6_905_215_808
+    assert bench.packed_bytes(T, N, H, d, d) == total
+
+
 def test_gate_form_bytes():
     B, T, H, d = 4, 2048, 16, 128
     tok = B * T * H

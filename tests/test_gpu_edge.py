@@ -97,7 +97,7 @@ def test_packed_ragged(dtype):
     inp = to_dev(inputs.packed(lens, 3, 64, 64, dtype, s0_std=0.1, seed=6))
     o, S = gpu_prefill(inp)
     o_ref, S_ref = oracle_prefill(inp)
-    check("o", o, o_ref, TOL[dtype])
+    check("o", o, o_ref, TOL[dtype], cu=inp["cu_seqlens"])
     check("S_final", S, S_ref, TOL[dtype])
     # zero-length sequences return their S0 exactly
     assert torch.equal(S[0], inp["S0"][0]) and torch.equal(S[7], inp["S0"][7])

@@ -97,7 +97,7 @@ def test_packed_fused_inputs():
     inp = _raw(inp, 53)
     o, S = _run(inp, "softplus_channel", QK | BETA)
     o_ref, S_ref = oracle_prefill(_activated(inp, QK | BETA, "softplus_channel", 128))
-    check("o", o, o_ref, TOL[torch.bfloat16])
+    check("o", o, o_ref, TOL[torch.bfloat16], cu=inp["cu_seqlens"])
     check("S_final", S, S_ref, TOL[torch.bfloat16])
 
 

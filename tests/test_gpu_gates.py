@@ -59,7 +59,7 @@ def test_packed_scalar_gates():
     o, S = _run(inp, "scalar")
     full = _expand(inp, 64)
     o_ref, S_ref = oracle_prefill(full)
-    check("o", o, o_ref, TOL[torch.bfloat16])
+    check("o", o, o_ref, TOL[torch.bfloat16], cu=inp["cu_seqlens"])
     check("S_final", S, S_ref, TOL[torch.bfloat16])
 
 

@@ -60,7 +60,7 @@ def test_packed_log_channel_gates():
                                gate_form="log_channel"))
     o, S = _run(inp, "log_channel")
     o_ref, S_ref = oracle_prefill(_linear(inp, 128))
-    check("o", o, o_ref, TOL[torch.bfloat16])
+    check("o", o, o_ref, TOL[torch.bfloat16], cu=inp["cu_seqlens"])
     check("S_final", S, S_ref, TOL[torch.bfloat16])
 
 

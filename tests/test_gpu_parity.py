@@ -1,7 +1,8 @@
 """HIP path vs the fp64 oracle on the five workloads (GPU).
 
-Tolerances are relative L2 over a whole tensor: 1e-5 for the fp32 path and
-2e-2 for bf16 inputs, on both o and S_final.
+Tolerances are relative L2, over the whole tensor and over every (sequence,
+head) unit on its own: 1e-5 for the fp32 path and 2e-2 for bf16 inputs, on
+both o and S_final.
 """
 import numpy as np
 import pytest
@@ -32,11 +33,14 @@ def test_prefill_bf16_full():
 
 
 def test_long_context_sampled_heads():
-    """Full T=65536 run; the oracle recomputes four of the 32 heads."""
-    announce("long B1 H32 T65536 d128 bf16 seed0 (oracle heads 0,9,22,31)")
+    """Full T=65536 run (a 1024-chunk chain per head); the oracle recomputes
+    eight of the 32 heads, one from each residue mod 8 (the units of one
+    residue share an XCD in the scan's mapping), every one checked on its
+    own as well as together."""
+    heads = [0, 9, 18, 27, 4, 13, 22, 31]
+    announce(f"long B1 H32 T65536 d128 bf16 seed0 (oracle heads {heads})")
     inp = inputs.workload("long", device="cuda")
     o, S = gpu_prefill(inp)
-    heads = [0, 9, 22, 31]
     o_ref, S_ref = oracle_prefill(inp, heads=heads)
     idx = torch.tensor(heads, device="cuda")
     check("o[heads]", o.index_select(2, idx), o_ref, TOL[torch.bfloat16])
@@ -61,34 +65,45 @@ def test_varlen_sampled_sequences():
                S0=inp["S0"][torch.tensor(pick).cuda()],
                cu_seqlens=torch.tensor(np.concatenate([[0], np.cumsum(sub_lens)]), dtype=torch.int32))
     o_ref, S_ref = oracle_prefill(sub)
-    check("o[sampled seqs]", o[toks.cuda()], o_ref, TOL[torch.bfloat16])
+    check("o[sampled seqs]", o[toks.cuda()], o_ref, TOL[torch.bfloat16], cu=sub["cu_seqlens"])
     check("S_final[sampled seqs]", S[torch.tensor(pick).cuda()], S_ref, TOL[torch.bfloat16])
     # the whole output must be finite and every state written
     assert torch.isfinite(o).all() and torch.isfinite(S).all()
 
 
 def test_decode_full_size_steps():
-    """Decode workload at full size (256 x 32 heads, 512 MiB state) for 4
-    steps; the oracle follows 96 sampled (sequence, head) states."""
+    """Decode workload at full size (256 x 32 heads, 512 MiB state) over its
+    whole chain of 1024 steps; the oracle follows 96 sampled (sequence, head)
+    states.  Outputs are checked at every step (the worst step is reported)
+    and the states after steps 1, 256 and 1024, so drift of the fp32 state
+    over the configured chain is pinned."""
     import linear_attention_kda_amd as kda
     import oracle
-    announce("decode N256 H32 d128 bf16 seed0, 4 steps (oracle on 96 units)")
     w = inputs.WORKLOADS["decode"]
-    N, H, dk, dv = w["N"], w["H"], w["dk"], w["dv"]
+    N, H, dk, dv, steps = w["N"], w["H"], w["dk"], w["dv"], w["steps"]
+    announce(f"decode N{N} H{H} d{dk} bf16 seed0, {steps} steps (oracle on 96 units)")
     S = inputs.decode_state(N, H, dk, dv, w["s0_std"], seed=0, device="cuda")
     g = torch.Generator().manual_seed(5)
     units = torch.randperm(N * H, generator=g)[:96]
-    nsel, hsel = units // H, units % H
-    S_ref = S[nsel.cuda(), hsel.cuda()].double().cpu().numpy()[:, None]
-    for step in range(4):
+    nsel, hsel = (units // H).cuda(), (units % H).cuda()
+    sel = lambda x: x[nsel, hsel].cpu()[:, None]
+    S_ref = S[nsel, hsel].double().cpu().numpy()[:, None]
+    worst_o, worst_step = 0.0, -1
+    for step in range(steps):
         tok = inputs.decode_token(N, H, dk, dv, w["dtype"], w["alpha_lo"], step=step, device="cuda")
         o = kda.decode_step(tok["q"], tok["k"], tok["v"], tok["alpha"], tok["beta"], S)
         torch.cuda.synchronize()
-        sel = lambda x: x[nsel.cuda(), hsel.cuda()].cpu()[:, None]
         o_ref, S_ref = oracle.decode(sel(tok["q"]), sel(tok["k"]), sel(tok["v"]), sel(tok["alpha"]),
                                      sel(tok["beta"]), S_ref)
-        check(f"o step {step}", o[nsel.cuda(), hsel.cuda()][:, None], o_ref, TOL[torch.bfloat16])
-    check("S after 4 steps", S[nsel.cuda(), hsel.cuda()][:, None], S_ref, TOL[torch.bfloat16])
+        o_got = o[nsel, hsel][:, None]
+        per = oracle.unit_rel_l2(o_got, o_ref)
+        if float(per.max()) > worst_o:
+            worst_o, worst_step = float(per.max()), step + 1
+        if step + 1 in (1, 256, steps):
+            check(f"o after step {step + 1}", o_got, o_ref, TOL[torch.bfloat16])
+            check(f"S after step {step + 1}", S[nsel, hsel][:, None], S_ref, TOL[torch.bfloat16])
+    print(f"    o: worst unit over all {steps} steps = {worst_o:.3e} (step {worst_step})", flush=True)
+    assert worst_o <= TOL[torch.bfloat16]
 
 
 def test_decode_tokens_full_size():

@@ -4,9 +4,10 @@ chunk's record as soon as its ready flag is set (page "Kimi Delta Attention
 (KDA)", section "Two schedules of computation for one recurrence": the
 parallel chunk stage feeds the sequential scan).  Both schedules execute the
 same arithmetic per chunk, so their results must be bitwise equal; one case
-per group is also checked against the fp64 oracle, and the schedule's error
-word (a timed-out wait or a record from another XCD) must stay clear."""
-import numpy as np
+per group is also checked against the fp64 oracle, and the call's status
+(kda_chunk_fwd_status: the schedule that ran, and the error bits for a
+timed-out wait or a record from another XCD) must name the schedule and show
+no error."""
 import pytest
 import torch
 
@@ -15,8 +16,6 @@ from tests.gpu_cases import TOL, announce, check, oracle_prefill, to_dev
 
 pytestmark = pytest.mark.gpu
 
-REC_BYTES = 62464          # one d=128 bf16 chunk record (see test_abi)
-ERR_WORD = 16              # index of the error word among the control words
 
 
 def _run(inp, schedule, gate="channel", act=0, ws=None):
@@ -37,10 +36,9 @@ def _workspace(B, T, H):
     return torch.zeros(n, dtype=torch.uint8, device="cuda")
 
 
-def _error_word(ws, B, T, H):
-    nrec = B * ((T + 63) // 64) * H
-    off = nrec * REC_BYTES + (nrec + ERR_WORD) * 4
-    return int(ws[off:off + 4].cpu().numpy().view(np.int32)[0])
+def _status(ws):
+    import linear_attention_kda_amd as kda
+    return kda.chunk_fwd_status(ws)
 
 
 @pytest.mark.parametrize("B,T,H,s0", [
@@ -55,8 +53,9 @@ def test_overlap_equals_two_phase(B, T, H, s0):
     inp = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=s0, seed=21))
     ws = _workspace(B, T, H)
     o1, S1 = _run(inp, "overlap", ws=ws)
-    assert _error_word(ws, B, T, H) == 0
-    o2, S2 = _run(inp, "two_phase")
+    assert _status(ws) == ("overlap", 0)
+    o2, S2 = _run(inp, "two_phase", ws=ws)
+    assert _status(ws) == ("two_phase", 0)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
@@ -102,18 +101,20 @@ def test_overlap_repeated_calls_share_workspace():
     for seed in (31, 32, 33):
         inp = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=0.02, seed=seed))
         o1, S1 = _run(inp, "overlap", ws=ws)
-        assert _error_word(ws, B, T, H) == 0
+        assert _status(ws) == ("overlap", 0)
         o2, S2 = _run(inp, "two_phase")
         assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
 def test_overlap_in_graph_capture():
-    """The overlapped call captured into a HIP graph (its fork and join are
-    event nodes, its clear is a kernel): replays with new inputs copied in,
-    with eager work and synchronisation between them, match the eager
-    two-phase results bitwise."""
+    """A call captured into a HIP graph while the overlapped schedule is
+    requested runs two-phase (a replay keeps neither the compute-unit masks
+    nor the concurrency the scan would wait on), also once the internal
+    streams exist: replays with new inputs copied in, with eager work and
+    synchronisation between them, match the eager two-phase results bitwise,
+    and the status of each replay names the two-phase schedule."""
     import linear_attention_kda_amd as kda
-    announce("schedule overlap captured in a graph: 3 replays vs eager two-phase, B=2 T=640 H=8")
+    announce("overlap requested under graph capture: 3 replays vs eager two-phase, B=2 T=640 H=8")
     B, T, H = 2, 640, 8
     ws = _workspace(B, T, H)
     static = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=0.02, seed=40))
@@ -126,6 +127,7 @@ def test_overlap_in_graph_capture():
                           out=o, S_final=S, workspace=ws)
         call()  # eager once: creates the internal streams outside the capture
         torch.cuda.synchronize()
+        assert _status(ws) == ("overlap", 0)
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -144,29 +146,75 @@ def test_overlap_in_graph_capture():
             graph.replay()
             torch.cuda.synchronize()
             o_g, S_g = o.clone(), S.clone()
-            assert _error_word(ws, B, T, H) == 0
+            assert _status(ws) == ("two_phase", 0)
             o_e, S_e = _run(new, "two_phase")
             assert torch.equal(o_g, o_e) and torch.equal(S_g, S_e)
     finally:
         kda.set_schedule(prev)
 
 
+def test_overlap_timeout_is_reported():
+    """The scan's bounded wait for a chunk record, forced to give up from the
+    host (a bound of zero ticks: no wait at all), ends every kernel normally
+    and is reported: kda_chunk_fwd_status shows the timeout bit, and with
+    value checks on the binding raises instead of returning the wrong
+    results.  A later call with the default bound is clean again."""
+    import linear_attention_kda_amd as kda
+    announce("overlap scan wait bound 0 (forced timeout), B=2 T=640 H=8; then the default bound")
+    B, T, H = 2, 640, 8
+    ws = _workspace(B, T, H)
+    inp = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=0.02, seed=44))
+    prev_limit = kda.set_sched_wait_limit(0)
+    try:
+        _run(inp, "overlap", ws=ws)
+        sched, errs = _status(ws)
+        assert sched == "overlap" and errs & kda.KDA_SCHED_ERR_TIMEOUT
+        prev_val = kda.set_validation(True)
+        try:
+            prev_sched = kda.set_schedule("overlap")
+            try:
+                with pytest.raises(RuntimeError, match="error bits"):
+                    kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"],
+                                  workspace=ws)
+                torch.cuda.synchronize()
+            finally:
+                kda.set_schedule(prev_sched)
+        finally:
+            kda.set_validation(prev_val)
+    finally:
+        kda.set_sched_wait_limit(prev_limit)
+    o1, S1 = _run(inp, "overlap", ws=ws)
+    assert _status(ws) == ("overlap", 0)
+    o2, S2 = _run(inp, "two_phase")
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
 @pytest.mark.parametrize("T,overlap", [(8192, True), (8128, False)])
 def test_auto_schedule_threshold(T, overlap):
     """The automatic schedule overlaps from 4096 chunk records (B * H *
-    ceil(T / 64)): 32 heads x 128 chunks do, 32 x 127 do not.  Only the
-    overlapped schedule touches the prep's per-XCD task counters, so in a
-    workspace that starts zeroed they show which schedule ran; the results
-    equal the two-phase schedule's bit for bit either way."""
+    ceil(T / 64)): 32 heads x 128 chunks do, 32 x 127 do not, as the call's
+    status shows; the results equal the two-phase schedule's bit for bit
+    either way."""
     B, H = 1, 32
     announce(f"schedule auto at the overlap threshold, B={B} T={T} H={H} (overlap expected: {overlap})")
     inp = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, seed=23))
     ws = _workspace(B, T, H)
     o1, S1 = _run(inp, "auto", ws=ws)
-    nrec = B * ((T + 63) // 64) * H
-    off = nrec * REC_BYTES + nrec * 4            # the control words follow the ready words
-    prep_tickets = ws[off:off + 32].cpu().numpy().view(np.int32)
-    assert (int(prep_tickets.sum()) > 0) == overlap
-    assert _error_word(ws, B, T, H) == 0
+    assert _status(ws) == ("overlap" if overlap else "two_phase", 0)
     o2, S2 = _run(inp, "two_phase")
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_long_context_overlap_equals_two_phase_all_heads():
+    """The long-context workload at full size (32 heads x 1024 chunks, the
+    shape the automatic schedule overlaps): every head, on every XCD's share
+    of the units, equals the two-phase result bit for bit."""
+    announce("long-context B1 H32 T65536 d128: overlap vs two-phase, all 32 heads bitwise")
+    inp = inputs.workload("long", device="cuda")
+    ws = _workspace(1, 65536, 32)
+    o1, S1 = _run(inp, "overlap", ws=ws)
+    assert _status(ws) == ("overlap", 0)
+    o2, S2 = _run(inp, "two_phase", ws=ws)
+    assert _status(ws) == ("two_phase", 0)
+    for h in range(32):
+        assert torch.equal(o1[:, :, h], o2[:, :, h]) and torch.equal(S1[:, h], S2[:, h]), f"head {h} differs"
