@@ -69,9 +69,11 @@ typedef enum {
   KDA_ERR_UNSUPPORTED_GATE = 10,   /* gate is not a kda_gate value           */
   KDA_ERR_INVALID_VALUE = 11,      /* a value check failed (validation on)   */
   KDA_ERR_UNSUPPORTED_ACT = 12,    /* input_act has bits no kda_input_act has */
-  KDA_ERR_STREAM_CAPTURE = 13      /* the call has to wait for the device
+  KDA_ERR_STREAM_CAPTURE = 13,     /* the call has to wait for the device
                                       (value checks, status query) but the
                                       stream is being captured into a graph  */
+  KDA_ERR_TOO_LARGE = 14           /* more scratch than kda_chunk_fwd_noalloc
+                                      holds                                  */
 } kda_status;
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
@@ -321,6 +323,34 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v,
                             int d_k, int d_v, float scale, kda_dtype dtype, void *o,
                             float *S_final, void *workspace,
                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_ex for callers that cannot allocate device memory: code
+ * being captured into a HIP graph, tight serving loops, harnesses that
+ * forbid allocation.  It takes no workspace: the kernels run on a static
+ * device array of the library's own, 64 MiB per device, held until the
+ * process ends.  The call itself allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine) and always runs the two-phase
+ * schedule; value checks (kda_set_validation) do not apply to it.
+ *  - A dense batch whose workspace (kda_chunk_fwd_workspace_size) fits in
+ *    64 MiB runs as one call.  A larger dense batch runs one sequence at a
+ *    time, in segments of whole 64-token chunks that fit, each segment
+ *    starting from the state the previous one left in S_final: the same
+ *    chunks and the same arithmetic, so the results equal kda_chunk_fwd_ex's
+ *    bit for bit.  Sizes where not even one chunk per head fits return
+ *    KDA_ERR_TOO_LARGE.
+ *  - A packed batch (cu_seqlens) must fit whole, else KDA_ERR_TOO_LARGE.
+ * Every call on a device shares that device's array, which keeps the last
+ * call's contents: calls that overlap in time on one device (two streams,
+ * or two host threads) race and give wrong results; serialise them.
+ */
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                 const float *alpha, kda_gate gate,
+                                 const float *beta, unsigned input_act,
+                                 const float *S0, const int32_t *cu_seqlens,
+                                 int N, int B, int T, int H, int d_k, int d_v,
+                                 float scale, kda_dtype dtype, void *o,
+                                 float *S_final, hipStream_t stream);
 
 kda_status kda_decode_step_gated(const void *q, const void *k, const void *v,
                                  const float *alpha, kda_gate gate,

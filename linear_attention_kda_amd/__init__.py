@@ -13,7 +13,8 @@ _BINDING_NAMES = ("EXPORTED", "GATES", "KDA_BF16", "KDA_F32", "KDA_GATE_CHANNEL"
                   "decode_step", "decode_tokens", "lib", "set_validation", "set_schedule", "status_string",
                   "KDA_SCHEDULE_AUTO", "KDA_SCHEDULE_TWO_PHASE", "KDA_SCHEDULE_OVERLAP", "SCHEDULES",
                   "KDA_ERR_INVALID_VALUE", "KDA_ERR_STREAM_CAPTURE", "KDA_SCHED_ERR_TIMEOUT", "KDA_SCHED_ERR_XCD",
-                  "chunk_fwd_status", "release", "validation_enabled", "set_sched_wait_limit")
+                  "chunk_fwd_status", "release", "validation_enabled", "set_sched_wait_limit",
+                  "chunk_fwd_noalloc", "KDA_ERR_TOO_LARGE", "NOALLOC_SCRATCH_BYTES")
 
 
 def __getattr__(name):

@@ -51,9 +51,11 @@ KDA_SCHED_ERR_XCD = 2
 EXPORTED = ("kda_status_string", "kda_set_validation", "kda_set_schedule", "kda_chunk_fwd_status",
             "kda_release", "kda_set_sched_wait_limit", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_decode_step", "kda_decode_step_gated",
-            "kda_decode_tokens", "kda_decode_tokens_ex")
+            "kda_decode_tokens", "kda_decode_tokens_ex", "kda_chunk_fwd_noalloc")
 KDA_ERR_INVALID_VALUE = 11
 KDA_ERR_STREAM_CAPTURE = 13
+KDA_ERR_TOO_LARGE = 14
+NOALLOC_SCRATCH_BYTES = 64 << 20   # the static device scratch of kda_chunk_fwd_noalloc
 
 
 class KdaError(RuntimeError):
@@ -100,6 +102,9 @@ def _load() -> ctypes.CDLL:
     lib.kda_set_schedule.argtypes = [i32]
     lib.kda_chunk_fwd_status.restype = i32
     lib.kda_chunk_fwd_status.argtypes = [vp, vp, ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_uint)]
+    lib.kda_chunk_fwd_noalloc.restype = i32
+    lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, i32, i32, i32, i32, i32,
+                                          i32, f32, i32, vp, vp, vp]
     lib.kda_release.restype = None
     lib.kda_release.argtypes = []
     lib.kda_set_sched_wait_limit.restype = ctypes.c_longlong
@@ -209,8 +214,17 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def chunk_fwd_noalloc(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gate=None, out=None,
+                      S_final=None, act=0):
+    """chunk_fwd through kda_chunk_fwd_noalloc: no workspace, the library's
+    static device scratch instead (outputs are still allocated here unless
+    given: pass ``out`` and ``S_final`` to allocate nothing)."""
+    return chunk_fwd(q, k, v, alpha, beta, S0, cu_seqlens, scale, gate=gate, out=out, S_final=S_final, act=act,
+                     _noalloc=True)
+
+
 def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gate=None, out=None,
-              S_final=None, workspace=None, act=0):
+              S_final=None, workspace=None, act=0, _noalloc=False):
     """Chunked prefill.  Returns (o, S_final).
 
     ``act``: kda_input_act flags (KDA_ACT_QK_SILU_L2NORM, KDA_ACT_BETA_SIGMOID)
@@ -263,6 +277,13 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gat
         out = torch.empty(v.shape, dtype=v.dtype, device=dev)
     if S_final is None:
         S_final = torch.empty((N, H, d_v, d_k), dtype=torch.float32, device=dev)
+    if _noalloc:
+        st = lib.kda_chunk_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), int(act), _ptr(S0),
+                                       _ptr(cu_seqlens), N, B, T, H, d_k, d_v, float(scale) if scale else 0.0, dt,
+                                       _ptr(out), _ptr(S_final), _stream(dev))
+        if st != 0:
+            raise KdaError("kda_chunk_fwd_noalloc", st)
+        return out, S_final
     ws_need = chunk_fwd_workspace_size(B, T, H, d_k, d_v, N if cu_seqlens is not None else -1, dt)
     if workspace is None or workspace.numel() < ws_need:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <atomic>
 #include <cstdint>
@@ -81,6 +82,162 @@ kda_status check_values(const float *alpha, size_t n_alpha, kda_gate gate, const
   return bits ? KDA_ERR_INVALID_VALUE : KDA_OK;
 }
 
+// The no-allocation prefill (kda_chunk_fwd_noalloc): the same kernels, two-
+// phase, on the library's static device scratch instead of a caller's
+// workspace.  A packed batch, or a dense batch whose whole plan fits, runs as
+// one call; a larger dense batch runs one sequence at a time in segments of
+// whole chunks, each segment starting from the state the previous one left
+// in S_final (identical arithmetic: a chunk boundary is a chunk boundary).
+// No value checks (they would copy to the host and wait).
+kda_status chunk_fwd_scratch(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                             const float *beta, unsigned input_act, const float *S0, const int32_t *cu_seqlens, int N,
+                             int B, int T, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
+                             float *S_final, hipStream_t stream) {
+  const int es = dtype == KDA_BF16 ? 2 : 4;
+  const bool packed = cu_seqlens != nullptr;
+  const kda::WorkspacePlan whole = kda::plan_workspace(packed, B, T, H, d_k, N, es);
+  char *scratch = nullptr;
+  if (kda::scratch_address(reinterpret_cast<void **>(&scratch)) != hipSuccess || !scratch) return KDA_ERR_HIP;
+  kda::PrefillArgs a{};
+  a.schedule = kda::kScheduleTwoPhase;
+  a.wait_ticks = kda::kDefaultWaitTicks;
+  a.gate = (int)gate;
+  a.act = input_act;
+  a.H = H;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.scale = default_scale(scale, d_k);
+  a.bf16 = dtype == KDA_BF16;
+  a.ws = scratch;
+  if (packed || T == 0 || whole.total <= kda::kScratchBytes) {
+    if (whole.total > kda::kScratchBytes) return KDA_ERR_TOO_LARGE;
+    a.q = q; a.k = k; a.v = v; a.alpha = alpha; a.beta = beta; a.S0 = S0; a.cu_seqlens = cu_seqlens;
+    a.o = o; a.S_final = S_final; a.plan = whole; a.B = B; a.T = T;
+    return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+  }
+  // chunks per segment: the most that fit, for one sequence
+  const int nct = (T + kda::kChunkTokens - 1) / kda::kChunkTokens;
+  int seg = nct;
+  while (seg > 0 && kda::plan_workspace(false, 1, seg * kda::kChunkTokens, H, d_k, 1, es).total > kda::kScratchBytes)
+    seg = seg > 64 ? seg / 2 : seg - 1;
+  if (seg == 0) return KDA_ERR_TOO_LARGE;
+  const size_t tok_q = (size_t)H * d_k, tok_v = (size_t)H * d_v;
+  const size_t tok_a = kda::gate_per_channel(gate) ? tok_q : kda::gate_per_token(gate) ? (size_t)H : 0;
+  const size_t state = (size_t)H * d_v * d_k;
+  for (int b = 0; b < B; ++b) {
+    for (int c0 = 0; c0 < nct; c0 += seg) {
+      const size_t t0 = (size_t)b * T + (size_t)c0 * kda::kChunkTokens;
+      const int Ts = (int)std::min<long long>((long long)seg * kda::kChunkTokens, (long long)T - (long long)c0 * kda::kChunkTokens);
+      a.q = static_cast<const char *>(q) + t0 * tok_q * es;
+      a.k = static_cast<const char *>(k) + t0 * tok_q * es;
+      a.v = static_cast<const char *>(v) + t0 * tok_v * es;
+      a.alpha = alpha ? alpha + t0 * tok_a : nullptr;
+      a.beta = beta + t0 * H;
+      a.o = static_cast<char *>(o) + t0 * tok_v * es;
+      a.S_final = S_final + (size_t)b * state;
+      // the first segment starts from S0 (or zeros), every later one from the
+      // state the previous segment wrote (S_final in place)
+      a.S0 = c0 == 0 ? (S0 ? S0 + (size_t)b * state : nullptr) : a.S_final;
+      a.cu_seqlens = nullptr;
+      a.B = 1;
+      a.T = Ts;
+      a.plan = kda::plan_workspace(false, 1, Ts, H, d_k, 1, es);
+      if (kda::launch_prefill(a, stream) != hipSuccess) return KDA_ERR_HIP;
+    }
+  }
+  return KDA_OK;
+}
+
+// kda_chunk_fwd_ex, and with noalloc its variant on the library's static
+// scratch (kda_chunk_fwd_noalloc; workspace is then ignored).
+kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                          const float *beta, unsigned input_act, const float *S0, const int32_t *cu_seqlens, int N,
+                          int B, int T, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
+                          float *S_final, void *workspace, size_t workspace_bytes, hipStream_t stream, bool noalloc) {
+  if (noalloc) {
+    workspace = nullptr;
+    workspace_bytes = 0;
+  }
+  if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
+  if (input_act & ~kActAll) return KDA_ERR_UNSUPPORTED_ACT;
+  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
+  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
+  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
+  const bool packed = cu_seqlens != nullptr;
+  if (packed) {
+    if (B != 1) return KDA_ERR_VARLEN_REQUIRES_B1;
+    if (N < 0) return KDA_ERR_BAD_SHAPE;
+  } else {
+    N = B;
+  }
+  const size_t es = dtype == KDA_BF16 ? 2 : 4;
+  const size_t ntok = (size_t)B * T;
+  const size_t qk_bytes = ntok * H * d_k * es, v_bytes = ntok * H * d_v * es;
+  const size_t a_bytes = kda::gate_per_channel(gate) ? ntok * H * d_k * sizeof(float)
+                         : kda::gate_per_token(gate) ? ntok * H * sizeof(float) : 0;
+  const size_t b_bytes = ntok * H * sizeof(float);
+  const size_t s_bytes = (size_t)N * H * d_v * d_k * sizeof(float);
+  if (gate == KDA_GATE_NONE) alpha = nullptr;
+  if (ntok > 0 && (!q || !k || !v || (a_bytes && !alpha) || !beta || !o)) return KDA_ERR_NULL_ARG;
+  if (s_bytes > 0 && !S_final) return KDA_ERR_NULL_ARG;
+  if (ntok > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
+  const void *ptrs[] = {q, k, v, alpha, beta, S0, cu_seqlens, o, S_final, workspace};
+  for (const void *p : ptrs)
+    if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+
+  const kda::WorkspacePlan plan = kda::plan_workspace(packed, B, T, H, d_k, N, (int)es);
+  if (!noalloc && plan.total > 0 && (!workspace || workspace_bytes < plan.total)) return KDA_ERR_WORKSPACE_TOO_SMALL;
+
+  {
+    // Every output (o, S_final) and the workspace must be disjoint from each
+    // other and from every input; S_final may only be S0 itself (in place).
+    const Range ro = range_of(o, ntok > 0 ? ntok * H * d_v * es : 0);
+    const Range rs = range_of(S_final, s_bytes), rw = range_of(workspace, noalloc ? 0 : plan.total);
+    const Range ins[] = {range_of(q, ntok > 0 ? qk_bytes : 0), range_of(k, ntok > 0 ? qk_bytes : 0),
+                         range_of(v, ntok > 0 ? v_bytes : 0), range_of(alpha, alpha && ntok > 0 ? a_bytes : 0),
+                         range_of(beta, ntok > 0 ? b_bytes : 0),
+                         range_of(cu_seqlens, packed ? ((size_t)N + 1) * sizeof(int32_t) : 0)};
+    for (const Range &r : ins)
+      if (overlaps(ro, r) || overlaps(rs, r) || overlaps(rw, r)) return KDA_ERR_ALIAS;
+    const Range rs0 = range_of(S0, S0 ? s_bytes : 0);
+    if (overlaps(ro, rs) || overlaps(ro, rw) || overlaps(rs, rw) || overlaps(ro, rs0) || overlaps(rw, rs0))
+      return KDA_ERR_ALIAS;
+    if (S0 && S0 != S_final && overlaps(rs, rs0)) return KDA_ERR_ALIAS;
+  }
+  if (N == 0) return KDA_OK;
+  if (noalloc)
+    return chunk_fwd_scratch(q, k, v, alpha, gate, beta, input_act, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale, dtype,
+                             o, S_final, stream);
+  if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, ntok * H, input_act, k,
+                                         ntok * H, d_k, dtype, cu_seqlens, N, T, stream))
+    return st;
+
+  kda::PrefillArgs a;
+  a.schedule = g_schedule.load(std::memory_order_relaxed);
+  a.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.alpha = alpha;
+  a.gate = (int)gate;
+  a.act = input_act;
+  a.beta = beta;
+  a.S0 = S0;
+  a.cu_seqlens = cu_seqlens;
+  a.o = o;
+  a.S_final = S_final;
+  a.ws = static_cast<char *>(workspace);
+  a.plan = plan;
+  a.B = B;
+  a.T = T;
+  a.H = H;
+  a.dk = d_k;
+  a.dv = d_v;
+  a.scale = default_scale(scale, d_k);
+  a.bf16 = dtype == KDA_BF16;
+  return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,6 +260,8 @@ const char *kda_status_string(kda_status s) {
     case KDA_ERR_UNSUPPORTED_ACT: return "input_act has bits that are not kda_input_act flags";
     case KDA_ERR_STREAM_CAPTURE:
       return "the stream is being captured into a graph, and this call has to wait for the device";
+    case KDA_ERR_TOO_LARGE:
+      return "the sizes need more device scratch than the no-allocation entry point holds";
   }
   return "unknown status";
 }
@@ -171,81 +330,16 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const f
                             const float *beta, unsigned input_act, const float *S0, const int32_t *cu_seqlens, int N,
                             int B, int T, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
                             float *S_final, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
-  if (input_act & ~kActAll) return KDA_ERR_UNSUPPORTED_ACT;
-  if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
-  if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
-  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
-  const bool packed = cu_seqlens != nullptr;
-  if (packed) {
-    if (B != 1) return KDA_ERR_VARLEN_REQUIRES_B1;
-    if (N < 0) return KDA_ERR_BAD_SHAPE;
-  } else {
-    N = B;
-  }
-  const size_t es = dtype == KDA_BF16 ? 2 : 4;
-  const size_t ntok = (size_t)B * T;
-  const size_t qk_bytes = ntok * H * d_k * es, v_bytes = ntok * H * d_v * es;
-  const size_t a_bytes = kda::gate_per_channel(gate) ? ntok * H * d_k * sizeof(float)
-                         : kda::gate_per_token(gate) ? ntok * H * sizeof(float) : 0;
-  const size_t b_bytes = ntok * H * sizeof(float);
-  const size_t s_bytes = (size_t)N * H * d_v * d_k * sizeof(float);
-  if (gate == KDA_GATE_NONE) alpha = nullptr;
-  if (ntok > 0 && (!q || !k || !v || (a_bytes && !alpha) || !beta || !o)) return KDA_ERR_NULL_ARG;
-  if (s_bytes > 0 && !S_final) return KDA_ERR_NULL_ARG;
-  if (ntok > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
-  const void *ptrs[] = {q, k, v, alpha, beta, S0, cu_seqlens, o, S_final, workspace};
-  for (const void *p : ptrs)
-    if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
+  return chunk_fwd_impl(q, k, v, alpha, gate, beta, input_act, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale, dtype, o,
+                        S_final, workspace, workspace_bytes, stream, false);
+}
 
-  const kda::WorkspacePlan plan = kda::plan_workspace(packed, B, T, H, d_k, N, (int)es);
-  if (plan.total > 0 && (!workspace || workspace_bytes < plan.total)) return KDA_ERR_WORKSPACE_TOO_SMALL;
-
-  {
-    // Every output (o, S_final) and the workspace must be disjoint from each
-    // other and from every input; S_final may only be S0 itself (in place).
-    const Range ro = range_of(o, ntok > 0 ? ntok * H * d_v * es : 0);
-    const Range rs = range_of(S_final, s_bytes), rw = range_of(workspace, plan.total);
-    const Range ins[] = {range_of(q, ntok > 0 ? qk_bytes : 0), range_of(k, ntok > 0 ? qk_bytes : 0),
-                         range_of(v, ntok > 0 ? v_bytes : 0), range_of(alpha, alpha && ntok > 0 ? a_bytes : 0),
-                         range_of(beta, ntok > 0 ? b_bytes : 0),
-                         range_of(cu_seqlens, packed ? ((size_t)N + 1) * sizeof(int32_t) : 0)};
-    for (const Range &r : ins)
-      if (overlaps(ro, r) || overlaps(rs, r) || overlaps(rw, r)) return KDA_ERR_ALIAS;
-    const Range rs0 = range_of(S0, S0 ? s_bytes : 0);
-    if (overlaps(ro, rs) || overlaps(ro, rw) || overlaps(rs, rw) || overlaps(ro, rs0) || overlaps(rw, rs0))
-      return KDA_ERR_ALIAS;
-    if (S0 && S0 != S_final && overlaps(rs, rs0)) return KDA_ERR_ALIAS;
-  }
-  if (N == 0) return KDA_OK;
-  if (const kda_status st = check_values(alpha, a_bytes / sizeof(float), gate, beta, ntok * H, input_act, k,
-                                         ntok * H, d_k, dtype, cu_seqlens, N, T, stream))
-    return st;
-
-  kda::PrefillArgs a;
-  a.schedule = g_schedule.load(std::memory_order_relaxed);
-  a.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.alpha = alpha;
-  a.gate = (int)gate;
-  a.act = input_act;
-  a.beta = beta;
-  a.S0 = S0;
-  a.cu_seqlens = cu_seqlens;
-  a.o = o;
-  a.S_final = S_final;
-  a.ws = static_cast<char *>(workspace);
-  a.plan = plan;
-  a.B = B;
-  a.T = T;
-  a.H = H;
-  a.dk = d_k;
-  a.dv = d_v;
-  a.scale = default_scale(scale, d_k);
-  a.bf16 = dtype == KDA_BF16;
-  return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                                 const float *beta, unsigned input_act, const float *S0, const int32_t *cu_seqlens,
+                                 int N, int B, int T, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
+                                 float *S_final, hipStream_t stream) {
+  return chunk_fwd_impl(q, k, v, alpha, gate, beta, input_act, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale, dtype, o,
+                        S_final, nullptr, 0, stream, true);
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *alpha, const float *beta,

@@ -149,6 +149,12 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
 // every device (kda_release); idempotent.
 void release_overlap();
 
+// The no-allocation prefill's device scratch: a static array of this many
+// bytes per device, whose address on the current device (looked up once per
+// device with hipGetSymbolAddress) goes to *ptr.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+hipError_t scratch_address(void **ptr);
+
 // Optional value checks (see kda_set_validation).  Bits of the result:
 constexpr unsigned kValidateAlpha = 1, kValidateBeta = 2, kValidateKey = 4, kValidateOffsets = 8;
 constexpr float kValidateKeyTol = 1.0f / 64;  // | |k|^2 - 1 | allowed

@@ -1819,7 +1819,35 @@ template <typename E> hipError_t run_prefill_dk(const PrefillArgs &a, hipStream_
   return hipErrorInvalidValue;
 }
 
+// Device scratch of kda_chunk_fwd_noalloc (prefill for callers that cannot
+// allocate): one copy per device, held for the life of the process.  Host
+// code never uses the array's name as an address (on the host it is a
+// stand-in, not device memory): scratch_address() looks the device address
+// up per device and the kernels take that pointer as their workspace.
+static __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];  // per device, guarded by g_scratch_mu
+
 }  // namespace
+
+hipError_t scratch_address(void **ptr) {
+  *ptr = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 void release_overlap() {
   std::lock_guard<std::mutex> lock(g_overlap_mu);

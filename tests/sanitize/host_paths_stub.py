@@ -97,3 +97,27 @@ def test_status_query_reads_the_words():
 
 def test_environment_is_the_stub_build():
     assert os.environ.get("KDA_LIBRARY", "").endswith("libkda_host_san.so")
+
+
+@pytest.mark.parametrize("B,T,H,segments", [(4, 2048, 16, 4), (2, 8192, 64, 16), (1, 300, 4, 1), (2, 0, 3, 1)])
+def test_noalloc_segments(B, T, H, segments):
+    """The no-allocation entry point: a batch that fits runs as one launch,
+    a larger one as segments of whole chunks per sequence (64 MiB scratch:
+    16 heads x 32 chunks of 61 KiB fit, 64 heads fit 16 chunks)."""
+    p = _ptrs()
+    st = kda.lib.kda_chunk_fwd_noalloc(P(p["q"]), P(p["k"]), P(p["v"]), P(p["alpha"]), 0, P(p["beta"]), 0,
+                                       P(p["S0"]), None, B, B, T, H, 128, 128, 0.0, 1, P(p["o"]), P(p["S"]), None)
+    assert st == 0
+    assert kda.lib.kda_stub_calls(0) == segments
+
+
+def test_noalloc_limits():
+    p = _ptrs()
+    # one chunk of 1100 heads does not fit
+    st = kda.lib.kda_chunk_fwd_noalloc(P(p["q"]), P(p["k"]), P(p["v"]), P(p["alpha"]), 0, P(p["beta"]), 0, None,
+                                       None, 1, 1, 64, 1100, 128, 128, 0.0, 1, P(p["o"]), P(p["S"]), None)
+    assert st == 14 and kda.lib.kda_stub_calls(0) == 0
+    # a packed batch must fit whole
+    st = kda.lib.kda_chunk_fwd_noalloc(P(p["q"]), P(p["k"]), P(p["v"]), P(p["alpha"]), 0, P(p["beta"]), 0, None,
+                                       P(p["cu"]), 1, 1, 70_000, 16, 128, 128, 0.0, 1, P(p["o"]), P(p["S"]), None)
+    assert st == 14 and kda.lib.kda_stub_calls(0) == 0

@@ -10,6 +10,7 @@
 // counts are read back through kda_stub_calls().
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
 #include <cstring>
 
 #include "kda_launch.h"
@@ -46,6 +47,13 @@ hipError_t run_validation(const ValidateArgs &, hipStream_t, unsigned *bits) {
 }
 
 void release_overlap() {}
+
+// a fake but aligned device address (never dereferenced: the launches above
+// are stand-ins too)
+hipError_t scratch_address(void **ptr) {
+  *ptr = reinterpret_cast<void *>((uintptr_t)1 << 44);
+  return hipSuccess;
+}
 
 }  // namespace kda
 
