@@ -1508,6 +1508,421 @@ void chunk_scan_kernel(ScanKArgs a) {
       *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
 }
 
+// ================================================= one-CU-per-unit scan
+// The scan for d_k = d_v = 128 bf16 batches of many units: one workgroup per
+// unit (sequence, head) on one CU instead of four, so each chunk record is
+// copied into LDS once per unit, not once per 32-column group.  Its chunk
+// step is longer than the four-workgroup scan's (1.9 against 1.5 us on the
+// prefill shape: one CU ingests the whole record and does all 128 columns'
+// products), but it holds a quarter of the CUs per unit, so it wins once the
+// units outnumber the chip (more than 64 units at four workgroups each).
+
+// One chunk for a wave owning NT 16-column tiles: the arithmetic and operand
+// order of scan_chunk, with the LDS operand reads software-pipelined one step
+// ahead of their products (the fragments of slab u+1 are requested before
+// slab u's products, each later phase's operands before the previous phase's
+// products), in fewer registers than scan_chunk's read-everything-first order,
+// which three waves per SIMD cannot hold.  (Scheduling barriers that pinned
+// this order exactly were measured slower: 63 against 60 us per prefill-shaped
+// scan.)
+template <int DK, typename E, int NT, int VSTRIDE>
+__device__ __forceinline__ void scan_chunk_lean(const char *recb, const E *vs, f32x4 (*st)[NT], f32x4 (*ov)[NT]) {
+  typedef RecordShape<DK, E> RS;
+  typedef FragShape<E, DK> FK;   // products over d_k
+  typedef FragShape<E, 64> FT;   // products over the 64 tokens
+  constexpr int CT = DK / 16;
+  constexpr int TILE_K = FK::NU * 64 * FK::KS;
+  constexpr int TILE_T = FT::NU * 64 * FT::KS;
+  const int l = lane_id(), col = l & 15, g = l >> 4;
+  typedef BOps<E, DK> BK;
+  typedef BOps<E, 64> BT;
+  constexpr int UK = FK::NU, UT = FT::NU;
+  static_assert(UT == 2, "64 tokens are two k-slabs of 32");
+  const E *Kh = reinterpret_cast<const E *>(recb + RS::kh);
+  const E *Qh = reinterpret_cast<const E *>(recb + RS::qh);
+  const E *KtT = reinterpret_cast<const E *>(recb + RS::ktt);
+  const E *Tb = reinterpret_cast<const E *>(recb + RS::tb);
+  const E *Aq = reinterpret_cast<const E *>(recb + RS::aqk);
+  const float *P63 = reinterpret_cast<const float *>(recb + RS::p63);
+  // the (row tile, slab) fragments of a lower-triangular 64 x 64 operand, in
+  // the order the products use them: slab 0 of tiles 0-3, slab 1 of tiles 2-3
+  constexpr int NTRI = 6;
+  auto tri_frag = [](const E *base, int f) {
+    const int I = f < 4 ? f : f - 2, u = f < 4 ? 0 : 1;
+    return BT::load1(base + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
+  };
+
+  // X_top = Kbnd S^T, X_bot = s Qbnd S^T, slab by slab
+  typename BK::frag fk[2][4], fq[2][4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    fk[0][I] = BK::load1(Kh + I * TILE_K, 0);
+    fq[0][I] = BK::load1(Qh + I * TILE_K, 0);
+  }
+  BK sb[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4 t[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) t[ct] = st[ct][nt];
+    sb[nt].build(t);
+  }
+  f32x4 xt[4][NT], xb[4][NT];
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) xt[I][nt] = xb[I][nt] = zero4();
+#pragma unroll
+  for (int u = 0; u < UK; ++u) {
+    if (u + 1 < UK) {
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        fk[(u + 1) & 1][I] = BK::load1(Kh + I * TILE_K, u + 1);
+        fq[(u + 1) & 1][I] = BK::load1(Qh + I * TILE_K, u + 1);
+      }
+    }
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        xt[I][nt] = sb[nt].mma1(fk[u & 1][I], u, xt[I][nt]);
+        xb[I][nt] = sb[nt].mma1(fq[u & 1][I], u, xb[I][nt]);
+      }
+  }
+  // E's operands and the value rows, requested behind the last X products
+  typename BT::frag ftb[NTRI];
+#pragma unroll
+  for (int f = 0; f < NTRI; ++f) ftb[f] = tri_frag(Tb, f);
+  float vv[NT][4][4];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) vv[nt][I][r] = to_f(vs[(16 * I + 4 * g + r) * VSTRIDE + 16 * nt + col]);
+  // Ebar = V - X_top ; E = Tb Ebar
+  BT ebo[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4 eb[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) eb[I][r] = vv[nt][I][r] - xt[I][nt][r];
+    ebo[nt].build(eb);
+  }
+  typename BT::frag faq[NTRI];
+#pragma unroll
+  for (int f = 0; f < NTRI; ++f) faq[f] = tri_frag(Aq, f);
+  f32x4 e[4][NT];
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) e[I][nt] = zero4();
+#pragma unroll
+  for (int f = 0; f < NTRI; ++f) {
+    const int I = f < 4 ? f : f - 2, u = f < 4 ? 0 : 1;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) e[I][nt] = ebo[nt].mma1(ftb[f], u, e[I][nt]);
+  }
+  // Kend^T, first group, requested behind E's products
+  typename BT::frag fkt[2][CT / 2];
+#pragma unroll
+  for (int j = 0; j < CT / 2; ++j) fkt[0][j] = BT::load1(KtT + j * TILE_T, 0);
+  BT eo[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    f32x4 et[4];
+#pragma unroll
+    for (int I = 0; I < 4; ++I) et[I] = e[I][nt];
+    eo[nt].build(et);
+  }
+  // O = s Qbnd S^T + A E
+#pragma unroll
+  for (int I = 0; I < 4; ++I)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) ov[I][nt] = xb[I][nt];
+#pragma unroll
+  for (int f = 0; f < NTRI; ++f) {
+    const int I = f < 4 ? f : f - 2, u = f < 4 ? 0 : 1;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) ov[I][nt] = eo[nt].mma1(faq[f], u, ov[I][nt]);
+  }
+  // S^T = D_{0:63} S^T + Kend^T E, in four groups of four channel tiles x one
+  // slab, each group's fragments requested before the previous group's
+  // products issue
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const f32x4 p = *reinterpret_cast<const f32x4 *>(P63 + 16 * ct + 4 * g);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st[ct][nt][r] *= p[r];
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {           // group q: slab q / 2, channel tiles (q % 2) * 4 .. + 3
+    const int u = q >> 1, c0 = (q & 1) * (CT / 2);
+    if (q + 1 < 4) {
+      const int un = (q + 1) >> 1, cn = ((q + 1) & 1) * (CT / 2);
+#pragma unroll
+      for (int j = 0; j < CT / 2; ++j) fkt[(q + 1) & 1][j] = BT::load1(KtT + (cn + j) * TILE_T, un);
+    }
+#pragma unroll
+    for (int j = 0; j < CT / 2; ++j)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) st[c0 + j][nt] = eo[nt].mma1(fkt[q & 1][j], u, st[c0 + j][nt]);
+  }
+}
+
+// 4 bytes per lane from global memory into LDS (global_load_lds_dword; lane
+// l's bytes land at lds_base + 4 l).  Used only to pull lines into L2 ahead
+// of their copy: the LDS bytes are a landing place nothing reads.
+__device__ __forceinline__ void lds_dma4(const void *src, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
+}
+
+// eight compute waves of 16 columns and four copy waves: measured against
+// four waves of 32 columns (each fragment feeding two products, one wave per
+// SIMD) and eight waves that copy as well, which were 1.3-1.7x slower
+constexpr int kUnitCW = 8, kUnitCP = 4;
+// The two-phase schedule takes this scan above 64 units (the four-workgroup
+// scan's 256 workgroups fill the chip at 64 units; measured on the packed
+// batch of 1024 units, 274,797 tokens: a call of 3412 against 3766 us).
+constexpr int kUnitScanMinUnits = 64;
+
+// The scan, one workgroup per unit: CW compute waves and CP copy waves (none:
+// the compute waves issue the copies).  While the compute waves work on
+// chunk c, the copiers stream chunk c+1's record (61 KiB) and value rows (64
+// tokens x 128 columns) into the other half of double-buffered LDS, and touch
+// chunk c+2's value rows so those come from L2, not HBM, when copied.
+// Outputs go straight to o.  SCHED: the overlapped schedule (a unit per
+// ticket of this XCD; a record is copied once its ready bit is set, with a
+// bounded wait).
+template <bool SCHED, int CW, int CP>
+__global__ __launch_bounds__(64 * (CW + CP)) __attribute__((amdgpu_waves_per_eu((CW + CP + 3) / 4, (CW + CP + 3) / 4)))
+void unit_scan_kernel(ScanKArgs a) {
+  constexpr int DK = 128, DV = 128;
+  constexpr int NT = DV / 16 / CW;               // 16-column tiles per compute wave
+  constexpr int NCOPY = CP > 0 ? CP : CW;        // waves issuing copies
+  typedef bf16 E;
+  typedef RecordShape<DK, E> RS;
+  constexpr int CT = DK / 16;
+  constexpr int VROW = DV * (int)sizeof(E);      // bytes of one token's values
+  constexpr int VBYTES = 64 * VROW;               // one chunk's value rows
+  __shared__ __attribute__((aligned(1024))) char rec[2][RS::bytes];
+  __shared__ __attribute__((aligned(1024))) char vbuf[2][VBYTES];
+  __shared__ __attribute__((aligned(16))) char touch[256];
+
+  const int w = wave_id(), l = lane_id(), col = l & 15, g = l >> 4;
+  const int x = SCHED ? xcd_id() : 0;
+  int u;
+  if constexpr (SCHED) {
+    __shared__ int sTicket;
+    if (threadIdx.x == 0)
+      sTicket = __hip_atomic_fetch_add(a.ctl + kCtlScanNext + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    u = x + 8 * sTicket;
+  } else {
+    u = blockIdx.x;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      a.ctl[kCtlSchedule] = kScheduleTwoPhase;
+      a.ctl[kCtlError] = 0;
+    }
+  }
+  if (u >= a.n_units) return;
+  const int n = a.seq_order ? a.seq_order[u / a.H] : u / a.H, h = u % a.H;
+  const int H = a.H;
+  long long tstart, ntok, chunk0;
+  if (a.seq_tok0) {
+    tstart = a.seq_tok0[n];
+    ntok = a.seq_tok0[n + 1] - tstart;
+    chunk0 = a.seq_chunk0[n];
+  } else {
+    tstart = (long long)n * a.T;
+    ntok = a.T;
+    chunk0 = (long long)n * a.nct;
+  }
+  const int nchunks = (int)((ntok + kChunk - 1) / kChunk);
+  const E *V = reinterpret_cast<const E *>(a.v);
+  E *O = reinterpret_cast<E *>(a.o);
+  const size_t tok_stride = (size_t)H * DV;
+  const bool copier = CP == 0 || w >= CW;
+  const int cpi = CP == 0 ? w : w - CW;          // index among the copiers
+
+  // ------------------------------------------------------------ copies
+  // record: 1 KiB blocks cpi*QPW .. cpi*QPW + QPW - 1, clamped to the last
+  // block (a clamped block is copied twice with the same bytes)
+  auto copy_rec = [&](int ci, char *dst) {
+    const char *src = a.ws_records + ((size_t)(chunk0 + ci) * H + h) * RS::bytes + l * 16;
+    const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)dst;
+    constexpr int NQ = RS::bytes / 1024, QPW = (NQ + NCOPY - 1) / NCOPY;
+#pragma unroll
+    for (int qq = 0; qq < QPW; ++qq) {
+      const int q = min(cpi * QPW + qq, NQ - 1);
+      lds_dma16(src + q * 1024, lds + q * 1024);
+    }
+  };
+  // value rows: one copy moves four rows (16 lanes x 16 bytes per row); rows
+  // past the end of the sequence repeat its last token (their Tb rows and
+  // columns are zero, so they never reach a valid output)
+  auto copy_v = [&](int ci, char *dst) {
+    const long long t0 = tstart + (long long)kChunk * ci;
+    const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
+    const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)dst;
+    constexpr int PER = 64 / 4 / NCOPY;   // copies per copier
+#pragma unroll
+    for (int jj = 0; jj < PER; ++jj) {
+      const int j = cpi * PER + jj, row = 4 * j + (l >> 4);
+      const E *src = V + (size_t)(t0 + min(row, L - 1)) * tok_stride + (size_t)h * DV + (l & 15) * 8;
+      lds_dma16_nt(src, lds + j * 1024);
+    }
+  };
+  // chunk ci's value rows into L2: copiers 0 and 1, one 4-byte load per
+  // 128-byte line (32 rows x 2 lines each)
+  const bool toucher = copier && cpi < 2;
+  const uint32_t touch_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)touch;
+  auto touch_v = [&](int ci) {
+    const long long t0 = tstart + (long long)kChunk * ci;
+    const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
+    const int row = 32 * cpi + (l >> 1);
+    const char *src = reinterpret_cast<const char *>(V + (size_t)(t0 + min(row, L - 1)) * tok_stride +
+                                                     (size_t)h * DV) + (l & 1) * 128;
+    lds_dma4(src, touch_lds);
+  };
+  unsigned known = 0;
+  int known_word = -1;
+  bool gave_up = false;
+  auto wait_rec = [&](int ci) {
+    if constexpr (SCHED) {
+      const int wd = ci >> 5;
+      const unsigned bit = 1u << (ci & 31);
+      if (wd != known_word) {
+        known_word = wd;
+        known = 0;
+      }
+      if ((known & bit) || gave_up) return;
+      if (a.wait_ticks <= 0) {
+        if (l == 0) __hip_atomic_fetch_or(a.ctl + kCtlError, kSchedErrTimeout, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        gave_up = true;
+        return;
+      }
+      const int *word = a.ready + (size_t)u * a.ready_words + wd;
+      const unsigned long long t0 = __builtin_amdgcn_s_memrealtime();
+      for (;;) {
+        unsigned v = 0;
+        if (l == 0) v = (unsigned)__hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        known = __builtin_amdgcn_readfirstlane(v);
+        if (known & bit) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > (unsigned long long)a.wait_ticks) {
+          if (l == 0) __hip_atomic_fetch_or(a.ctl + kCtlError, kSchedErrTimeout, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+          gave_up = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+  };
+  // chunk ci's copies (and the touch of chunk ci + 1's value rows); returns
+  // the loads issued after the copies (the touch, which nothing waits for)
+  auto issue_copies = [&](int ci) {
+    if (!copier) return 0;
+    wait_rec(ci);
+    copy_rec(ci, rec[ci & 1]);
+    copy_v(ci, vbuf[ci & 1]);
+    if (toucher && ci + 1 < nchunks) {
+      touch_v(ci + 1);
+      return 1;
+    }
+    return 0;
+  };
+  // this wave's copies have landed (a touch issued after them may still fly)
+  auto wait_copies = [&](int touched) {
+    if (touched) wait_vmcnt<1>();
+    else wait_vmcnt<0>();
+  };
+
+  if constexpr (CP > 0) {
+    if (copier) {
+      int touched = nchunks > 0 ? issue_copies(0) : 0;
+      wait_copies(touched);
+      __syncthreads();  // chunk 0 ready
+      for (int ci = 0; ci < nchunks; ++ci) {
+        touched = ci + 1 < nchunks ? issue_copies(ci + 1) : 0;
+        wait_copies(touched);
+        __syncthreads();  // chunk ci done, chunk ci+1 ready
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      return;
+    }
+  }
+
+  // ------------------------------------------------------------ compute
+  const int v0 = w * 16 * NT;
+  const size_t sbase = ((size_t)n * H + h) * DV * DK + (size_t)(v0 + col) * DK;
+  f32x4 st[CT][NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      st[ct][nt] = a.S0 ? *reinterpret_cast<const f32x4 *>(a.S0 + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g)
+                        : zero4();
+
+  // outputs of chunk ci straight to o: the buffer descriptor covers exactly
+  // the chunk's valid rows, so rows past the end of the sequence are dropped
+  // by the hardware (the whole offset goes in the VGPR operand: the range
+  // check of a raw buffer access does not include soffset); nontemporal
+  auto store_o = [&](int ci, f32x4 (*ov)[NT]) {
+    const long long t0 = tstart + (long long)kChunk * ci;
+    const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        O + (size_t)t0 * tok_stride, 0, (int)((size_t)L * tok_stride * sizeof(E)), 0x00020000);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const int o_lane = (int)(((size_t)(4 * g) * tok_stride + (size_t)h * DV + v0 + 16 * nt + col) * sizeof(E));
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row_off = (int)((size_t)(16 * I + r) * tok_stride * sizeof(E));
+          const float xv = ov[I][nt][r];  // copied out of the vector before the bit cast
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, from_f<E>(xv)), rs,
+                                                o_lane + row_off, 0, 2);
+        }
+    }
+  };
+
+  int touched = (CP == 0 && nchunks > 0) ? issue_copies(0) : 0;
+  if (CP == 0) wait_copies(touched);
+  __syncthreads();  // chunk 0 ready
+  f32x4 ov[4][NT];
+  for (int ci = 0; ci < nchunks; ++ci) {
+    // buffers (ci+1) % 2 held chunk ci-1, finished before the last barrier
+    touched = (CP == 0 && ci + 1 < nchunks) ? issue_copies(ci + 1) : 0;
+    const char *recb = rec[ci & 1];
+    if constexpr (SCHED) {
+      // the record must come from this XCD's prep workers (stamped by them)
+      static_assert(RS::p63 + DK * 4 + 4 <= RS::bytes, "room for the XCD stamp");
+      if (w == 0 && l == 0 && *reinterpret_cast<const int *>(recb + RS::p63 + DK * 4) != x)
+        __hip_atomic_fetch_or(a.ctl + kCtlError, kSchedErrXcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    scan_chunk_lean<DK, E, NT, DV>(recb, reinterpret_cast<const E *>(vbuf[ci & 1]) + v0, st, ov);
+    store_o(ci, ov);
+    if (CP == 0) wait_copies(touched);
+    __syncthreads();  // chunk ci done, chunk ci+1 ready
+  }
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
+}
+
 // Zeroes the control words and the ready words of the overlapped schedule
 // and records that schedule as the one this call runs.
 __global__ void sched_clear_kernel(int *ctl, int *ready, int n_ready) {
@@ -1562,12 +1977,12 @@ void launch_scan(int cw, dim3 grid, hipStream_t stream, const ScanKArgs &sa) {
 
 // ================================================================ dispatch
 // CU-masked streams of the overlapped schedule, one set per device: the scan
-// on the first 128 CUs of the runtime's mask numbering (16 on each XCD) and
-// the prep on the next 112 (14 on each XCD), so neither can hold the CUs the
-// other needs.  The last 16 CUs stay idle: on a 1024-chunk chain the prep,
-// which finishes well before the scan, slowed the scan less on 112 CUs (a
-// call of 1833-1839 us) than on 128 (1985 us) or 96 (1852 us); on 80 it
-// became the bound (2441 us).
+// on the first 128 CUs of the runtime's mask numbering (16 per XCD) and the
+// prep on the next 112 (14 per XCD), so neither can hold the CUs the other
+// needs.  The last 16 CUs stay idle: on a 1024-chunk chain the prep, which
+// finishes well before the scan, slowed the scan less on 112 CUs (a call of
+// 1833-1839 us) than on 128 (1985 us) or 96 (1852 us); on 80 it became the
+// bound (2441 us).
 // Created on the first overlapped call on a device; released by
 // kda_release() (also run at process exit, before the HIP runtime and any
 // profiler attached to it are torn down: streams still alive at that point
@@ -1645,10 +2060,11 @@ template <int DK, typename E> bool overlap_supported(const PrefillArgs &a) {
 // d_v = 128) to fit on its 128 CUs, and it pays once the batch holds at least
 // 4096 chunk records (256 MB at d = 128, the size of the Infinity Cache):
 // the two-phase scan then fetches its records from HBM while the overlapped
-// one reads them soon after they are written, and the fork and join (about
-// 50 us) are amortised.  Measured (two-phase / overlap, us): 8 units x 256
-// chunks 300 / 380, 8 x 512 800 / 759, 16 x 192 293 / 336, 16 x 256 477 /
-// 419, 32 x 128 310 / 315, 32 x 192 473 / 416, 32 x 1024 2430 / 1800.
+// one reads them soon after they are written, and the fork and join of the
+// two streams (about 24 us, measured with empty kernels) are amortised.
+// Measured (two-phase / overlap, us): 8 units x 256 chunks 300 / 380, 8 x 512
+// 800 / 759, 16 x 192 293 / 336, 16 x 256 477 / 419, 32 x 128 310 / 315,
+// 32 x 192 473 / 416, 32 x 1024 2430 / 1800.
 constexpr long long kOverlapMinRecords = 4096;
 bool overlap_chosen(const PrefillArgs &a, int nct) {
   if (a.schedule == kScheduleTwoPhase) return false;
@@ -1797,12 +2213,20 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     // (which halves the LDS reads per column but doubles each wave's serial
     // chain of products) and against one, two, three, five and six copy
     // waves.
-    int cw = a.dv >= 32 ? 2 : 1;
-    while (cw > 1 && !scan_stage_fits<DK, E>(1, cw)) cw /= 2;
-    sa.wg_per_unit = a.dv / (16 * cw);
-    const long long slots = ((long long)sa.n_units + 7) / 8 * 8 * sa.wg_per_unit;
-    const dim3 grid((unsigned)slots);
-    launch_scan<DK, E, 1, 4>(cw, grid, stream, sa);
+    if (DK == 128 && sizeof(E) == 2 && a.dv == 128 && sa.n_units > kUnitScanMinUnits) {
+      // one workgroup per unit (units in dispatch order: longest packed
+      // sequences first)
+      sa.wg_per_unit = 1;
+      hipLaunchKernelGGL((unit_scan_kernel<false, kUnitCW, kUnitCP>), dim3((unsigned)sa.n_units),
+                         dim3(64 * (kUnitCW + kUnitCP)), 0, stream, sa);
+    } else {
+      int cw = a.dv >= 32 ? 2 : 1;
+      while (cw > 1 && !scan_stage_fits<DK, E>(1, cw)) cw /= 2;
+      sa.wg_per_unit = a.dv / (16 * cw);
+      const long long slots = ((long long)sa.n_units + 7) / 8 * 8 * sa.wg_per_unit;
+      const dim3 grid((unsigned)slots);
+      launch_scan<DK, E, 1, 4>(cw, grid, stream, sa);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

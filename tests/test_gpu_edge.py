@@ -191,3 +191,26 @@ def test_deterministic():
     o1, S1 = gpu_prefill(inp)
     o2, S2 = gpu_prefill(inp)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("B,T,H", [(5, 130, 16), (1, 700, 72)])
+def test_many_units_one_cu_scan(B, T, H):
+    """Batches of more than 64 (sequence, head) units at d = 128 bf16 run the
+    two-phase scan with one workgroup per unit: ragged lengths, S0, against
+    the oracle per unit; then bitwise equal to the same units run 64 at a
+    time (the four-workgroup scan)."""
+    announce(f"many units (one-CU scan): dense B{B} T{T} H{H} d128 bf16 with S0")
+    inp = _dense(B, T, H, 128, 128, BF16, seed=B * 100 + H, s0=0.02)
+    o, S = gpu_prefill(inp)
+    o_ref, S_ref = oracle_prefill(inp)
+    check("o", o, o_ref, TOL[BF16])
+    check("S_final", S, S_ref, TOL[BF16])
+    # the same arithmetic through the four-workgroup scan: split the heads so
+    # each call has at most 64 units
+    hs = max(1, 64 // B)
+    for h0 in range(0, H, hs):
+        sl = slice(h0, min(H, h0 + hs))
+        part = {key: inp[key][:, :, sl].contiguous() for key in ("q", "k", "v", "alpha", "beta")}
+        part["S0"] = inp["S0"][:, sl].contiguous()
+        o_p, S_p = gpu_prefill(part)
+        assert torch.equal(o_p, o[:, :, sl]) and torch.equal(S_p, S[:, sl]), f"heads {h0}.. differ"
