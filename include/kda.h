@@ -325,6 +325,62 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v,
                             size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The operations around the method in a KDA block, fused into the prefill
+ * (page "K3 架构图解": chapter 08, "KDA 与 MLA 如何混合", figure caption:
+ * the KDA module holds a short convolution, a normalisation and an output
+ * gate besides the recurrence; chapter 09: the short convolution, like the
+ * recurrence, depends on token order, so it is causal; chapter 05, section
+ * on the extra norm: RMSNorm(u) = gamma * u / sqrt(mean(u^2) + eps);
+ * chapter 07: a per-coordinate gate on the concatenated head outputs before
+ * the output projection).  Every member is optional (NULL: that operation
+ * is not applied).
+ *
+ *  conv_q, conv_k  [H, d_k, 4] fp32   conv_v  [H, d_v, 4] fp32
+ *      Short convolution: all three, or none.  Channel c of head h of q (k,
+ *      v) at token t becomes  sum_{i=0..3} w[h][c][i] * x[t-3+i]  over the
+ *      token and the three before it in its own sequence (tokens before the
+ *      sequence's first count as zero: no convolution state flows in from a
+ *      previous call), rounded to dtype.  Requires KDA_ACT_QK_SILU_L2NORM,
+ *      which then applies to the convolved q and k; v gets no activation.
+ *      Runs the two-phase schedule.
+ *  norm_weight  [d_v] fp32, norm_eps
+ *      RMS norm of each output row (token, head) over its d_v values, with
+ *      gains norm_weight shared by the heads:  o <- o / sqrt(mean(o^2) +
+ *      norm_eps) * norm_weight.
+ *  out_gate  same layout and dtype as o
+ *      Output gate:  o <- o * sigmoid(out_gate)  elementwise (after the norm
+ *      when both are given).
+ * The norm and gate run in fp32 on the outputs as rounded to dtype, and
+ * round once more.  In a packed batch, rows of o outside every sequence are
+ * left alone.
+ */
+typedef struct {
+  const float *conv_q, *conv_k, *conv_v;
+  const float *norm_weight;
+  float norm_eps;
+  const void *out_gate;
+} kda_module_ops;
+
+/*
+ * kda_chunk_fwd_ex with the operations of kda_module_ops (ops may be NULL:
+ * then this is kda_chunk_fwd_ex).  Returns KDA_ERR_NULL_ARG when only some
+ * of the three convolution weights are given, KDA_ERR_UNSUPPORTED_ACT when
+ * they are given without KDA_ACT_QK_SILU_L2NORM, KDA_ERR_MISALIGNED for a
+ * weight or gate pointer not 16-byte aligned, KDA_ERR_BAD_SHAPE for a
+ * negative or NaN norm_eps, and KDA_ERR_ALIAS when o overlaps a weight or
+ * the gate.  Everything else as for kda_chunk_fwd.
+ */
+kda_status kda_chunk_fwd_module(const void *q, const void *k, const void *v,
+                                const float *alpha, kda_gate gate,
+                                const float *beta, unsigned input_act,
+                                const kda_module_ops *ops, const float *S0,
+                                const int32_t *cu_seqlens, int N, int B, int T,
+                                int H, int d_k, int d_v, float scale,
+                                kda_dtype dtype, void *o, float *S_final,
+                                void *workspace, size_t workspace_bytes,
+                                hipStream_t stream);
+
+/*
  * kda_chunk_fwd_ex for callers that cannot allocate device memory: code
  * being captured into a HIP graph, tight serving loops, harnesses that
  * forbid allocation.  It takes no workspace: the kernels run on a static

@@ -51,11 +51,17 @@ KDA_SCHED_ERR_XCD = 2
 EXPORTED = ("kda_status_string", "kda_set_validation", "kda_set_schedule", "kda_chunk_fwd_status",
             "kda_release", "kda_set_sched_wait_limit", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_decode_step", "kda_decode_step_gated",
-            "kda_decode_tokens", "kda_decode_tokens_ex", "kda_chunk_fwd_noalloc")
+            "kda_decode_tokens", "kda_decode_tokens_ex", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_module")
 KDA_ERR_INVALID_VALUE = 11
 KDA_ERR_STREAM_CAPTURE = 13
 KDA_ERR_TOO_LARGE = 14
 NOALLOC_SCRATCH_BYTES = 64 << 20   # the static device scratch of kda_chunk_fwd_noalloc
+
+
+class KdaModuleOps(ctypes.Structure):
+    """kda_module_ops: device pointers (None: operation off) and the norm's eps."""
+    _fields_ = [("conv_q", ctypes.c_void_p), ("conv_k", ctypes.c_void_p), ("conv_v", ctypes.c_void_p),
+                ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("out_gate", ctypes.c_void_p)]
 
 
 class KdaError(RuntimeError):
@@ -105,6 +111,9 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_noalloc.restype = i32
     lib.kda_chunk_fwd_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_uint, vp, vp, i32, i32, i32, i32, i32,
                                           i32, f32, i32, vp, vp, vp]
+    lib.kda_chunk_fwd_module.restype = i32
+    lib.kda_chunk_fwd_module.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_uint, ctypes.POINTER(KdaModuleOps), vp,
+                                         vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
     lib.kda_release.restype = None
     lib.kda_release.argtypes = []
     lib.kda_set_sched_wait_limit.restype = ctypes.c_longlong
@@ -224,11 +233,18 @@ def chunk_fwd_noalloc(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None
 
 
 def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gate=None, out=None,
-              S_final=None, workspace=None, act=0, _noalloc=False):
+              S_final=None, workspace=None, act=0, conv=None, norm_weight=None, norm_eps=1e-6, out_gate=None,
+              _noalloc=False):
     """Chunked prefill.  Returns (o, S_final).
 
     ``act``: kda_input_act flags (KDA_ACT_QK_SILU_L2NORM, KDA_ACT_BETA_SIGMOID)
     applied to the raw q, k and beta as the kernels load them.
+    Module operations (kda_module_ops; any given selects
+    kda_chunk_fwd_module): ``conv`` = (w_q, w_k, w_v), fp32 taps [H, d_k, 4],
+    [H, d_k, 4], [H, d_v, 4] of the short causal convolution (needs
+    KDA_ACT_QK_SILU_L2NORM in ``act``); ``norm_weight`` [d_v] fp32 gains of the
+    output RMS norm (with ``norm_eps``); ``out_gate`` logits of the output gate,
+    shaped and typed like the output.
     Dense batch: q, k [B, T, H, d_k]; v [B, T, H, d_v]; beta [B, T, H].
     alpha: [B, T, H, d_k] (gate "channel"), [B, T, H] (gate "scalar"), or
     None (gate "none"); ``gate`` defaults to what alpha's shape says.
@@ -287,12 +303,31 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gat
     ws_need = chunk_fwd_workspace_size(B, T, H, d_k, d_v, N if cu_seqlens is not None else -1, dt)
     if workspace is None or workspace.numel() < ws_need:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
-    st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), int(act), _ptr(S0),
-                              _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
-                              float(scale) if scale else 0.0, dt, _ptr(out), _ptr(S_final),
-                              _ptr(workspace), workspace.numel(), _stream(dev))
-    if st != 0:
-        raise KdaError("kda_chunk_fwd_ex", st)
+    if conv is not None or norm_weight is not None or out_gate is not None:
+        wq, wk, wv = map(_prep, conv) if conv is not None else (None, None, None)
+        for w, d in ((wq, d_k), (wk, d_k), (wv, d_v)):
+            if w is not None and (w.dtype != torch.float32 or w.numel() != H * d * 4):
+                raise ValueError("convolution taps must be float32 [H, d, 4]")
+        norm_weight = _prep(norm_weight)
+        if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d_v):
+            raise ValueError("norm_weight must be float32 [d_v]")
+        out_gate = _prep(out_gate)
+        if out_gate is not None and (out_gate.dtype != v.dtype or out_gate.numel() != v.numel()):
+            raise ValueError("out_gate must have the dtype and size of the output")
+        ops = KdaModuleOps(_ptr(wq), _ptr(wk), _ptr(wv), _ptr(norm_weight), float(norm_eps), _ptr(out_gate))
+        st = lib.kda_chunk_fwd_module(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), int(act),
+                                      ctypes.byref(ops), _ptr(S0), _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
+                                      float(scale) if scale else 0.0, dt, _ptr(out), _ptr(S_final),
+                                      _ptr(workspace), workspace.numel(), _stream(dev))
+        if st != 0:
+            raise KdaError("kda_chunk_fwd_module", st)
+    else:
+        st = lib.kda_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), int(act), _ptr(S0),
+                                  _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
+                                  float(scale) if scale else 0.0, dt, _ptr(out), _ptr(S_final),
+                                  _ptr(workspace), workspace.numel(), _stream(dev))
+        if st != 0:
+            raise KdaError("kda_chunk_fwd_ex", st)
     if validation_enabled():
         # with value checks on the call has already waited for the device;
         # a schedule error (a record wait that gave up) means wrong results

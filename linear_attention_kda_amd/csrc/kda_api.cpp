@@ -148,18 +148,26 @@ kda_status chunk_fwd_scratch(const void *q, const void *k, const void *v, const 
   return KDA_OK;
 }
 
-// kda_chunk_fwd_ex, and with noalloc its variant on the library's static
-// scratch (kda_chunk_fwd_noalloc; workspace is then ignored).
+// kda_chunk_fwd_module (ops may be null), and with noalloc the variant of
+// kda_chunk_fwd_ex on the library's static scratch (kda_chunk_fwd_noalloc;
+// workspace and ops are then ignored).
 kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
-                          const float *beta, unsigned input_act, const float *S0, const int32_t *cu_seqlens, int N,
-                          int B, int T, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
-                          float *S_final, void *workspace, size_t workspace_bytes, hipStream_t stream, bool noalloc) {
+                          const float *beta, unsigned input_act, const kda_module_ops *ops, const float *S0,
+                          const int32_t *cu_seqlens, int N, int B, int T, int H, int d_k, int d_v, float scale,
+                          kda_dtype dtype, void *o, float *S_final, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream, bool noalloc) {
   if (noalloc) {
     workspace = nullptr;
     workspace_bytes = 0;
+    ops = nullptr;
   }
+  const kda_module_ops mo = ops ? *ops : kda_module_ops{nullptr, nullptr, nullptr, nullptr, 0.f, nullptr};
+  const bool conv = mo.conv_q || mo.conv_k || mo.conv_v;
   if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
   if (input_act & ~kActAll) return KDA_ERR_UNSUPPORTED_ACT;
+  if (conv && !(mo.conv_q && mo.conv_k && mo.conv_v)) return KDA_ERR_NULL_ARG;
+  if (conv && !(input_act & KDA_ACT_QK_SILU_L2NORM)) return KDA_ERR_UNSUPPORTED_ACT;
+  if (mo.norm_weight && !(mo.norm_eps >= 0.f)) return KDA_ERR_BAD_SHAPE;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
   if (B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
@@ -181,7 +189,8 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
   if (ntok > 0 && (!q || !k || !v || (a_bytes && !alpha) || !beta || !o)) return KDA_ERR_NULL_ARG;
   if (s_bytes > 0 && !S_final) return KDA_ERR_NULL_ARG;
   if (ntok > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
-  const void *ptrs[] = {q, k, v, alpha, beta, S0, cu_seqlens, o, S_final, workspace};
+  const void *ptrs[] = {q,  k,         v, alpha, beta, S0, cu_seqlens, o, S_final, workspace, mo.conv_q, mo.conv_k,
+                        mo.conv_v, mo.norm_weight, mo.out_gate};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
 
@@ -193,10 +202,16 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
     // other and from every input; S_final may only be S0 itself (in place).
     const Range ro = range_of(o, ntok > 0 ? ntok * H * d_v * es : 0);
     const Range rs = range_of(S_final, s_bytes), rw = range_of(workspace, noalloc ? 0 : plan.total);
+    const size_t wq_bytes = (size_t)H * d_k * kda::kConvTaps * sizeof(float);
+    const size_t wv_bytes = (size_t)H * d_v * kda::kConvTaps * sizeof(float);
     const Range ins[] = {range_of(q, ntok > 0 ? qk_bytes : 0), range_of(k, ntok > 0 ? qk_bytes : 0),
                          range_of(v, ntok > 0 ? v_bytes : 0), range_of(alpha, alpha && ntok > 0 ? a_bytes : 0),
                          range_of(beta, ntok > 0 ? b_bytes : 0),
-                         range_of(cu_seqlens, packed ? ((size_t)N + 1) * sizeof(int32_t) : 0)};
+                         range_of(cu_seqlens, packed ? ((size_t)N + 1) * sizeof(int32_t) : 0),
+                         range_of(mo.conv_q, mo.conv_q ? wq_bytes : 0), range_of(mo.conv_k, mo.conv_k ? wq_bytes : 0),
+                         range_of(mo.conv_v, mo.conv_v ? wv_bytes : 0),
+                         range_of(mo.norm_weight, mo.norm_weight ? (size_t)d_v * sizeof(float) : 0),
+                         range_of(mo.out_gate, mo.out_gate && ntok > 0 ? v_bytes : 0)};
     for (const Range &r : ins)
       if (overlaps(ro, r) || overlaps(rs, r) || overlaps(rw, r)) return KDA_ERR_ALIAS;
     const Range rs0 = range_of(S0, S0 ? s_bytes : 0);
@@ -212,7 +227,7 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
                                          ntok * H, d_k, dtype, cu_seqlens, N, T, stream))
     return st;
 
-  kda::PrefillArgs a;
+  kda::PrefillArgs a{};
   a.schedule = g_schedule.load(std::memory_order_relaxed);
   a.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
   a.q = q;
@@ -235,6 +250,14 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
   a.dv = d_v;
   a.scale = default_scale(scale, d_k);
   a.bf16 = dtype == KDA_BF16;
+  if (conv) {
+    a.conv_q = mo.conv_q;
+    a.conv_k = mo.conv_k;
+    a.conv_v = mo.conv_v;
+  }
+  a.norm_w = mo.norm_weight;
+  a.norm_eps = mo.norm_eps;
+  a.out_gate = mo.out_gate;
   return kda::launch_prefill(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
@@ -330,16 +353,25 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v, const f
                             const float *beta, unsigned input_act, const float *S0, const int32_t *cu_seqlens, int N,
                             int B, int T, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
                             float *S_final, void *workspace, size_t workspace_bytes, hipStream_t stream) {
-  return chunk_fwd_impl(q, k, v, alpha, gate, beta, input_act, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale, dtype, o,
-                        S_final, workspace, workspace_bytes, stream, false);
+  return chunk_fwd_impl(q, k, v, alpha, gate, beta, input_act, nullptr, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale,
+                        dtype, o, S_final, workspace, workspace_bytes, stream, false);
+}
+
+kda_status kda_chunk_fwd_module(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                                const float *beta, unsigned input_act, const kda_module_ops *ops, const float *S0,
+                                const int32_t *cu_seqlens, int N, int B, int T, int H, int d_k, int d_v, float scale,
+                                kda_dtype dtype, void *o, float *S_final, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  return chunk_fwd_impl(q, k, v, alpha, gate, beta, input_act, ops, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale,
+                        dtype, o, S_final, workspace, workspace_bytes, stream, false);
 }
 
 kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
                                  const float *beta, unsigned input_act, const float *S0, const int32_t *cu_seqlens,
                                  int N, int B, int T, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
                                  float *S_final, hipStream_t stream) {
-  return chunk_fwd_impl(q, k, v, alpha, gate, beta, input_act, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale, dtype, o,
-                        S_final, nullptr, 0, stream, true);
+  return chunk_fwd_impl(q, k, v, alpha, gate, beta, input_act, nullptr, S0, cu_seqlens, N, B, T, H, d_k, d_v, scale,
+                        dtype, o, S_final, nullptr, 0, stream, true);
 }
 
 kda_status kda_decode_step(const void *q, const void *k, const void *v, const float *alpha, const float *beta,

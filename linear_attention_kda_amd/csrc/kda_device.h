@@ -125,4 +125,14 @@ __device__ __forceinline__ f32x4 mma_rows(const E *a_row, const E *bt_row, f32x4
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// One output of a causal convolution of width four: taps w[0..3] on the
+// values of tokens t-3 .. t, summed in that order (one product, then three
+// fused multiply-adds; every caller that must agree bit for bit uses this).
+__device__ __forceinline__ float conv_taps(const f32x4 &w, float x0, float x1, float x2, float x3) {
+  float y = w[0] * x0;
+  y = __builtin_fmaf(w[1], x1, y);
+  y = __builtin_fmaf(w[2], x2, y);
+  return __builtin_fmaf(w[3], x3, y);
+}
+
 }  // namespace kda

@@ -71,7 +71,7 @@ struct WorkspacePlan {
   size_t ready_bytes;  // one int32 per record slot, 0 for packed batches
   size_t total;
   // int32 table offsets (in elements from `tables`), packed only
-  size_t seq_tok0, seq_chunk0, chunk_t0, chunk_len, seq_order;
+  size_t seq_tok0, seq_chunk0, chunk_t0, chunk_len, chunk_s0, seq_order;
 };
 
 inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
@@ -87,7 +87,8 @@ inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
     P.seq_chunk0 = P.seq_tok0 + (size_t)N + 1;
     P.chunk_t0 = P.seq_chunk0 + (size_t)N + 1;
     P.chunk_len = P.chunk_t0 + (size_t)P.max_chunks;
-    P.seq_order = P.chunk_len + (size_t)P.max_chunks;
+    P.chunk_s0 = P.chunk_len + (size_t)P.max_chunks;
+    P.seq_order = P.chunk_s0 + (size_t)P.max_chunks;
     size_t n_int = P.seq_order + (size_t)N;
     P.tables_bytes = (n_int * sizeof(int32_t) + 255) / 256 * 256;
   } else {
@@ -118,6 +119,10 @@ constexpr bool gate_is_softplus(int g) { return g == kGateSoftplusChannel || g =
 constexpr unsigned kActQK = 1;    // q, k <- L2-normalised SiLU, per token and head
 constexpr unsigned kActBeta = 2;  // beta <- sigmoid(beta)
 
+// Short causal convolution of q, k and v (kda_module_ops): this many taps
+// per channel, the last one on the current token.
+constexpr int kConvTaps = 4;
+
 // Prefill schedules (kda_set_schedule): automatic, always prep then scan, or
 // prep and scan overlapped whenever the shapes allow it.
 constexpr int kScheduleAuto = 0, kScheduleTwoPhase = 1, kScheduleOverlap = 2;
@@ -141,6 +146,14 @@ struct PrefillArgs {
   int B, T, H, dk, dv;
   float scale;
   bool bf16;
+  // module operations around the method (kda_module_ops), all optional:
+  // depthwise causal convolution taps [H, d, kConvTaps] of q, k and v (all
+  // three or none), and the output's RMS norm gains [d_v] and gate logits
+  // (same layout and type as o)
+  const float *conv_q, *conv_k, *conv_v;
+  const float *norm_w;
+  const void *out_gate;
+  float norm_eps;
 };
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);

@@ -49,7 +49,7 @@ namespace {
 // token index used later stays inside the buffers even for malformed input.
 __global__ __launch_bounds__(1024) void varlen_index_kernel(
     const int32_t *__restrict__ cu, int N, int T, int32_t *seq_tok0,
-    int32_t *seq_chunk0, int32_t *chunk_t0, int32_t *chunk_len,
+    int32_t *seq_chunk0, int32_t *chunk_t0, int32_t *chunk_len, int32_t *chunk_s0,
     long long max_chunks, int32_t *seq_order) {
   __shared__ int32_t s[1024];
   const int tid = threadIdx.x;
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(1024) void varlen_index_kernel(
         if (c < max_chunks) {
           chunk_t0[c] = e_prev + kChunk * j;
           chunk_len[c] = min(kChunk, e - e_prev - kChunk * j);
+          chunk_s0[c] = e_prev;  // the sequence's first token
         }
       }
     }
@@ -129,19 +130,23 @@ struct ChunkSource {
   // dense batch: sequence n starts at token n*T, nct chunks per sequence
   int T, nct;
   // packed batch (device tables; null for dense)
-  const int32_t *chunk_t0, *chunk_len, *seq_chunk0;
+  const int32_t *chunk_t0, *chunk_len, *chunk_s0, *seq_chunk0;
   int n_seq;
 };
 
+// Chunk slot c: its first token t0, its length L and the first token s0 of
+// its sequence; false for a slot past the last chunk.
 __device__ __forceinline__ bool chunk_span(const ChunkSource &cs, long long c,
-                                           long long &t0, int &L) {
+                                           long long &t0, int &L, long long &s0) {
   if (cs.chunk_t0) {
     if (c >= cs.seq_chunk0[cs.n_seq]) return false;
     t0 = cs.chunk_t0[c];
     L = cs.chunk_len[c];
+    s0 = cs.chunk_s0[c];
   } else {
     const long long n = c / cs.nct, ci = c % cs.nct;
-    t0 = n * cs.T + ci * kChunk;
+    s0 = n * cs.T;
+    t0 = s0 + ci * kChunk;
     L = (int)min((long long)kChunk, (long long)cs.T - ci * kChunk);
   }
   return true;
@@ -214,6 +219,12 @@ struct PrepKArgs {
   // unit), the control words (kCtlWords) and the number of units
   int *ready, *ctl;
   int ready_words, n_units;
+  // short convolution (CONV instantiations only): taps [H, d, kConvTaps] of
+  // q, k and v; v [.., H, dv] is read and its convolution written to o
+  const float *conv_q, *conv_k, *conv_v;
+  const void *v;
+  void *o;
+  int dv;
 };
 
 // Index of the XCD (accelerator complex die) this wave runs on, 0..7.  Each
@@ -331,6 +342,17 @@ template <int GATE> __device__ __forceinline__ float gate_value(float x) {
   else return x;
 }
 
+// Sixteen bytes of E as one vector.
+template <typename E> struct Row16;
+template <> struct Row16<bf16> {
+  typedef bf16x8 vec;
+  static constexpr int N = 8;
+};
+template <> struct Row16<float> {
+  typedef f32x4 vec;
+  static constexpr int N = 4;
+};
+
 // Four elements of E from / to fp32.
 template <typename E> struct Four;
 template <> struct Four<bf16> {
@@ -417,7 +439,16 @@ __device__ __forceinline__ void tile_ij(int p, int &I, int &J) {
 // Exact path (a chunk with some D_{0:63} below 2^-100, e.g. a gate of 0):
 // no division at all.  Kbnd and Qbnd as above, Kend from suffix products, and
 // R and A summed channel by channel with running products of the gates.
-template <int DK, typename E, int GATE, bool ACTQK, bool SCHED = false>
+//
+// CONV (with ACTQK, two-phase schedule only): q, k and v first go through a
+// depthwise causal convolution over the token and the three before it, within
+// the sequence (tokens before its first count as zero), each result rounded
+// to E.  q and k are convolved as they are loaded (the three tokens before
+// the chunk are read from the previous chunk's rows of the raw input); v's
+// convolution is written to o, from where the scan reads it in place of v
+// (the scan reads the rows of a chunk before it writes that chunk's outputs
+// over them).
+template <int DK, typename E, int GATE, bool ACTQK, bool SCHED = false, bool CONV = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrepKArgs a) {
   typedef LdsFrag<E, DK, 64> LK;   // Kbnd, Qbnd, k / a: rows = tokens, K = d_k
   typedef LdsFrag<E, 64, DK> LT;   // Kend^T: rows = channels, K = tokens
@@ -436,11 +467,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   __shared__ float sBeta[kChunk];
   __shared__ float sInvNorm[2][kChunk];  // 1/|SiLU(k)|, 1/|SiLU(q)| per token (input activation only)
 
+  static_assert(!CONV || (ACTQK && !SCHED), "the convolution comes with the q, k activation, two-phase");
   // one record: chunk slot c, head h
   auto prep_one = [&](const long long c, const int h) {
-    long long t0;
+    long long t0, s0;
     int L;
-    if (!chunk_span(a.src, c, t0, L)) return;
+    if (!chunk_span(a.src, c, t0, L, s0)) return;
 
     char *rec = a.ws_records + ((size_t)c * a.H + h) * a.lay.bytes;
     const int tid = threadIdx.x, w = wave_id(), l = lane_id();
@@ -470,6 +502,55 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         for (int j = 0; j < 4; ++j) al[j] = x;
       }
     };
+    const int tb0 = 16 * w + TPL * th;   // first token of this lane
+    // CONV: four channels ch.. of token `rel` of the chunk (rel <= L - 1,
+    // may be negative) after the convolution, rounded to E
+    auto conv_load4 = [&](const E *x, const float *w, int rel, int ch, float *out) {
+      f32x4 wt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wt[j] = *reinterpret_cast<const f32x4 *>(w + ((size_t)h * DK + ch + j) * kConvTaps);
+      float xs[kConvTaps][4];
+#pragma unroll
+      for (int i = 0; i < kConvTaps; ++i) {
+        const int r = rel - (kConvTaps - 1) + i;
+        const bool ok = t0 + r >= s0;
+        F4::load(x + (size_t)(t0 + (ok ? r : 0)) * hs + (size_t)h * DK + ch, xs[i]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xs[i][j] = ok ? xs[i][j] : 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) out[j] = (float)(E)conv_taps(wt[j], xs[0][j], xs[1][j], xs[2][j], xs[3][j]);
+    };
+    // CONV: this lane's TPL tokens (channels c0..c0+3) after the convolution,
+    // from the TPL + 3 rows ending at its last token, packed in E
+    auto conv_lane = [&](const E *x, const float *w, typename F4::vec *out) {
+      constexpr int NW = TPL + kConvTaps - 1;
+      typename F4::vec win[NW];
+      unsigned okm = 0;
+#pragma unroll
+      for (int i = 0; i < NW; ++i) {
+        const int rel = min(tb0 - (kConvTaps - 1) + i, L - 1);
+        const bool ok = t0 + rel >= s0;
+        okm |= (unsigned)ok << i;
+        win[i] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(
+            x + (size_t)(t0 + (ok ? rel : 0)) * hs + (size_t)h * DK + c0));
+      }
+      f32x4 wt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wt[j] = *reinterpret_cast<const f32x4 *>(w + ((size_t)h * DK + c0 + j) * kConvTaps);
+#pragma unroll
+      for (int u = 0; u < TPL; ++u) {
+        float y[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float xv[kConvTaps];
+#pragma unroll
+          for (int i = 0; i < kConvTaps; ++i) xv[i] = (okm >> (u + i)) & 1 ? (float)win[u + i][j] : 0.f;
+          y[j] = conv_taps(wt[j], xv[0], xv[1], xv[2], xv[3]);
+        }
+        out[u] = F4::pack(y);
+      }
+    };
     char *sKh = arena, *sQh = arena + LK::BYTES, *sKd = arena + 2 * LK::BYTES;
     float *sR = reinterpret_cast<float *>(arena);
     float *sT = reinterpret_cast<float *>(arena + RT_BYTES);
@@ -487,19 +568,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // take q = k = 0 and alpha = 1; their loads read a valid token instead.
     // Each input byte is read once here, so the loads carry the nontemporal
     // hint (measured faster: they do not displace the records in the caches).
-    const int tb0 = 16 * w + TPL * th;   // first token of this lane
     // q and k stay packed in their own type until used (register budget)
     typename F4::vec kraw[TPL], qraw[TPL];
     float pa[TPL][4];
+    if constexpr (CONV) {
+      conv_lane(k, a.conv_k, kraw);
+      __builtin_amdgcn_sched_barrier(0);  // one tensor's window at a time
+      conv_lane(q, a.conv_q, qraw);
+    }
 #pragma unroll
     for (int u = 0; u < TPL; ++u) {
       const int tok = tb0 + u;
-      const bool live = tok < L;
       const size_t off = base + (size_t)min(tok, L - 1) * hs;
       float al[4];
       gate4(min(tok, L - 1), c0, al, true, true);   // converted below, after the q, k activation
-      kraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(k + off));
-      qraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(q + off));
+      if constexpr (!CONV) {
+        kraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(k + off));
+        qraw[u] = __builtin_nontemporal_load(reinterpret_cast<const typename F4::vec *>(q + off));
+      }
 #pragma unroll
       for (int j = 0; j < 4; ++j) pa[u][j] = al[j];
     }
@@ -769,7 +855,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         float kj[CQ], rho[CQ];
 #pragma unroll
         for (int cc = 0; cc < CQ; cc += 4) {
-          F4::load(k + cb + (size_t)min(j, L - 1) * hs + cc, kj + cc);
+          if constexpr (CONV)
+            conv_load4(k, a.conv_k, min(j, L - 1), qd * CQ + cc, kj + cc);
+          else
+            F4::load(k + cb + (size_t)min(j, L - 1) * hs + cc, kj + cc);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             if constexpr (ACTQK) kj[cc + e] = (float)(E)(silu_f(kj[cc + e]) * sInvNorm[0][min(j, L - 1)]);
@@ -785,8 +874,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
           for (int cc = 0; cc < CQ; cc += 4) {
             float al[4], kx[4], qx[4];
             gate4(min(i, L - 1), qd * CQ + cc, al, false);
-            F4::load(k + off + cc, kx);
-            F4::load(q + off + cc, qx);
+            if constexpr (CONV) {
+              // the taps are read again for every token: kept live across the
+              // loop, those of all channel groups would not fit in registers
+              __asm__ volatile("" ::: "memory");
+              conv_load4(k, a.conv_k, min(i, L - 1), qd * CQ + cc, kx);
+              conv_load4(q, a.conv_q, min(i, L - 1), qd * CQ + cc, qx);
+            } else {
+              F4::load(k + off + cc, kx);
+              F4::load(q + off + cc, qx);
+            }
             if constexpr (ACTQK) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
@@ -859,6 +956,49 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     else tile64_out<E, LDR>(gTb, sT, sBeta, 2, 3, 64, 192);     // row tile 2
     __syncthreads();
     tile64_out<E, LDR>(gTb, sT, sBeta, 3, 4);                   // row tile 3
+
+    // CONV: v's convolution into this chunk's rows of o; a thread takes a run
+    // of four tokens and 16 bytes of channels (its window: the seven rows
+    // ending at the run's last token)
+    if constexpr (CONV) {
+      typedef typename Row16<E>::vec RV;
+      constexpr int VE = Row16<E>::N, NW = 4 + kConvTaps - 1;
+      const int GR = a.dv / VE;  // 16-byte groups per row
+      const E *V = reinterpret_cast<const E *>(a.v);
+      E *O = reinterpret_cast<E *>(a.o);
+      const size_t vs = (size_t)a.H * a.dv;
+      for (int idx = tid; idx < (kChunk / 4) * GR; idx += kThreads) {
+        const int r0 = 4 * (idx / GR), ch = (idx % GR) * VE;
+        if (r0 >= L) continue;
+        RV win[NW];
+        unsigned okm = 0;
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+          const int rel = min(r0 - (kConvTaps - 1) + i, L - 1);
+          const bool ok = t0 + rel >= s0;
+          okm |= (unsigned)ok << i;
+          win[i] = __builtin_nontemporal_load(
+              reinterpret_cast<const RV *>(V + (size_t)(t0 + (ok ? rel : 0)) * vs + (size_t)h * a.dv + ch));
+        }
+        f32x4 wt[VE];
+#pragma unroll
+        for (int j = 0; j < VE; ++j)
+          wt[j] = *reinterpret_cast<const f32x4 *>(a.conv_v + ((size_t)h * a.dv + ch + j) * kConvTaps);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (r0 + u >= L) break;
+          RV y;
+#pragma unroll
+          for (int j = 0; j < VE; ++j) {
+            float xv[kConvTaps];
+#pragma unroll
+            for (int i = 0; i < kConvTaps; ++i) xv[i] = (okm >> (u + i)) & 1 ? (float)win[u + i][j] : 0.f;
+            y[j] = (E)conv_taps(wt[j], xv[0], xv[1], xv[2], xv[3]);
+          }
+          __builtin_nontemporal_store(y, reinterpret_cast<RV *>(O + (size_t)(t0 + r0 + u) * vs + (size_t)h * a.dv + ch));
+        }
+      }
+    }
   };
 
   if constexpr (!SCHED) {
@@ -1923,6 +2063,86 @@ void unit_scan_kernel(ScanKArgs a) {
       *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
 }
 
+// ======================================================= output norm + gate
+// One pass over o after the scan (kda_module_ops): per token and head,
+//   o <- o / sqrt(mean_c o_c^2 + eps) * w   (RMS norm over the d_v values, with
+//                                            gains w; when w is given)
+//   o <- o * sigmoid(g)                     (g the gate logits; when given)
+// in fp32, rounded to E once.  LPR lanes per (token, head) row, 16 bytes of
+// it each; tokens [tok_begin, tok_end), from the sequence offsets when
+// seq_tok0 is given (a packed batch: rows outside every sequence are left
+// alone), else [0, n_tok).
+template <typename E, int LPR>
+__global__ __launch_bounds__(kThreads) void out_norm_gate_kernel(void *o, const void *gate, const float *w, float eps,
+                                                                int H, long long n_tok, const int32_t *seq_tok0,
+                                                                int n_seq) {
+  typedef typename Row16<E>::vec RV;
+  constexpr int VE = Row16<E>::N, DV = LPR * VE;
+  const long long r = (long long)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;  // row (token * H + head)
+  const int part = threadIdx.x % LPR;
+  long long tb = 0, te = n_tok;
+  if (seq_tok0) {
+    tb = seq_tok0[0];
+    te = seq_tok0[n_seq];
+  }
+  const long long row = tb * H + r;
+  // whole groups of LPR lanes leave together: the sum below stays within a group
+  if (row >= te * H) return;
+  E *po = reinterpret_cast<E *>(o) + (size_t)row * DV + part * VE;
+  const RV x = __builtin_nontemporal_load(reinterpret_cast<const RV *>(po));
+  float y[VE];
+#pragma unroll
+  for (int j = 0; j < VE; ++j) y[j] = (float)x[j];
+  if (w) {
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < VE; ++j) ss += y[j] * y[j];
+    const float rn = __builtin_amdgcn_rsqf(group_sum<LPR>(ss) * (1.f / DV) + eps);
+#pragma unroll
+    for (int j = 0; j < VE; j += 4) {
+      const f32x4 g4 = *reinterpret_cast<const f32x4 *>(w + part * VE + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[j + e] = y[j + e] * rn * g4[e];
+    }
+  }
+  if (gate) {
+    const RV gv = __builtin_nontemporal_load(reinterpret_cast<const RV *>(reinterpret_cast<const E *>(gate) +
+                                                                         (size_t)row * DV + part * VE));
+#pragma unroll
+    for (int j = 0; j < VE; ++j) y[j] *= sigmoid_f((float)gv[j]);
+  }
+  RV out;
+#pragma unroll
+  for (int j = 0; j < VE; ++j) out[j] = (E)y[j];
+  __builtin_nontemporal_store(out, reinterpret_cast<RV *>(po));
+}
+
+template <typename E>
+hipError_t launch_out_post(const PrefillArgs &a, const int32_t *seq_tok0, hipStream_t stream) {
+  if (!a.norm_w && !a.out_gate) return hipSuccess;
+  const long long n_tok = seq_tok0 ? a.T : (long long)a.B * a.T;
+  constexpr int VE = Row16<E>::N;
+  const int lpr = a.dv / VE;
+  const long long rows = n_tok * a.H;
+  if (rows == 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows * lpr + kThreads - 1) / kThreads));
+#define KDA_POST(L)                                                                                           \
+  case L:                                                                                                     \
+    hipLaunchKernelGGL((out_norm_gate_kernel<E, L>), grid, dim3(kThreads), 0, stream, a.o, a.out_gate, a.norm_w, \
+                       a.norm_eps, a.H, n_tok, seq_tok0, a.plan.n_seq);                                       \
+    break;
+  switch (lpr) {
+    KDA_POST(2)
+    KDA_POST(4)
+    KDA_POST(8)
+    KDA_POST(16)
+    KDA_POST(32)
+    default: return hipErrorInvalidValue;
+  }
+#undef KDA_POST
+  return hipGetLastError();
+}
+
 // Zeroes the control words and the ready words of the overlapped schedule
 // and records that schedule as the one this call runs.
 __global__ void sched_clear_kernel(int *ctl, int *ready, int n_ready) {
@@ -1931,32 +2151,33 @@ __global__ void sched_clear_kernel(int *ctl, int *ready, int n_ready) {
   for (int i = tid; i < n_ready; i += gridDim.x * blockDim.x) ready[i] = 0;
 }
 
-// The prep kernel for a gate form, with or without the q, k activation.
-template <int DK, typename E, bool ACTQK, bool SCHED = false>
+// The prep kernel for a gate form, with or without the q, k activation (and
+// the convolution).
+template <int DK, typename E, bool ACTQK, bool SCHED = false, bool CONV = false>
 void launch_prep(int gate, dim3 grid, hipStream_t stream, const PrepKArgs &pa) {
   switch (gate) {
     case kGateScalar:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
       break;
     case kGateNone:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
       break;
     case kGateLogChannel:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogChannel, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogChannel, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
       break;
     case kGateLogScalar:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogScalar, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogScalar, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
       break;
     case kGateSoftplusChannel:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusChannel, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream,
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusChannel, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream,
                          pa);
       break;
     case kGateSoftplusScalar:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusScalar, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream,
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusScalar, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream,
                          pa);
       break;
     default:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
+      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
   }
 }
 
@@ -2052,8 +2273,10 @@ OverlapCtx *overlap_ctx(hipStream_t stream) {
 
 // Shapes the overlapped schedule supports: dense bf16 batches at
 // d_k = d_v = 128 (two records and two value tiles fill the scan's LDS).
+// Not with the short convolution, whose prep writes the convolved v that the
+// scan reads.
 template <int DK, typename E> bool overlap_supported(const PrefillArgs &a) {
-  return DK == 128 && a.dv == 128 && sizeof(E) == 2 && !a.cu_seqlens && a.plan.ready_bytes > 0;
+  return DK == 128 && a.dv == 128 && sizeof(E) == 2 && !a.cu_seqlens && a.plan.ready_bytes > 0 && !a.conv_q;
 }
 
 // Automatic choice: the overlap needs the scan's workgroups (four per unit at
@@ -2151,7 +2374,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
   if (packed) {
     hipLaunchKernelGGL(varlen_index_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, P.n_seq, a.T,
                        tables + P.seq_tok0, tables + P.seq_chunk0, tables + P.chunk_t0, tables + P.chunk_len,
-                       P.max_chunks, tables + P.seq_order);
+                       tables + P.chunk_s0, P.max_chunks, tables + P.seq_order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -2168,6 +2391,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.src.nct = nct;
     pa.src.chunk_t0 = packed ? tables + P.chunk_t0 : nullptr;
     pa.src.chunk_len = packed ? tables + P.chunk_len : nullptr;
+    pa.src.chunk_s0 = packed ? tables + P.chunk_s0 : nullptr;
     pa.src.seq_chunk0 = packed ? tables + P.seq_chunk0 : nullptr;
     pa.src.n_seq = P.n_seq;
     pa.H = a.H;
@@ -2176,12 +2400,28 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.lay = lay;
     pa.ready = pa.ctl = nullptr;
     pa.ready_words = pa.n_units = 0;
+    pa.conv_q = a.conv_q;
+    pa.conv_k = a.conv_k;
+    pa.conv_v = a.conv_v;
+    pa.v = a.v;
+    pa.o = a.o;
+    pa.dv = a.dv;
     if (overlap_supported<DK, E>(a) && overlap_chosen(a, nct)) {
-      std::lock_guard<std::mutex> lock(g_overlap_mu);
-      if (OverlapCtx *ov = overlap_ctx(stream)) return run_prefill_overlap<DK, E>(a, stream, pa, lay, records, *ov);
+      hipError_t e = hipSuccess;
+      bool ran = false;
+      {
+        std::lock_guard<std::mutex> lock(g_overlap_mu);
+        if (OverlapCtx *ov = overlap_ctx(stream)) {
+          e = run_prefill_overlap<DK, E>(a, stream, pa, lay, records, *ov);
+          ran = true;
+        }
+      }
+      if (ran) return e != hipSuccess ? e : launch_out_post<E>(a, nullptr, stream);
     }
     const dim3 pg((unsigned)P.max_chunks, a.H);
-    if (a.act & kActQK)
+    if (a.conv_q)
+      launch_prep<DK, E, true, false, true>(a.gate, pg, stream, pa);
+    else if (a.act & kActQK)
       launch_prep<DK, E, true>(a.gate, pg, stream, pa);
     else
       launch_prep<DK, E, false>(a.gate, pg, stream, pa);
@@ -2191,7 +2431,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
 
   if (P.n_seq > 0) {
     ScanKArgs sa{};
-    sa.v = a.v;
+    sa.v = a.conv_q ? a.o : a.v;  // the prep left v's convolution in o
     sa.S0 = a.S0;
     sa.o = a.o;
     sa.S_final = a.S_final;
@@ -2230,7 +2470,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  return launch_out_post<E>(a, packed ? tables + P.seq_tok0 : nullptr, stream);
 }
 
 template <typename E> hipError_t run_prefill_dk(const PrefillArgs &a, hipStream_t s) {

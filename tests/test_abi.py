@@ -232,3 +232,42 @@ def test_set_validation_query(kda):
         assert kda.validation_enabled() is True
     finally:
         kda.set_validation(prev)
+
+
+def _module(kda, ops, act=1, ws_bytes=10, **kw):
+    """kda_chunk_fwd_module with fake aligned pointers; every case below is
+    rejected on the host."""
+    P = lambda a: ctypes.c_void_p(a)
+    a = dict(q=P(0x10000), k=P(0x20000), v=P(0x30000), alpha=P(0x40000), beta=P(0x50000), o=P(0x60000),
+             S_final=P(0x70000), ws=P(0x80000))
+    a.update(kw)
+    return kda.lib.kda_chunk_fwd_module(a["q"], a["k"], a["v"], a["alpha"], kda.KDA_GATE_CHANNEL, a["beta"], act,
+                                        None if ops is None else ctypes.byref(ops), None, None, 2, 2, 8, 2, 16,
+                                        16, 0.0, kda.KDA_BF16, a["o"], a["S_final"], a["ws"], ws_bytes, None)
+
+
+def test_module_ops_host_checks(kda):
+    from linear_attention_kda_amd._binding import KdaModuleOps
+    W = [0x100000, 0x101000, 0x102000]
+    # ops == NULL is kda_chunk_fwd_ex: the workspace of 10 bytes is too small
+    assert _module(kda, None) == 6
+    # only some of the convolution weights
+    assert _module(kda, KdaModuleOps(W[0], W[1], None, None, 0.0, None)) == 1
+    assert _module(kda, KdaModuleOps(None, None, W[2], None, 0.0, None)) == 1
+    # the convolution needs the q, k activation
+    assert _module(kda, KdaModuleOps(W[0], W[1], W[2], None, 0.0, None), act=0) == 12
+    assert _module(kda, KdaModuleOps(W[0], W[1], W[2], None, 0.0, None), act=2) == 12
+    # negative or NaN eps with a norm
+    assert _module(kda, KdaModuleOps(None, None, None, 0x103000, -1.0, None)) == 2
+    assert _module(kda, KdaModuleOps(None, None, None, 0x103000, float("nan"), None)) == 2
+    # misaligned weight or gate
+    assert _module(kda, KdaModuleOps(W[0] + 4, W[1], W[2], None, 0.0, None)) == 5
+    assert _module(kda, KdaModuleOps(None, None, None, None, 0.0, 0x104008)) == 5
+    # o overlapping a weight or the gate (checked after the workspace size)
+    big = 1 << 30
+    assert _module(kda, KdaModuleOps(W[0], W[1], W[2], None, 0.0, None), ws_bytes=big, o=ctypes.c_void_p(W[1])) == 8
+    assert _module(kda, KdaModuleOps(None, None, None, 0x103000, 1e-6, None), ws_bytes=big,
+                   o=ctypes.c_void_p(0x103000)) == 8
+    assert _module(kda, KdaModuleOps(None, None, None, None, 0.0, 0x60000 + 512), ws_bytes=big) == 8
+    # valid ops, then the workspace check as for kda_chunk_fwd_ex
+    assert _module(kda, KdaModuleOps(W[0], W[1], W[2], 0x103000, 1e-6, 0x104000)) == 6
