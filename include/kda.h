@@ -179,26 +179,44 @@ int kda_set_validation(int enable);
  *     process holding its compute units), the scan stops waiting and its
  *     results are wrong: kda_chunk_fwd_status then reports
  *     KDA_SCHED_ERR_TIMEOUT for that workspace.
- *   KDA_SCHEDULE_AUTO (default): overlap when supported, the scan's
+ *   KDA_SCHEDULE_SPLIT: split-sequence, for long sequences over few heads
+ *     (page "Kimi Delta Attention (KDA)": the state has a fixed size, which
+ *     is what makes very long contexts feasible; the chunk-to-chunk step is
+ *     affine in the state).  Each sequence is cut into G segments of whole
+ *     chunks.  After the preparation, one pass computes for every segment
+ *     but the last the affine map of the state over it (S_end = S_start M +
+ *     X: the scan from S = 0 gives X, the scan from the identity with v = 0
+ *     gives M), a small pass chains the maps into each segment's start state
+ *     (in fp32), and the scan then runs all segments at once.  The result
+ *     equals the other schedules' up to rounding (not bitwise: the start
+ *     states come from the maps).  Dense bf16 batches with d_k = d_v = 128
+ *     whose B * H leaves room for it (G >= 2 segments of at least 16
+ *     chunks whose modelled cost beats the sequential scan); other calls run
+ *     as under KDA_SCHEDULE_AUTO.  Needs the larger workspace
+ *     kda_chunk_fwd_workspace_size reports for those shapes.
+ *   KDA_SCHEDULE_AUTO (default): split-sequence when supported and its
+ *     modelled cost is at most 3/4 of the sequential scan's (for example
+ *     B = 1, H = 8, T = 65536); else overlap when supported, the scan's
  *     workgroups (B * H * d_v / 32) fit on 128 compute units, and the batch
  *     holds at least 4096 chunks over all sequences and heads
  *     (B * H * ceil(T / 64); long sequences over few heads, whose records
  *     overflow the Infinity Cache); else two-phase.
  * The initial value is taken from the environment variable KDA_SCHEDULE
- * (0, 1 or 2) at load time.  Process-wide; returns the previous setting, or
- * -1 (nothing changed) for an unknown value.
+ * (0, 1, 2 or 3) at load time.  Process-wide; returns the previous setting,
+ * or -1 (nothing changed) for an unknown value.
  */
 typedef enum {
   KDA_SCHEDULE_AUTO = 0,
   KDA_SCHEDULE_TWO_PHASE = 1,
-  KDA_SCHEDULE_OVERLAP = 2
+  KDA_SCHEDULE_OVERLAP = 2,
+  KDA_SCHEDULE_SPLIT = 3
 } kda_schedule;
 int kda_set_schedule(int schedule);
 
 /*
  * What the last kda_chunk_fwd call that launched work with this workspace
- * did: *schedule receives the schedule it ran (KDA_SCHEDULE_TWO_PHASE or
- * KDA_SCHEDULE_OVERLAP) and *errors the overlapped schedule's error bits
+ * did: *schedule receives the schedule it ran (KDA_SCHEDULE_TWO_PHASE,
+ * KDA_SCHEDULE_OVERLAP or KDA_SCHEDULE_SPLIT) and *errors the overlapped schedule's error bits
  * (0 for a clean call; KDA_SCHED_ERR_TIMEOUT: a wait for a chunk record gave
  * up, so that call's o and S_final are wrong; KDA_SCHED_ERR_XCD: a record
  * was read on another XCD than the one that wrote it).  The workspace keeps

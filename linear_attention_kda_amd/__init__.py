@@ -11,7 +11,8 @@ _BINDING_NAMES = ("EXPORTED", "GATES", "KDA_BF16", "KDA_F32", "KDA_GATE_CHANNEL"
                   "KDA_GATE_SCALAR", "KDA_GATE_SOFTPLUS_CHANNEL", "KDA_GATE_SOFTPLUS_SCALAR",
                   "KDA_ACT_QK_SILU_L2NORM", "KDA_ACT_BETA_SIGMOID", "LIB_PATH", "KdaError", "chunk_fwd", "chunk_fwd_workspace_size",
                   "decode_step", "decode_tokens", "lib", "set_validation", "set_schedule", "status_string",
-                  "KDA_SCHEDULE_AUTO", "KDA_SCHEDULE_TWO_PHASE", "KDA_SCHEDULE_OVERLAP", "SCHEDULES",
+                  "KDA_SCHEDULE_AUTO", "KDA_SCHEDULE_TWO_PHASE", "KDA_SCHEDULE_OVERLAP", "KDA_SCHEDULE_SPLIT",
+                  "SCHEDULES",
                   "KDA_ERR_INVALID_VALUE", "KDA_ERR_STREAM_CAPTURE", "KDA_SCHED_ERR_TIMEOUT", "KDA_SCHED_ERR_XCD",
                   "chunk_fwd_status", "release", "validation_enabled", "set_sched_wait_limit",
                   "chunk_fwd_noalloc", "KDA_ERR_TOO_LARGE", "NOALLOC_SCRATCH_BYTES")

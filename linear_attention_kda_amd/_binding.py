@@ -41,7 +41,9 @@ KDA_ACT_BETA_SIGMOID = 2
 KDA_SCHEDULE_AUTO = 0
 KDA_SCHEDULE_TWO_PHASE = 1
 KDA_SCHEDULE_OVERLAP = 2
-SCHEDULES = {"auto": KDA_SCHEDULE_AUTO, "two_phase": KDA_SCHEDULE_TWO_PHASE, "overlap": KDA_SCHEDULE_OVERLAP}
+KDA_SCHEDULE_SPLIT = 3
+SCHEDULES = {"auto": KDA_SCHEDULE_AUTO, "two_phase": KDA_SCHEDULE_TWO_PHASE, "overlap": KDA_SCHEDULE_OVERLAP,
+             "split": KDA_SCHEDULE_SPLIT}
 
 # error bits of kda_chunk_fwd_status
 KDA_SCHED_ERR_TIMEOUT = 1

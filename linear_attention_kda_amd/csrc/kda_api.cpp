@@ -50,7 +50,8 @@ std::atomic<int> g_validate{[] {
 std::atomic<int> g_schedule{[] {
   const char *e = std::getenv("KDA_SCHEDULE");
   const int v = e ? std::atoi(e) : 0;
-  return v == kda::kScheduleTwoPhase || v == kda::kScheduleOverlap ? v : kda::kScheduleAuto;
+  return v == kda::kScheduleTwoPhase || v == kda::kScheduleOverlap || v == kda::kScheduleSplit ? v
+                                                                                               : kda::kScheduleAuto;
 }()};
 
 // Bound on the overlapped scan's ready-flag waits (kda_set_sched_wait_limit).
@@ -194,7 +195,7 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
 
-  const kda::WorkspacePlan plan = kda::plan_workspace(packed, B, T, H, d_k, N, (int)es);
+  const kda::WorkspacePlan plan = kda::plan_workspace(packed, B, T, H, d_k, N, (int)es, noalloc ? 0 : d_v);
   if (!noalloc && plan.total > 0 && (!workspace || workspace_bytes < plan.total)) return KDA_ERR_WORKSPACE_TOO_SMALL;
 
   {
@@ -316,7 +317,8 @@ long long kda_set_sched_wait_limit(long long ticks) {
 }
 
 int kda_set_schedule(int schedule) {
-  if (schedule != KDA_SCHEDULE_AUTO && schedule != KDA_SCHEDULE_TWO_PHASE && schedule != KDA_SCHEDULE_OVERLAP)
+  if (schedule != KDA_SCHEDULE_AUTO && schedule != KDA_SCHEDULE_TWO_PHASE && schedule != KDA_SCHEDULE_OVERLAP &&
+      schedule != KDA_SCHEDULE_SPLIT)
     return -1;
   return g_schedule.exchange(schedule);
 }
@@ -325,7 +327,7 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int N
   if (B < 0 || T < 0 || H <= 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
   const int esize = dtype == KDA_BF16 ? 2 : 4;
-  size_t need = kda::plan_workspace(false, B, T, H, d_k, B, esize).total;
+  size_t need = kda::plan_workspace(false, B, T, H, d_k, B, esize, d_v).total;
   if (B == 1 && N >= 0) {  // may be a packed batch of N sequences
     const size_t pk = kda::plan_workspace(true, 1, T, H, d_k, N, esize).total;
     if (pk > need) need = pk;

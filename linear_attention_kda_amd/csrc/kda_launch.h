@@ -58,8 +58,48 @@ constexpr size_t kCtlBytes = kCtlWords * sizeof(int32_t);
 // error bits: a ready-flag wait timed out / a record came from another XCD
 constexpr int kSchedErrTimeout = 1, kSchedErrXcd = 2;
 
+// Split-sequence prefill (a dense batch of few units at d_k = d_v = 128,
+// bf16): each sequence is cut into G segments of cps chunks (the last one
+// shorter).  A first scan pass gives the affine map of the state over every
+// segment but the last (S_end = S_start M + X), a small pass chains the maps
+// into each segment's start state, and the ordinary scan then runs all
+// segments at once.  The pass over the maps costs about as much per chunk as
+// the scan, so the split pays only when the units leave most of the chip
+// idle: G is chosen by a cost model in scan steps (the map pass at 0.8 of a
+// scan step, whole waves of 256 workgroups), and taken automatically when
+// it saves a quarter of the sequential chain.
+struct SplitPlan {
+  int G = 1;          // segments per sequence (1: no split)
+  int cps = 0;        // chunks per segment (all but the last)
+  bool worth = false; // the automatic schedule takes it
+};
+constexpr int kSplitMinChunks = 16;  // chunks per segment, at least
+constexpr int kSplitMaxSegments = 16;
+inline SplitPlan split_plan(int B, int T, int H, int dk, int dv, int esize) {
+  SplitPlan sp;
+  if (dk != 128 || dv != 128 || esize != 2 || B <= 0 || T <= 0) return sp;
+  const long long units = (long long)B * H, nct = ((long long)T + kChunkTokens - 1) / kChunkTokens;
+  const long long wg_scan = units * (dv / 32), wg_map = units * ((dv + dk) / 32);
+  double best = (double)nct;  // the sequential chain, in scan steps
+  for (int G = 2; G <= kSplitMaxSegments; ++G) {
+    const long long cps = (nct + G - 1) / G;
+    if (cps < kSplitMinChunks) break;
+    if ((G - 1) * cps >= nct) continue;  // the last segment would be empty
+    const double waves1 = (double)(((G - 1) * wg_map + 255) / 256), waves3 = (double)((G * wg_scan + 255) / 256);
+    const double est = waves1 * cps * 0.8 + waves3 * cps + 2.0 * (G - 1);
+    if (est < best) {
+      best = est;
+      sp.G = G;
+      sp.cps = (int)cps;
+    }
+  }
+  sp.worth = sp.G > 1 && best < 0.75 * (double)nct;
+  return sp;
+}
+
 // Workspace = [control words] [index tables (packed batches only)]
-//             [chunk records] [ready flags (dense batches only)].
+//             [chunk records] [ready flags (dense batches only)]
+//             [split-sequence buffers (dense batches a split can serve)].
 struct WorkspacePlan {
   int n_seq;           // sequences
   long long max_chunks;// chunk slots (dense: exact count)
@@ -72,10 +112,18 @@ struct WorkspacePlan {
   size_t total;
   // int32 table offsets (in elements from `tables`), packed only
   size_t seq_tok0, seq_chunk0, chunk_t0, chunk_len, chunk_s0, seq_order;
+  // split-sequence prefill (split.G > 1 only): byte offsets of the segment
+  // tables (B G + 1 token offsets, then B G + 1 chunk offsets, int32), the
+  // maps ([B (G-1) H] x (d_v + d_k) x d_k fp32: X rows, then M^T rows), the
+  // segment start states and the segments' end states ([B G H] x d_v x d_k
+  // fp32 each)
+  SplitPlan split;
+  size_t sp_tables, sp_maps, sp_start, sp_end;
 };
 
+// dv = 0: no split-sequence buffers (the no-allocation entry point).
 inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
-                                    int N, int esize) {
+                                    int N, int esize, int dv = 0) {
   WorkspacePlan P{};
   ChunkRecordLayout L = chunk_record_layout(dk, esize);
   P.record_bytes = L.bytes;
@@ -100,6 +148,15 @@ inline WorkspacePlan plan_workspace(bool packed, int B, int T, int H, int dk,
   P.ready = P.records + (size_t)P.max_chunks * H * P.record_bytes;
   P.ready_bytes = packed ? 0 : ((size_t)P.max_chunks * H * sizeof(int32_t) + 255) / 256 * 256;
   P.total = P.ready + P.ready_bytes;
+  if (!packed && dv > 0) P.split = split_plan(B, T, H, dk, dv, esize);
+  if (P.split.G > 1) {
+    const size_t G = (size_t)P.split.G, state = (size_t)dv * dk * sizeof(float);
+    P.sp_tables = P.total;
+    P.sp_maps = P.sp_tables + ((2 * ((size_t)B * G + 1) * sizeof(int32_t) + 255) / 256 * 256);
+    P.sp_start = P.sp_maps + (size_t)B * (G - 1) * H * (size_t)(dv + dk) * dk * sizeof(float);
+    P.sp_end = P.sp_start + (size_t)B * G * H * state;
+    P.total = P.sp_end + (size_t)B * G * H * state;
+  }
   return P;
 }
 
@@ -123,9 +180,10 @@ constexpr unsigned kActBeta = 2;  // beta <- sigmoid(beta)
 // per channel, the last one on the current token.
 constexpr int kConvTaps = 4;
 
-// Prefill schedules (kda_set_schedule): automatic, always prep then scan, or
-// prep and scan overlapped whenever the shapes allow it.
-constexpr int kScheduleAuto = 0, kScheduleTwoPhase = 1, kScheduleOverlap = 2;
+// Prefill schedules (kda_set_schedule): automatic, always prep then scan,
+// prep and scan overlapped whenever the shapes allow it, or split-sequence
+// whenever the shapes allow it.
+constexpr int kScheduleAuto = 0, kScheduleTwoPhase = 1, kScheduleOverlap = 2, kScheduleSplit = 3;
 
 // Default bound on one ready-flag wait of the overlapped scan: 2^27 ticks of
 // the 100 MHz real-time counter, about 1.3 s.

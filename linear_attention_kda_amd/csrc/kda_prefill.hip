@@ -35,6 +35,7 @@
 
 #include <hip/hip_ext.h>
 
+#include <algorithm>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -1055,6 +1056,10 @@ struct ScanKArgs {
   int ready_words;
   int *ctl;
   long long wait_ticks;  // bound on one ready-flag wait (100 MHz ticks; 0: give up at once)
+  // two-phase only: pull each chunk record into L2 a step before it is
+  // copied to LDS (set when the records outgrow the 256 MB Infinity Cache,
+  // so they come from HBM)
+  int touch_ahead;
 };
 
 // B operands built from accumulator tiles.  Tile q of a K x 16 operand holds
@@ -1159,6 +1164,26 @@ __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// 4 bytes per lane from global memory into LDS (global_load_lds_dword; lane
+// l's bytes land at lds_base + 4 l).  Used only to pull lines into L2 ahead
+// of their copy: the LDS bytes are a landing place nothing reads.
+__device__ __forceinline__ void lds_dma4(const void *src, uint32_t lds_base) {
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(src), "s"(base)
+               : "memory", "m0");
+}
+
+// Pulls 8 KiB blocks b0, b0 + 1, .., b0 + NB - 1 of a record (of `bytes`
+// bytes) into L2: one line of 128 bytes per lane, addresses clamped to the
+// record; the data lands in a 256-byte LDS scratch that nobody reads.
+template <int NB>
+__device__ __forceinline__ void touch_record(const char *rec, int bytes, int b0, uint32_t scratch_lds) {
+#pragma unroll
+  for (int i = 0; i < NB; ++i) lds_dma4(rec + min((b0 + i) * 8192 + lane_id() * 128, bytes - 4), scratch_lds);
+}
+
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
 // vmcnt[3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).  Vector memory loads
 // retire in issue order, so this waits for all but the N latest.
@@ -1194,7 +1219,9 @@ template <int DK, typename E> struct RecordShape {
 // 16-row tiles inner), so consecutive matrix-core products are independent
 // and none waits for the previous one's result; the LDS operand reads of
 // later phases are issued early, in the order they are used.
-template <int DK, typename E, int NT, int VSTRIDE>
+// OUT = false: the state update alone (no X_bot, no outputs; s Qbnd and A
+// are not read).  VZERO: V = 0 (vs is not read).
+template <int DK, typename E, int NT, int VSTRIDE, bool OUT = true, bool VZERO = false>
 __device__ __forceinline__ void scan_chunk(const char *recb, const E *vs, f32x4 (*st)[NT], f32x4 (*ov)[NT]) {
   typedef RecordShape<DK, E> RS;
   typedef FragShape<E, DK> FK;   // products over d_k
@@ -1235,14 +1262,14 @@ __device__ __forceinline__ void scan_chunk(const char *recb, const E *vs, f32x4 
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
       fk[I] = BK::load1(Kh + I * TILE_K, u);
-      fq[I] = BK::load1(Qh + I * TILE_K, u);
+      if constexpr (OUT) fq[I] = BK::load1(Qh + I * TILE_K, u);
     }
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         xt[I][nt] = sb[nt].mma1(fk[I], u, xt[I][nt]);
-        xb[I][nt] = sb[nt].mma1(fq[I], u, xb[I][nt]);
+        if constexpr (OUT) xb[I][nt] = sb[nt].mma1(fq[I], u, xb[I][nt]);
       }
   }
   // operands of the later phases
@@ -1253,17 +1280,20 @@ __device__ __forceinline__ void scan_chunk(const char *recb, const E *vs, f32x4 
 #pragma unroll
     for (int I = 0; I < 4; ++I)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vv[nt][I][r] = to_f(vs[(16 * I + 4 * g + r) * VSTRIDE + 16 * nt + col]);
+      for (int r = 0; r < 4; ++r)
+        vv[nt][I][r] = VZERO ? 0.f : to_f(vs[(16 * I + 4 * g + r) * VSTRIDE + 16 * nt + col]);
 #pragma unroll
   for (int u = 0; u < UT; ++u)
 #pragma unroll
     for (int I = 0; I < 4; ++I)
       if (need(I, u)) ftb[I][u] = BT::load1(Tb + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
+  if constexpr (OUT) {
 #pragma unroll
-  for (int u = 0; u < UT; ++u)
+    for (int u = 0; u < UT; ++u)
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
-      if (need(I, u)) faq[I][u] = BT::load1(Aq + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
+      for (int I = 0; I < 4; ++I)
+        if (need(I, u)) faq[I][u] = BT::load1(Aq + tri_slab0(I, (int)sizeof(E)) * 64 * FT::KS, u);
+  }
 #pragma unroll
   for (int u = 0; u < UT; ++u)
 #pragma unroll
@@ -1304,10 +1334,12 @@ __device__ __forceinline__ void scan_chunk(const char *recb, const E *vs, f32x4 
     for (int I = 0; I < 4; ++I) et[I] = e[I][nt];
     eo[nt].build(et);
   }
+  if constexpr (OUT) {
 #pragma unroll
-  for (int I = 0; I < 4; ++I)
+    for (int I = 0; I < 4; ++I)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) ov[I][nt] = xb[I][nt];
+      for (int nt = 0; nt < NT; ++nt) ov[I][nt] = xb[I][nt];
+  }
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -1316,11 +1348,13 @@ __device__ __forceinline__ void scan_chunk(const char *recb, const E *vs, f32x4 
       for (int r = 0; r < 4; ++r) st[ct][nt][r] *= p[ct][r];
 #pragma unroll
   for (int u = 0; u < UT; ++u) {
+    if constexpr (OUT) {
 #pragma unroll
-    for (int I = 0; I < 4; ++I)
-      if (need(I, u))
+      for (int I = 0; I < 4; ++I)
+        if (need(I, u))
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) ov[I][nt] = eo[nt].mma1(faq[I][u], u, ov[I][nt]);
+          for (int nt = 0; nt < NT; ++nt) ov[I][nt] = eo[nt].mma1(faq[I][u], u, ov[I][nt]);
+    }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -1364,6 +1398,7 @@ void chunk_scan_kernel(ScanKArgs a) {
   __shared__ __attribute__((aligned(1024))) char rec1[NBUF == 2 ? RS::bytes : 1024];
   __shared__ __attribute__((aligned(16))) E vring[NV][CW * VSL];
   __shared__ __attribute__((aligned(16))) char otile[2][NBUF == 2 ? 64 * OROW : 16];
+  __shared__ __attribute__((aligned(16))) char touch_area[256];
 
   const int w = wave_id(), l = lane_id(), col = l & 15, g = l >> 4;
   int u, grp;  // unit and value-column group of this workgroup
@@ -1532,7 +1567,12 @@ void chunk_scan_kernel(ScanKArgs a) {
         }
         // the compute waves staged chunk ci-1's outputs before the last barrier
         if (cpi == 0 && ci > 0) store_tile(ci - 1, otile[(ci - 1) & 1]);
-        if (vcopier && ci + 2 < nchunks) {
+        if (!SCHED && a.touch_ahead && cpi == 1 && !vcopier && ci + 2 < nchunks) {
+          // record ci+2 into L2: this workgroup's share, two 8 KiB blocks
+          touch_record<2>(a.ws_records + ((size_t)(chunk0 + ci + 2) * H + h) * RS::bytes, RS::bytes, 2 * grp,
+                          (uint32_t)(size_t)(__attribute__((address_space(3))) char *)touch_area);
+          wait_vmcnt<2>();             // the copies; the touches may still fly
+        } else if (vcopier && ci + 2 < nchunks) {
           copy_v(ci + 2, vring[(ci + 2) % 3]);
           wait_vmcnt<NVD>();           // all but chunk ci+2's values
         } else {
@@ -1814,16 +1854,6 @@ __device__ __forceinline__ void scan_chunk_lean(const char *recb, const E *vs, f
   }
 }
 
-// 4 bytes per lane from global memory into LDS (global_load_lds_dword; lane
-// l's bytes land at lds_base + 4 l).  Used only to pull lines into L2 ahead
-// of their copy: the LDS bytes are a landing place nothing reads.
-__device__ __forceinline__ void lds_dma4(const void *src, uint32_t lds_base) {
-  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_base);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :
-               : "v"(src), "s"(base)
-               : "memory", "m0");
-}
 
 // eight compute waves of 16 columns and four copy waves: measured against
 // four waves of 32 columns (each fragment feeding two products, one wave per
@@ -1968,22 +1998,31 @@ void unit_scan_kernel(ScanKArgs a) {
       }
     }
   };
-  // chunk ci's copies (and the touch of chunk ci + 1's value rows); returns
-  // the loads issued after the copies (the touch, which nothing waits for)
+  // chunk ci's copies (and the touch of chunk ci + 1's value rows, and with
+  // touch_ahead of its record: copiers 2 and 3 take four 8 KiB blocks each);
+  // returns the loads issued after the copies (touches, which nothing waits
+  // for)
   auto issue_copies = [&](int ci) {
     if (!copier) return 0;
     wait_rec(ci);
     copy_rec(ci, rec[ci & 1]);
     copy_v(ci, vbuf[ci & 1]);
-    if (toucher && ci + 1 < nchunks) {
+    if (ci + 1 >= nchunks) return 0;
+    if (toucher) {
       touch_v(ci + 1);
       return 1;
     }
+    if (!SCHED && a.touch_ahead && NCOPY == 4 && cpi >= 2) {
+      touch_record<4>(a.ws_records + ((size_t)(chunk0 + ci + 1) * H + h) * RS::bytes, RS::bytes, 4 * (cpi - 2),
+                      touch_lds);
+      return 4;
+    }
     return 0;
   };
-  // this wave's copies have landed (a touch issued after them may still fly)
+  // this wave's copies have landed (touches issued after them may still fly)
   auto wait_copies = [&](int touched) {
-    if (touched) wait_vmcnt<1>();
+    if (touched == 4) wait_vmcnt<4>();
+    else if (touched) wait_vmcnt<1>();
     else wait_vmcnt<0>();
   };
 
@@ -2196,6 +2235,215 @@ void launch_scan(int cw, dim3 grid, hipStream_t stream, const ScanKArgs &sa) {
   hipLaunchKernelGGL((chunk_scan_kernel<DK, E, NT, 1, NCP>), grid, dim3(64 * (1 + NCP)), 0, stream, sa);
 }
 
+// ================================================== split-sequence prefill
+// A dense batch of few long sequences leaves most of the chip idle in the
+// scan, whose chain is as long as a sequence's chunk count.  The step from
+// one chunk's start state to the next is affine in the state (in the scan's
+// terms S^T <- (D_{0:63} - Kend^T Tb Kbnd) S^T + Kend^T Tb V), so the map over
+// a segment of chunks is S_end = S_start M + X: X the segment's scan from
+// S = 0, M^T the scan of the d_k columns of the identity with V = 0.  The
+// maps of all segments but the last run at once (map_scan_kernel), a small
+// pass chains them into every segment's start state (split_chain_kernel),
+// and the scan then runs all segments at once from those states.
+
+struct MapKArgs {
+  const void *v;
+  const char *ws_records;
+  float *maps;          // per map unit (sequence, segment < G-1, head): X rows (d_v), then M^T rows (d_k), fp32 x d_k
+  int H, T, nct;        // dense batch: sequences of T tokens, nct chunks
+  int G, cps;           // segments per sequence, chunks per segment
+  int n_maps;           // B (G - 1) H
+  int touch_ahead;      // pull record ci+2 into L2 while chunk ci runs
+};
+
+// One workgroup per (map unit, group of 16 CW columns): the groups
+// 0 .. DV/WC-1 scan value columns from S = 0 (X), the rest scan columns of the
+// identity with V = 0 (M^T).  The state update alone (scan_chunk without
+// outputs), so only Kbnd, Kend^T, Tb and D_{0:63} of each record are copied.
+// Workgroups of one map unit get ids congruent mod 8 (one XCD).
+template <int CW, int NCP>
+__global__ __launch_bounds__(64 * (CW + NCP)) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void map_scan_kernel(MapKArgs a) {
+  constexpr int DK = 128, DV = 128;
+  typedef bf16 E;
+  typedef RecordShape<DK, E> RS;
+  constexpr int CT = DK / 16;
+  constexpr int WC = CW * 16;                // columns per workgroup
+  constexpr int GX = DV / WC, GM = DK / WC;  // workgroups per map unit: X columns, M columns
+  __shared__ __attribute__((aligned(1024))) char rec[2][RS::bytes];
+  __shared__ __attribute__((aligned(1024))) E vt[2][64 * WC];
+  __shared__ __attribute__((aligned(16))) char touch_area[256];
+
+  const int w = wave_id(), l = lane_id(), col = l & 15, g = l >> 4;
+  const int bid = blockIdx.x, xcd = bid & 7, slot = bid >> 3;
+  const int mu = (slot / (GX + GM)) * 8 + xcd, grp = slot % (GX + GM);
+  if (mu >= a.n_maps) return;
+  const int nm = mu / a.H, h = mu % a.H;
+  const int n = nm / (a.G - 1), sg = nm % (a.G - 1);
+  const long long tstart = (long long)n * a.T + (long long)sg * a.cps * kChunk;
+  const long long chunk0 = (long long)n * a.nct + (long long)sg * a.cps;
+  const int nchunks = a.cps;  // segments before the last are whole chunks
+  const bool ident = grp >= GX;
+  const int c0 = (ident ? grp - GX : grp) * WC;  // first value column / identity column
+  const E *V = reinterpret_cast<const E *>(a.v);
+  const size_t tok_stride = (size_t)a.H * DV;
+
+  if (w >= CW) {
+    const int cpi = w - CW;
+    // 1 KiB blocks of Kbnd, of Kend^T and Tb (adjacent), and of D_{0:63}
+    constexpr int B_KH = RS::kh / 1024, N_KH = (RS::qh - RS::kh) / 1024;
+    constexpr int B_KT = RS::ktt / 1024, N_KT = (RS::aqk - RS::ktt) / 1024;
+    constexpr int B_P = RS::p63 / 1024, N_P = (RS::bytes - RS::p63) / 1024;
+    constexpr int NB = N_KH + N_KT + N_P, QPW = (NB + NCP - 1) / NCP;
+    static_assert(RS::kh % 1024 == 0 && RS::ktt % 1024 == 0 && RS::aqk % 1024 == 0 && RS::p63 % 1024 == 0,
+                  "record parts on 1 KiB boundaries");
+    auto copy_rec = [&](int ci, char *dst) {
+      const char *src = a.ws_records + ((size_t)(chunk0 + ci) * a.H + h) * RS::bytes + l * 16;
+      const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)dst;
+#pragma unroll
+      for (int qq = 0; qq < QPW; ++qq) {
+        const int b = min(cpi * QPW + qq, NB - 1);  // clamped blocks are copied twice, same bytes
+        const int blk = b < N_KH ? B_KH + b : (b < N_KH + N_KT ? B_KT + b - N_KH : B_P + b - N_KH - N_KT);
+        lds_dma16(src + blk * 1024, lds + blk * 1024);
+      }
+    };
+    // the value columns c0 .. c0+WC-1 of chunk ci: 64 rows of WC elements,
+    // 1 KiB per copy
+    constexpr int LPR = WC * (int)sizeof(E) / 16, RPI = 64 / LPR;
+    auto copy_v = [&](int ci, E *dst) {
+      const uint32_t lds = (uint32_t)(size_t)(__attribute__((address_space(3))) E *)dst;
+#pragma unroll
+      for (int j = 0; j < 64 / RPI; ++j) {
+        const E *src = V + (size_t)(tstart + (long long)kChunk * ci + j * RPI + l / LPR) * tok_stride +
+                       (size_t)h * DV + c0 + (l % LPR) * (16 / (int)sizeof(E));
+        lds_dma16_nt(src, lds + j * 1024);
+      }
+    };
+    const bool vcopier = !ident && cpi == NCP - 1;
+    const uint32_t touch_lds = (uint32_t)(size_t)(__attribute__((address_space(3))) char *)touch_area;
+    if (nchunks > 0) {
+      copy_rec(0, rec[0]);
+      if (vcopier) copy_v(0, vt[0]);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // chunk 0 ready
+    for (int ci = 0; ci < nchunks; ++ci) {
+      // buffers (ci+1)%2 held chunk ci-1, finished before the last barrier
+      if (ci + 1 < nchunks) {
+        copy_rec(ci + 1, rec[(ci + 1) & 1]);
+        if (vcopier) copy_v(ci + 1, vt[(ci + 1) & 1]);
+      }
+      if (a.touch_ahead && cpi == 1 && !vcopier && ci + 2 < nchunks) {
+        // record ci+2 into L2: block grp of its eight 8 KiB blocks
+        touch_record<1>(a.ws_records + ((size_t)(chunk0 + ci + 2) * a.H + h) * RS::bytes, RS::bytes, grp, touch_lds);
+        wait_vmcnt<1>();  // the copies; the touch may still fly
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      __syncthreads();  // chunk ci done, chunk ci+1 ready
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+
+  // compute waves: S^T (d_k x 16 columns) in accumulator tiles, from 0 or
+  // from the identity's columns v0 .. v0+15
+  const int v0 = c0 + w * 16;
+  f32x4 st[CT][1], ov[4][1];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) st[ct][0][r] = ident && 16 * ct + 4 * g + r == v0 + col ? 1.f : 0.f;
+  __syncthreads();  // chunk 0 ready
+  for (int ci = 0; ci < nchunks; ++ci) {
+    if (ident)
+      scan_chunk<DK, E, 1, WC, false, true>(rec[ci & 1], nullptr, st, ov);
+    else
+      scan_chunk<DK, E, 1, WC, false, false>(rec[ci & 1], vt[ci & 1] + w * 16, st, ov);
+    __syncthreads();
+  }
+  float *out = a.maps + (size_t)mu * (DV + DK) * DK + (size_t)((ident ? DV : 0) + v0 + col) * DK;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4 *>(out + 16 * ct + 4 * g) = st[ct][0];
+}
+
+// Segment start states: S_0 = S0 (or zero), S_{g+1} = S_g M_g + X_g in fp32
+// (S-form, d_v x d_k; M_g's rows are the stored M^T rows, so the product is
+// sum_j S_g[r][j] Mt_g[j][c]).  Rows are independent: one workgroup per
+// (sequence, head, block of 32 rows); start is [B G H] x d_v x d_k.  Each
+// segment's Mt (64 KiB) is first brought into LDS with all its loads in
+// flight at once (read straight from memory inside the product loop, every
+// iteration waited on one load: 28 us per segment instead of a few).
+__global__ __launch_bounds__(256) void split_chain_kernel(const float *S0, const float *maps, float *start, int H,
+                                                          int G, int n_units) {
+  constexpr int DK = 128, DV = 128, RB = 32;
+  __shared__ __attribute__((aligned(16))) float sS[RB][DK];
+  __shared__ __attribute__((aligned(16))) float sM[DK][DK];
+  const int unit = blockIdx.x / (DV / RB), rb = blockIdx.x % (DV / RB);
+  if (unit >= n_units) return;  // whole workgroup
+  const int n = unit / H, h = unit % H;
+  const int t = threadIdx.x, c = t % DK, rh = t / DK;  // output column, half of the block's rows
+  auto start_row = [&](int sg, int r) { return start + (((size_t)n * G + sg) * H + h) * DV * DK + (size_t)r * DK; };
+  for (int i = t; i < RB * DK; i += 256) {
+    const int r = i / DK, k = i % DK;
+    const float x = S0 ? S0[((size_t)unit * DV + rb * RB + r) * DK + k] : 0.f;
+    sS[r][k] = x;
+    start_row(0, rb * RB + r)[k] = x;
+  }
+  for (int sg = 0; sg + 1 < G; ++sg) {
+    const float *X = maps + (((size_t)n * (G - 1) + sg) * H + h) * (size_t)(DV + DK) * DK;
+    const f32x4 *Mt4 = reinterpret_cast<const f32x4 *>(X + (size_t)DV * DK);
+    constexpr int NV = DK * DK / 4 / 256;  // 16-byte loads per thread
+    f32x4 mv[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) mv[i] = Mt4[t + 256 * i];
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = X[(size_t)(rb * RB + 16 * rh + i) * DK + c];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) reinterpret_cast<f32x4 *>(&sM[0][0])[t + 256 * i] = mv[i];
+    __syncthreads();  // sM and S_g complete
+#pragma unroll 4
+    for (int j = 0; j < DK; ++j) {
+      const float m = sM[j][c];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[i] = __builtin_fmaf(sS[16 * rh + i][j], m, acc[i]);
+    }
+    __syncthreads();  // every thread is done reading S_g and sM
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sS[16 * rh + i][c] = acc[i];
+      start_row(sg + 1, rb * RB + 16 * rh + i)[c] = acc[i];
+    }
+  }
+}
+
+// Segment tables in the packed-batch form the scan reads: segment i = n G + g
+// starts at token n T + min(g cps 64, T) and at chunk slot n nct + g cps.
+__global__ void split_tables_kernel(int32_t *tok0, int32_t *chunk0, int B, int T, int nct, int G, int cps) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= B * G; i += gridDim.x * blockDim.x) {
+    const int n = i / G, sg = i % G;
+    tok0[i] = (int32_t)((long long)n * T + min((long long)sg * cps * kChunk, (long long)T));
+    chunk0[i] = (int32_t)((long long)n * nct + (long long)sg * cps);
+  }
+}
+
+// The last segments' end states are the sequences' final states; records the
+// schedule this call ran.
+__global__ void split_final_kernel(const float *end, float *S_final, int *ctl, int B, int H, int G, int state) {
+  const size_t per = (size_t)state / 4, total = (size_t)B * H * per;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t unit = i / per, e = i % per;
+    const size_t n = unit / H, h = unit % H;
+    reinterpret_cast<f32x4 *>(S_final)[i] =
+        reinterpret_cast<const f32x4 *>(end + (((size_t)n * G + G - 1) * H + h) * state)[e];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    ctl[kCtlSchedule] = kScheduleSplit;
+    ctl[kCtlError] = 0;
+  }
+}
+
 // ================================================================ dispatch
 // CU-masked streams of the overlapped schedule, one set per device: the scan
 // on the first 128 CUs of the runtime's mask numbering (16 per XCD) and the
@@ -2361,6 +2609,97 @@ hipError_t run_prefill_overlap(const PrefillArgs &a, hipStream_t stream, PrepKAr
   return hipStreamWaitEvent(stream, ov.done_prep, 0);
 }
 
+// The two-phase scan over sa.n_units units (sa filled in but for the
+// workgroup shape).  Two compute waves of one 16-column tile each per
+// workgroup (one wave when d_v = 16 or two stages would not fit in LDS) and
+// four copy waves: measured fastest at d_v = 128 against two tiles per wave
+// (which halves the LDS reads per column but doubles each wave's serial chain
+// of products) and against one, two, three, five and six copy waves.  Past 64
+// units at d = 128 bf16, one workgroup per unit.
+template <int DK, typename E>
+hipError_t launch_scan_phase(const PrefillArgs &a, ScanKArgs sa, hipStream_t stream) {
+  if (DK == 128 && sizeof(E) == 2 && a.dv == 128 && sa.n_units > kUnitScanMinUnits) {
+    // one workgroup per unit (units in dispatch order: longest packed
+    // sequences first)
+    sa.wg_per_unit = 1;
+    hipLaunchKernelGGL((unit_scan_kernel<false, kUnitCW, kUnitCP>), dim3((unsigned)sa.n_units),
+                       dim3(64 * (kUnitCW + kUnitCP)), 0, stream, sa);
+  } else {
+    int cw = a.dv >= 32 ? 2 : 1;
+    while (cw > 1 && !scan_stage_fits<DK, E>(1, cw)) cw /= 2;
+    sa.wg_per_unit = a.dv / (16 * cw);
+    const long long slots = ((long long)sa.n_units + 7) / 8 * 8 * sa.wg_per_unit;
+    launch_scan<DK, E, 1, 4>(cw, dim3((unsigned)slots), stream, sa);
+  }
+  return hipGetLastError();
+}
+
+// Split-sequence schedule after the prep (d = 128 bf16, dense): segment
+// tables, the maps of all segments but the last, the chained start states,
+// the scan of every segment, and the final states.
+template <int DK, typename E>
+hipError_t run_split(const PrefillArgs &a, hipStream_t stream, char *records, const ChunkRecordLayout &lay) {
+  const WorkspacePlan &P = a.plan;
+  const int G = P.split.G, cps = P.split.cps, nct = (a.T + kChunk - 1) / kChunk;
+  int32_t *tok0 = reinterpret_cast<int32_t *>(a.ws + P.sp_tables);
+  int32_t *ch0 = tok0 + ((size_t)a.B * G + 1);
+  float *maps = reinterpret_cast<float *>(a.ws + P.sp_maps);
+  float *start = reinterpret_cast<float *>(a.ws + P.sp_start);
+  float *end = reinterpret_cast<float *>(a.ws + P.sp_end);
+  int *ctl = reinterpret_cast<int *>(a.ws);
+  const bool touch = (size_t)P.max_chunks * a.H * lay.bytes > ((size_t)256 << 20);
+  const void *vsrc = a.conv_q ? a.o : a.v;  // the prep left v's convolution in o
+  hipLaunchKernelGGL(split_tables_kernel, dim3(1), dim3(256), 0, stream, tok0, ch0, a.B, a.T, nct, G, cps);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  MapKArgs ma{};
+  ma.v = vsrc;
+  ma.ws_records = records;
+  ma.maps = maps;
+  ma.H = a.H;
+  ma.T = a.T;
+  ma.nct = nct;
+  ma.G = G;
+  ma.cps = cps;
+  ma.n_maps = a.B * (G - 1) * a.H;
+  ma.touch_ahead = touch;
+  constexpr int kMapCW = 2, kMapCP = 4, kMapGroups = (128 + 128) / (16 * kMapCW);
+  const dim3 mg((unsigned)((ma.n_maps + 7) / 8 * 8 * kMapGroups));
+  hipLaunchKernelGGL((map_scan_kernel<kMapCW, kMapCP>), mg, dim3(64 * (kMapCW + kMapCP)), 0, stream, ma);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  hipLaunchKernelGGL(split_chain_kernel, dim3((unsigned)(a.B * a.H * 4)), dim3(256), 0, stream, a.S0, maps, start,
+                     a.H, G, a.B * a.H);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  ScanKArgs sa{};
+  sa.v = vsrc;
+  sa.S0 = start;
+  sa.o = a.o;
+  sa.S_final = end;
+  sa.ws_records = records;
+  sa.lay = lay;
+  sa.H = a.H;
+  sa.dv = a.dv;
+  sa.T = a.T;
+  sa.nct = nct;
+  sa.seq_tok0 = tok0;
+  sa.seq_chunk0 = ch0;
+  sa.seq_order = nullptr;
+  sa.scale = a.scale;
+  sa.n_units = a.B * G * a.H;
+  sa.ctl = ctl;
+  sa.touch_ahead = touch;
+  if ((e = launch_scan_phase<DK, E>(a, sa, stream)) != hipSuccess) return e;
+
+  const int state = a.dv * a.dk;
+  const long long vec4 = (long long)a.B * a.H * state / 4;
+  hipLaunchKernelGGL(split_final_kernel, dim3((unsigned)std::min<long long>(1024, (vec4 + 255) / 256)), dim3(256), 0,
+                     stream, end, a.S_final, ctl, a.B, a.H, G, state);
+  return hipGetLastError();
+}
+
 template <int DK, typename E>
 hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
   const WorkspacePlan &P = a.plan;
@@ -2370,6 +2709,8 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
   int *ctl = reinterpret_cast<int *>(a.ws);
   const bool packed = a.cu_seqlens != nullptr;
   const int nct = (a.T + kChunk - 1) / kChunk;
+  const bool split = DK == 128 && sizeof(E) == 2 && !packed && P.split.G > 1 &&
+                     (a.schedule == kScheduleSplit || (a.schedule == kScheduleAuto && P.split.worth));
 
   if (packed) {
     hipLaunchKernelGGL(varlen_index_kernel, dim3(1), dim3(1024), 0, stream, a.cu_seqlens, P.n_seq, a.T,
@@ -2406,7 +2747,7 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     pa.v = a.v;
     pa.o = a.o;
     pa.dv = a.dv;
-    if (overlap_supported<DK, E>(a) && overlap_chosen(a, nct)) {
+    if (!split && overlap_supported<DK, E>(a) && overlap_chosen(a, nct)) {
       hipError_t e = hipSuccess;
       bool ran = false;
       {
@@ -2429,6 +2770,12 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
 
+  if constexpr (DK == 128 && sizeof(E) == 2) {
+    if (split) {
+      const hipError_t e = run_split<DK, E>(a, stream, records, lay);
+      return e != hipSuccess ? e : launch_out_post<E>(a, nullptr, stream);
+    }
+  }
   if (P.n_seq > 0) {
     ScanKArgs sa{};
     sa.v = a.conv_q ? a.o : a.v;  // the prep left v's convolution in o
@@ -2447,27 +2794,12 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     sa.scale = a.scale;
     sa.n_units = P.n_seq * a.H;
     sa.ctl = ctl;
-    // Two compute waves of one 16-column tile each per workgroup (one wave
-    // when d_v = 16 or two stages would not fit in LDS) and four copy
-    // waves: measured fastest at d_v = 128 against two tiles per wave
-    // (which halves the LDS reads per column but doubles each wave's serial
-    // chain of products) and against one, two, three, five and six copy
-    // waves.
-    if (DK == 128 && sizeof(E) == 2 && a.dv == 128 && sa.n_units > kUnitScanMinUnits) {
-      // one workgroup per unit (units in dispatch order: longest packed
-      // sequences first)
-      sa.wg_per_unit = 1;
-      hipLaunchKernelGGL((unit_scan_kernel<false, kUnitCW, kUnitCP>), dim3((unsigned)sa.n_units),
-                         dim3(64 * (kUnitCW + kUnitCP)), 0, stream, sa);
-    } else {
-      int cw = a.dv >= 32 ? 2 : 1;
-      while (cw > 1 && !scan_stage_fits<DK, E>(1, cw)) cw /= 2;
-      sa.wg_per_unit = a.dv / (16 * cw);
-      const long long slots = ((long long)sa.n_units + 7) / 8 * 8 * sa.wg_per_unit;
-      const dim3 grid((unsigned)slots);
-      launch_scan<DK, E, 1, 4>(cw, grid, stream, sa);
-    }
-    hipError_t e = hipGetLastError();
+    // records beyond the 256 MB Infinity Cache come from HBM: touch each one
+    // a step ahead (measured at d = 128 bf16 with 32 units x 256 chunks, 500
+    // MB of records: 423 -> 368 us per scan; with 125 MB of records, which
+    // stay in the cache, the touches cost 49 -> 52 us)
+    sa.touch_ahead = DK == 128 && sizeof(E) == 2 && (size_t)P.max_chunks * a.H * lay.bytes > ((size_t)256 << 20);
+    hipError_t e = launch_scan_phase<DK, E>(a, sa, stream);
     if (e != hipSuccess) return e;
   }
   return launch_out_post<E>(a, packed ? tables + P.seq_tok0 : nullptr, stream);

@@ -25,9 +25,19 @@ namespace kda {
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t) {
   ++g_calls[0];
   const WorkspacePlan &P = a.plan;
+  // the split-sequence buffers, when planned, follow the ready flags in order
+  const size_t base_end = P.ready + P.ready_bytes;
+  const size_t state = (size_t)a.dv * a.dk * sizeof(float);
+  const bool split_ok =
+      P.split.G > 1 ? (!a.cu_seqlens && P.sp_tables == base_end && P.sp_maps > P.sp_tables &&
+                       P.sp_start == P.sp_maps + (size_t)a.B * (P.split.G - 1) * a.H * (a.dv + a.dk) * a.dk * 4 &&
+                       P.sp_end == P.sp_start + (size_t)a.B * P.split.G * a.H * state &&
+                       P.total == P.sp_end + (size_t)a.B * P.split.G * a.H * state &&
+                       (long long)P.split.cps * (P.split.G - 1) < ((long long)a.T + 63) / 64)
+                    : P.total == base_end;
   const bool ok = P.tables == kCtlBytes && P.records == P.tables + P.tables_bytes &&
                   P.ready == P.records + (size_t)P.max_chunks * a.H * P.record_bytes &&
-                  P.total == P.ready + P.ready_bytes && P.record_bytes % 1024 == 0 && a.ws != nullptr &&
+                  split_ok && P.record_bytes % 1024 == 0 && a.ws != nullptr &&
                   (a.cu_seqlens ? P.ready_bytes == 0 : P.n_seq == a.B) && a.scale > 0.f &&
                   (a.dk == 16 || a.dk == 32 || a.dk == 64 || a.dk == 128);
   if (!ok) ++g_bad_plans;

@@ -55,6 +55,13 @@ def test_workspace_size(kda):
     packed = kda.chunk_fwd_workspace_size(1, 1000, 2, 64, 64, 5, kda.KDA_BF16)
     rec64 = (3 * 64 * 64 * 2 + 2 * 6 * 1024 + 64 * 4 + 1023) // 1024 * 1024
     assert packed >= (16 + 5) * 2 * rec64
+    # few long heads: the split-sequence buffers follow (here 8 segments of 128
+    # chunks: segment tables, 7 x 8 maps of (d_v + d_k) x d_k fp32, and the
+    # start and end states of 8 x 8 segments)
+    nrec = 1024 * 8
+    base = 256 + nrec * rec + (nrec * 4 + 255) // 256 * 256
+    split = 256 + 7 * 8 * 256 * 128 * 4 + 2 * 8 * 8 * 128 * 128 * 4
+    assert kda.chunk_fwd_workspace_size(1, 65536, 8, 128, 128, -1, kda.KDA_BF16) == base + split
     # invalid sizes
     assert kda.chunk_fwd_workspace_size(1, 10, 2, 48, 64, -1, kda.KDA_BF16) == 0
     assert kda.chunk_fwd_workspace_size(1, 10, 0, 64, 64, -1, kda.KDA_BF16) == 0
