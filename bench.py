@@ -41,6 +41,7 @@ MEASURED_TRAFFIC = {
     "decode": ("kda_decode.hip", "278dd0ca3f70dd05", 1_086_895_866),
     "decode_tokens": ("kda_decode.hip", "278dd0ca3f70dd05", 1_125_438_808),
     "long_context": ("kda_prefill.hip", "0", None),
+    "long_share": ("kda_prefill.hip", "0", None),
     "varlen": ("kda_prefill.hip", "0", None),
 }
 
@@ -86,7 +87,7 @@ def decode_bytes(N, H, dk, dv, esize=2):
     return units * (2 * dv * dk * 4 + (2 * dk + 2 * dv) * esize + dk * 4 + 4)
 
 
-def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None, act=0):
+def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None, act=0, module=False):
     w = inputs.WORKLOADS["prefill"]
     B, T, H, dk, dv = w["B"], w["T"], w["H"], w["dk"], w["dv"]
     steps = steps or args.steps
@@ -103,13 +104,21 @@ def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None, act
                                gate_form=gate_form)
         o = torch.empty_like(inp["v"])
         S = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
-        sets.append((inp, ws, o, S))
+        ops = {}
+        if module:
+            # random module weights (no trained ones): convolution taps, norm
+            # gains, and gate logits shaped like the output
+            g = torch.Generator(device=dev).manual_seed(100 + s)
+            ops = dict(conv=tuple(torch.randn((H, d, 4), generator=g, device=dev) * 0.5 for d in (dk, dk, dv)),
+                       norm_weight=1.0 + 0.1 * torch.randn(dv, generator=g, device=dev), norm_eps=1e-6,
+                       out_gate=torch.randn(inp["v"].shape, generator=g, device=dev).to(w["dtype"]))
+        sets.append((inp, ws, o, S, ops))
     torch.cuda.synchronize()
 
     def step(i):
-        inp, ws, o, S = sets[i % NSETS]
+        inp, ws, o, S, ops = sets[i % NSETS]
         kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], gate=gate_form, out=o,
-                      S_final=S, workspace=ws, act=act)
+                      S_final=S, workspace=ws, act=act, **ops)
 
     for i in range(args.warmup):
         step(i)
@@ -141,21 +150,24 @@ def bench_prefill(args, torch, kda, inputs, gate_form="channel", steps=None, act
                 tokens=B * T)
 
 
-def bench_long_context(args, torch, kda, inputs, steps=10, warmup=2):
-    """The long-context workload (B=1, H=32, T=65536, S0 given): one chunk
-    chain of 1024 steps per (sequence, head), under the automatic schedule
-    (which overlaps prep and scan for this shape) and under two-phase."""
-    w = inputs.WORKLOADS["long"]
+def bench_long_context(args, torch, kda, inputs, steps=10, warmup=2, name="long",
+                       others=("two_phase",), first="auto"):
+    """A long-context workload (S0 given): one chunk chain of 1024 steps per
+    (sequence, head).  `long` (B=1, H=32, T=65536) under the automatic
+    schedule (which overlaps prep and scan for this shape) and under
+    two-phase; `long_share` (its 4-head share) under the automatic schedule
+    (split-sequence) and the others for comparison."""
+    w = inputs.WORKLOADS[name]
     B, T, H, dk, dv = w["B"], w["T"], w["H"], w["dk"], w["dv"]
     dev = torch.device("cuda:0")
-    inp = inputs.workload("long", seed=0, device=dev)
+    inp = inputs.workload(name, seed=0, device=dev)
     o = torch.empty_like(inp["v"])
     S = torch.empty((B, H, dv, dk), dtype=torch.float32, device=dev)
     ws = torch.empty(kda.chunk_fwd_workspace_size(B, T, H, dk, dv, -1, kda.KDA_BF16), dtype=torch.uint8,
                      device=dev)
     stream = torch.cuda.current_stream(dev)
     out, status = {}, {}
-    for sched in ("auto", "two_phase"):
+    for sched in (first,) + tuple(others):
         prev = kda.set_schedule(sched)
         for _ in range(warmup):
             kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"], out=o,
@@ -175,15 +187,18 @@ def bench_long_context(args, torch, kda, inputs, steps=10, warmup=2):
         if status[sched][1]:
             raise RuntimeError(f"long-context {sched}: schedule error bits {status[sched][1]:#x}")
     nbytes = prefill_bytes(B, T, H, dk, dv, s0=True)
-    ach = nbytes / (out["auto"] * 1e-6) / 1e9
-    return {"workload": f"long-context prefill B={B} H={H} T={T} d_k=d_v={dk} bf16, S0 given",
-            "calls": steps, "call_us_mean": round(out["auto"], 1),
-            "schedule": status["auto"][0],
-            "call_us_two_phase": round(out["two_phase"], 1),
-            "tokens_per_s": round(B * T / (out["auto"] * 1e-6), 1),
-            "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": measured_traffic("long_context"),
-                         "algorithmic_bytes": nbytes}}
+    ach = nbytes / (out[first] * 1e-6) / 1e9
+    res = {"workload": f"long-context prefill B={B} H={H} T={T} d_k=d_v={dk} bf16, S0 given",
+           "calls": steps, "call_us_mean": round(out[first], 1),
+           "schedule": status[first][0]}
+    for sched in others:
+        res[f"call_us_{sched}"] = round(out[sched], 1)
+    res.update({"tokens_per_s": round(B * T / (out[first] * 1e-6), 1),
+                "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(ach / HBM_PEAK_GBS, 4),
+                             "traffic": measured_traffic("long_context" if name == "long" else name),
+                             "algorithmic_bytes": nbytes}})
+    return res
 
 
 def bench_varlen(args, torch, kda, inputs, steps=20, warmup=3):
@@ -378,6 +393,11 @@ def main():
                     help="skip the long-context workload (B=1 H=32 T=65536, timed under both schedules)")
     ap.add_argument("--long-only", action="store_true",
                     help="time only the long-context workload (for profiling); prints its object")
+    ap.add_argument("--long-share-only", action="store_true",
+                    help="time only the 4-head long-context share (split-sequence; for profiling)")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "two_phase", "overlap", "split"],
+                    help="with --long-only / --long-share-only: the one schedule to time (counter "
+                         "collection serialises kernels, which the overlapped schedule cannot run under)")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed-batch workload (64 sequences, H=16)")
     ap.add_argument("--varlen-only", action="store_true",
@@ -395,7 +415,17 @@ def main():
     from linear_attention_kda_amd import inputs
 
     if args.long_only:
-        print(json.dumps({"long_context": bench_long_context(args, torch, kda, inputs)}), flush=True)
+        out = {"long_context": bench_long_context(args, torch, kda, inputs, others=(), first=args.schedule)}
+        if args.copy_calib_mib:
+            out["copy_calib_bytes"] = copy_calib(args, torch)
+        print(json.dumps(out), flush=True)
+        return
+    if args.long_share_only:
+        out = {"long_context_share": bench_long_context(args, torch, kda, inputs, name="long_share", others=(),
+                                                        first=args.schedule)}
+        if args.copy_calib_mib:
+            out["copy_calib_bytes"] = copy_calib(args, torch)
+        print(json.dumps(out), flush=True)
         return
     if args.varlen_only:
         out = {"varlen": bench_varlen(args, torch, kda, inputs)}
@@ -445,10 +475,18 @@ def main():
                  ("softplus_channel", "prefill_fused_inputs",
                   "raw q, k (SiLU and unit length applied on load), beta logits (sigmoid on load), "
                   "per-channel gate logits g with alpha = exp(-softplus(g))",
+                  kda.KDA_ACT_QK_SILU_L2NORM | kda.KDA_ACT_BETA_SIGMOID),
+                 ("softplus_channel", "prefill_module_ops",
+                  "the fused inputs above after a short causal convolution of q, k and v (width 4, random taps), "
+                  "outputs through an RMS norm and a sigmoid gate (gate logits bf16, shaped like o)",
                   kda.KDA_ACT_QK_SILU_L2NORM | kda.KDA_ACT_BETA_SIGMOID))
         for form, key, what, act in forms:
-            sg = bench_prefill(args, torch, kda, inputs, gate_form=form, steps=max(20, args.steps // 4), act=act)
+            module = key == "prefill_module_ops"
+            sg = bench_prefill(args, torch, kda, inputs, gate_form=form, steps=max(20, args.steps // 4), act=act,
+                               module=module)
             sb = prefill_bytes(sg["B"], sg["T"], sg["H"], sg["dk"], sg["dv"], gate_form=form)
+            if module:  # the gate logits are read once; the weights are a few KB
+                sb += sg["B"] * sg["T"] * sg["H"] * sg["dv"] * 2
             ach = sb / (sg["call_ms_mean"] * 1e-3) / 1e9
             result[key] = {
                 "workload": f"prefill B=4 H=16 T=2048 d=128 bf16, {what}",
@@ -458,6 +496,8 @@ def main():
                              "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_bytes": sb}}
     if not args.no_long_context:
         result["long_context"] = bench_long_context(args, torch, kda, inputs)
+        result["long_context_share"] = bench_long_context(args, torch, kda, inputs, name="long_share",
+                                                          others=("two_phase", "overlap"))
     if not args.no_varlen:
         result["varlen"] = bench_varlen(args, torch, kda, inputs)
     if args.copy_calib_mib:

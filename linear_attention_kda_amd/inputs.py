@@ -11,6 +11,8 @@ Workloads (names used by tests and the benchmark):
            g ~ N(-4,1) per channel, fp32; beta = sigmoid(N(0,1)); S0 = 0
   long     B=1 H=32 T=65536 d=128, distributions of `prefill`;
            S0 ~ N(0, 0.02^2) fp32
+  long_share  `long` with H=4: one GPU's share of its heads when they are
+           split over eight GPUs
   decode   N=256 sequences, H=32, d=128; state ~ N(0, 0.02^2) fp32; per step
            q/k/v bf16 (k unit), alpha ~ U(0.95,1), beta = sigmoid(N(0,1))
   varlen   64 sequences, lengths round(lognormal(8.3, 0.6)) clipped to
@@ -34,6 +36,8 @@ WORKLOADS = {
                     gate="softplus", s0_std=None),
     "long": dict(kind="dense", B=1, H=32, T=65536, dk=128, dv=128, dtype=torch.bfloat16,
                  gate="softplus", s0_std=0.02),
+    "long_share": dict(kind="dense", B=1, H=4, T=65536, dk=128, dv=128, dtype=torch.bfloat16,
+                       gate="softplus", s0_std=0.02),
     "decode": dict(kind="decode", N=256, H=32, dk=128, dv=128, steps=1024,
                    dtype=torch.bfloat16, alpha_lo=0.95, s0_std=0.02),
     "varlen": dict(kind="packed", n_seq=64, H=16, dk=128, dv=128, dtype=torch.bfloat16,
