@@ -368,6 +368,16 @@ kda_status kda_chunk_fwd_ex(const void *q, const void *k, const void *v,
  *  out_gate  same layout and dtype as o
  *      Output gate:  o <- o * sigmoid(out_gate)  elementwise (after the norm
  *      when both are given).
+ *  conv_state  [N, H, 3, 2 d_k + d_v] dtype: the raw (unconvolved) q, k
+ *      and v of three consecutive tokens of each sequence, oldest first,
+ *      each token laid out q | k | v.  kda_chunk_fwd_module writes there,
+ *      when given, the last three tokens of each sequence (zeros for the
+ *      positions before a sequence shorter than three), which is what
+ *      kda_decode_tokens_module needs to continue it.  The decode entry point
+ *      reads it as the three tokens before its first, and replaces it by the
+ *      last three of (those, then its Tk tokens).  Optional for the prefill,
+ *      required by the decode entry point with the convolution; must not
+ *      overlap any other argument.
  * The norm and gate run in fp32 on the outputs as rounded to dtype, and
  * round once more.  In a packed batch, rows of o outside every sequence are
  * left alone.
@@ -377,6 +387,7 @@ typedef struct {
   const float *norm_weight;
   float norm_eps;
   const void *out_gate;
+  void *conv_state;
 } kda_module_ops;
 
 /*
@@ -425,6 +436,25 @@ kda_status kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
                                  int N, int B, int T, int H, int d_k, int d_v,
                                  float scale, kda_dtype dtype, void *o,
                                  float *S_final, hipStream_t stream);
+
+/*
+ * kda_decode_tokens_ex with the operations of kda_module_ops (ops may be
+ * NULL: then this is kda_decode_tokens_ex): the short convolution (its
+ * conv_state required: the three raw tokens before the launch's first,
+ * replaced by the last three; needs KDA_ACT_QK_SILU_L2NORM), then the output
+ * norm and gate on each (token, head) row.  The convolved q, k and v are
+ * rounded to dtype, as in kda_chunk_fwd_module, so a prefill followed by
+ * decode steps convolves every token as one prefill over all of them would.
+ * out_gate is [N, Tk, H, d_v] dtype.  Error returns as for
+ * kda_chunk_fwd_module, and KDA_ERR_NULL_ARG for a missing conv_state.
+ */
+kda_status kda_decode_tokens_module(const void *q, const void *k, const void *v,
+                                    const float *alpha, kda_gate gate,
+                                    const float *beta, unsigned input_act,
+                                    const kda_module_ops *ops,
+                                    const float *S_in, float *S_out, int N,
+                                    int Tk, int H, int d_k, int d_v, float scale,
+                                    kda_dtype dtype, void *o, hipStream_t stream);
 
 kda_status kda_decode_step_gated(const void *q, const void *k, const void *v,
                                  const float *alpha, kda_gate gate,

@@ -53,7 +53,8 @@ KDA_SCHED_ERR_XCD = 2
 EXPORTED = ("kda_status_string", "kda_set_validation", "kda_set_schedule", "kda_chunk_fwd_status",
             "kda_release", "kda_set_sched_wait_limit", "kda_chunk_fwd_workspace_size", "kda_chunk_fwd",
             "kda_chunk_fwd_gated", "kda_chunk_fwd_ex", "kda_decode_step", "kda_decode_step_gated",
-            "kda_decode_tokens", "kda_decode_tokens_ex", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_module")
+            "kda_decode_tokens", "kda_decode_tokens_ex", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_module",
+            "kda_decode_tokens_module")
 KDA_ERR_INVALID_VALUE = 11
 KDA_ERR_STREAM_CAPTURE = 13
 KDA_ERR_TOO_LARGE = 14
@@ -63,7 +64,8 @@ NOALLOC_SCRATCH_BYTES = 64 << 20   # the static device scratch of kda_chunk_fwd_
 class KdaModuleOps(ctypes.Structure):
     """kda_module_ops: device pointers (None: operation off) and the norm's eps."""
     _fields_ = [("conv_q", ctypes.c_void_p), ("conv_k", ctypes.c_void_p), ("conv_v", ctypes.c_void_p),
-                ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("out_gate", ctypes.c_void_p)]
+                ("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("out_gate", ctypes.c_void_p),
+                ("conv_state", ctypes.c_void_p)]
 
 
 class KdaError(RuntimeError):
@@ -116,6 +118,9 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_module.restype = i32
     lib.kda_chunk_fwd_module.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_uint, ctypes.POINTER(KdaModuleOps), vp,
                                          vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, vp, sz, vp]
+    lib.kda_decode_tokens_module.restype = i32
+    lib.kda_decode_tokens_module.argtypes = [vp, vp, vp, vp, i32, vp, ctypes.c_uint, ctypes.POINTER(KdaModuleOps),
+                                             vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, vp]
     lib.kda_release.restype = None
     lib.kda_release.argtypes = []
     lib.kda_set_sched_wait_limit.restype = ctypes.c_longlong
@@ -225,6 +230,29 @@ def _stream(device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _module_ops(torch, H, d_k, d_v, dtype, n_out, conv, norm_weight, norm_eps, out_gate, conv_state, n_state):
+    """kda_module_ops from tensors (None: off), checked for dtype and size;
+    returns (ops, tensors to keep alive during the call)."""
+    wq, wk, wv = map(_prep, conv) if conv is not None else (None, None, None)
+    for w, d in ((wq, d_k), (wk, d_k), (wv, d_v)):
+        if w is not None and (w.dtype != torch.float32 or w.numel() != H * d * 4):
+            raise ValueError("convolution taps must be float32 [H, d, 4]")
+    norm_weight = _prep(norm_weight)
+    if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d_v):
+        raise ValueError("norm_weight must be float32 [d_v]")
+    out_gate = _prep(out_gate)
+    if out_gate is not None and (out_gate.dtype != dtype or out_gate.numel() != n_out):
+        raise ValueError("out_gate must have the dtype and size of the output")
+    if conv_state is not None:
+        if (not conv_state.is_contiguous() or conv_state.dtype != dtype or conv_state.data_ptr() % 16
+                or conv_state.numel() != n_state * 3 * (2 * d_k + d_v)):
+            raise ValueError("conv_state must be a contiguous, 16-byte aligned [N, H, 3, 2 d_k + d_v] tensor "
+                             "of the inputs' dtype")
+    ops = KdaModuleOps(_ptr(wq), _ptr(wk), _ptr(wv), _ptr(norm_weight), float(norm_eps), _ptr(out_gate),
+                       _ptr(conv_state))
+    return ops, (wq, wk, wv, norm_weight, out_gate, conv_state)
+
+
 def chunk_fwd_noalloc(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gate=None, out=None,
                       S_final=None, act=0):
     """chunk_fwd through kda_chunk_fwd_noalloc: no workspace, the library's
@@ -236,7 +264,7 @@ def chunk_fwd_noalloc(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None
 
 def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gate=None, out=None,
               S_final=None, workspace=None, act=0, conv=None, norm_weight=None, norm_eps=1e-6, out_gate=None,
-              _noalloc=False):
+              conv_state=None, _noalloc=False):
     """Chunked prefill.  Returns (o, S_final).
 
     ``act``: kda_input_act flags (KDA_ACT_QK_SILU_L2NORM, KDA_ACT_BETA_SIGMOID)
@@ -246,7 +274,9 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gat
     [H, d_k, 4], [H, d_v, 4] of the short causal convolution (needs
     KDA_ACT_QK_SILU_L2NORM in ``act``); ``norm_weight`` [d_v] fp32 gains of the
     output RMS norm (with ``norm_eps``); ``out_gate`` logits of the output gate,
-    shaped and typed like the output.
+    shaped and typed like the output; ``conv_state`` (with ``conv``) an
+    [N, H, 3, 2 d_k + d_v] tensor of the inputs' dtype that receives each
+    sequence's last three raw tokens, for decode_tokens to continue from.
     Dense batch: q, k [B, T, H, d_k]; v [B, T, H, d_v]; beta [B, T, H].
     alpha: [B, T, H, d_k] (gate "channel"), [B, T, H] (gate "scalar"), or
     None (gate "none"); ``gate`` defaults to what alpha's shape says.
@@ -306,17 +336,8 @@ def chunk_fwd(q, k, v, alpha, beta, S0=None, cu_seqlens=None, scale=None, *, gat
     if workspace is None or workspace.numel() < ws_need:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
     if conv is not None or norm_weight is not None or out_gate is not None:
-        wq, wk, wv = map(_prep, conv) if conv is not None else (None, None, None)
-        for w, d in ((wq, d_k), (wk, d_k), (wv, d_v)):
-            if w is not None and (w.dtype != torch.float32 or w.numel() != H * d * 4):
-                raise ValueError("convolution taps must be float32 [H, d, 4]")
-        norm_weight = _prep(norm_weight)
-        if norm_weight is not None and (norm_weight.dtype != torch.float32 or norm_weight.numel() != d_v):
-            raise ValueError("norm_weight must be float32 [d_v]")
-        out_gate = _prep(out_gate)
-        if out_gate is not None and (out_gate.dtype != v.dtype or out_gate.numel() != v.numel()):
-            raise ValueError("out_gate must have the dtype and size of the output")
-        ops = KdaModuleOps(_ptr(wq), _ptr(wk), _ptr(wv), _ptr(norm_weight), float(norm_eps), _ptr(out_gate))
+        ops, _keep = _module_ops(torch, H, d_k, d_v, v.dtype, v.numel(), conv, norm_weight, norm_eps, out_gate,
+                                 conv_state, N * H)
         st = lib.kda_chunk_fwd_module(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), int(act),
                                       ctypes.byref(ops), _ptr(S0), _ptr(cu_seqlens), N, B, T, H, d_k, d_v,
                                       float(scale) if scale else 0.0, dt, _ptr(out), _ptr(S_final),
@@ -377,13 +398,17 @@ def decode_step(q, k, v, alpha, beta, S, scale=None, *, gate=None, out=None, act
     return out
 
 
-def decode_tokens(q, k, v, alpha, beta, S_in, S_out=None, scale=None, *, gate=None, out=None, act=0):
+def decode_tokens(q, k, v, alpha, beta, S_in, S_out=None, scale=None, *, gate=None, out=None, act=0,
+                  conv=None, conv_state=None, norm_weight=None, norm_eps=1e-6, out_gate=None):
     """Tk tokens per sequence in one launch: q, k [N, Tk, H, d_k]; v
     [N, Tk, H, d_v]; beta [N, Tk, H]; alpha [N, Tk, H, d_k] ("channel"),
     [N, Tk, H] ("scalar") or None ("none").  The state is read from S_in
     ([N, H, d_v, d_k] fp32) and the state after the last token is written to
     S_out: a new tensor by default, so S_in stays the checkpoint; pass
-    S_out=S_in to update in place.  ``act`` as for chunk_fwd.  Returns
+    S_out=S_in to update in place.  ``act`` as for chunk_fwd.  Module
+    operations as for chunk_fwd (kda_decode_tokens_module): with ``conv``,
+    ``conv_state`` [N, H, 3, 2 d_k + d_v] holds the three raw tokens before
+    the first and is replaced by the last three.  Returns
     (o [N, Tk, H, d_v], S_out)."""
     import torch
     dt = _dtype_code(q)
@@ -412,6 +437,15 @@ def decode_tokens(q, k, v, alpha, beta, S_in, S_out=None, scale=None, *, gate=No
         raise ValueError("S_out must be a contiguous, 16-byte aligned float32 tensor shaped like S_in")
     if out is None:
         out = torch.empty((N, Tk, H, d_v), dtype=v.dtype, device=q.device)
+    if conv is not None or norm_weight is not None or out_gate is not None:
+        ops, _keep = _module_ops(torch, H, d_k, d_v, v.dtype, N * Tk * H * d_v, conv, norm_weight, norm_eps,
+                                 out_gate, conv_state, N * H)
+        st = lib.kda_decode_tokens_module(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), int(act),
+                                          ctypes.byref(ops), _ptr(S_in), _ptr(S_out), N, Tk, H, d_k, d_v,
+                                          float(scale) if scale else 0.0, dt, _ptr(out), _stream(q.device))
+        if st != 0:
+            raise KdaError("kda_decode_tokens_module", st)
+        return out, S_out
     st = lib.kda_decode_tokens_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), gc, _ptr(beta), int(act),
                                   _ptr(S_in), _ptr(S_out), N, Tk, H, d_k, d_v, float(scale) if scale else 0.0,
                                   dt, _ptr(out), _stream(q.device))

@@ -162,7 +162,7 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
     workspace_bytes = 0;
     ops = nullptr;
   }
-  const kda_module_ops mo = ops ? *ops : kda_module_ops{nullptr, nullptr, nullptr, nullptr, 0.f, nullptr};
+  const kda_module_ops mo = ops ? *ops : kda_module_ops{nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr};
   const bool conv = mo.conv_q || mo.conv_k || mo.conv_v;
   if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
   if (input_act & ~kActAll) return KDA_ERR_UNSUPPORTED_ACT;
@@ -190,8 +190,9 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
   if (ntok > 0 && (!q || !k || !v || (a_bytes && !alpha) || !beta || !o)) return KDA_ERR_NULL_ARG;
   if (s_bytes > 0 && !S_final) return KDA_ERR_NULL_ARG;
   if (ntok > (size_t)INT32_MAX) return KDA_ERR_BAD_SHAPE;
-  const void *ptrs[] = {q,  k,         v, alpha, beta, S0, cu_seqlens, o, S_final, workspace, mo.conv_q, mo.conv_k,
-                        mo.conv_v, mo.norm_weight, mo.out_gate};
+  const void *ptrs[] = {q,         k,         v,         alpha,          beta,        S0,           cu_seqlens,
+                        o,         S_final,   workspace, mo.conv_q,      mo.conv_k,   mo.conv_v,    mo.norm_weight,
+                        mo.out_gate, mo.conv_state};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
 
@@ -219,6 +220,13 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
     if (overlaps(ro, rs) || overlaps(ro, rw) || overlaps(rs, rw) || overlaps(ro, rs0) || overlaps(rw, rs0))
       return KDA_ERR_ALIAS;
     if (S0 && S0 != S_final && overlaps(rs, rs0)) return KDA_ERR_ALIAS;
+    // the final convolution state (an output, with the convolution) overlaps nothing
+    if (conv && mo.conv_state) {
+      const Range rcs = range_of(mo.conv_state, (size_t)N * H * 3 * (2 * (size_t)d_k + d_v) * es);
+      for (const Range &r : ins)
+        if (overlaps(rcs, r)) return KDA_ERR_ALIAS;
+      if (overlaps(rcs, ro) || overlaps(rcs, rs) || overlaps(rcs, rw) || overlaps(rcs, rs0)) return KDA_ERR_ALIAS;
+    }
   }
   if (N == 0) return KDA_OK;
   if (noalloc)
@@ -255,6 +263,7 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
     a.conv_q = mo.conv_q;
     a.conv_k = mo.conv_k;
     a.conv_v = mo.conv_v;
+    a.conv_state = mo.conv_state;
   }
   a.norm_w = mo.norm_weight;
   a.norm_eps = mo.norm_eps;
@@ -412,7 +421,7 @@ kda_status kda_decode_step_gated(const void *q, const void *k, const void *v, co
                                          dtype, nullptr, 0, 0, stream))
     return st;
 
-  kda::DecodeArgs a;
+  kda::DecodeArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -440,12 +449,17 @@ kda_status kda_decode_tokens(const void *q, const void *k, const void *v, const 
                               dtype, o, stream);
 }
 
-kda_status kda_decode_tokens_ex(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
-                                const float *beta, unsigned input_act, const float *S_in, float *S_out, int N,
-                                int Tk, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
-                                hipStream_t stream) {
+kda_status kda_decode_tokens_module(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                                    const float *beta, unsigned input_act, const kda_module_ops *ops,
+                                    const float *S_in, float *S_out, int N, int Tk, int H, int d_k, int d_v,
+                                    float scale, kda_dtype dtype, void *o, hipStream_t stream) {
+  const kda_module_ops mo = ops ? *ops : kda_module_ops{nullptr, nullptr, nullptr, nullptr, 0.f, nullptr, nullptr};
+  const bool conv = mo.conv_q || mo.conv_k || mo.conv_v;
   if (!valid_gate(gate)) return KDA_ERR_UNSUPPORTED_GATE;
   if (input_act & ~kActAll) return KDA_ERR_UNSUPPORTED_ACT;
+  if (conv && !(mo.conv_q && mo.conv_k && mo.conv_v && mo.conv_state)) return KDA_ERR_NULL_ARG;
+  if (conv && !(input_act & KDA_ACT_QK_SILU_L2NORM)) return KDA_ERR_UNSUPPORTED_ACT;
+  if (mo.norm_weight && !(mo.norm_eps >= 0.f)) return KDA_ERR_BAD_SHAPE;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
   if (N < 0 || H <= 0 || Tk < 0) return KDA_ERR_BAD_SHAPE;
@@ -456,7 +470,8 @@ kda_status kda_decode_tokens_ex(const void *q, const void *k, const void *v, con
   if (gate == KDA_GATE_NONE) alpha = nullptr;
   if (!S_in || !S_out) return KDA_ERR_NULL_ARG;
   if (toks > 0 && (!q || !k || !v || (gate != KDA_GATE_NONE && !alpha) || !beta || !o)) return KDA_ERR_NULL_ARG;
-  const void *ptrs[] = {q, k, v, alpha, beta, S_in, S_out, o};
+  const void *ptrs[] = {q,         k,         v,         alpha,          beta,        S_in,         S_out, o,
+                        mo.conv_q, mo.conv_k, mo.conv_v, mo.norm_weight, mo.out_gate, mo.conv_state};
   for (const void *p : ptrs)
     if (p && !aligned16(p)) return KDA_ERR_MISALIGNED;
   const size_t es = dtype == KDA_BF16 ? 2 : 4;
@@ -465,6 +480,26 @@ kda_status kda_decode_tokens_ex(const void *q, const void *k, const void *v, con
   const size_t s_bytes = units * d_v * d_k * sizeof(float);
   // the state is updated in place or written to a disjoint buffer
   if (S_in != S_out && overlaps(range_of(S_in, s_bytes), range_of(S_out, s_bytes))) return KDA_ERR_ALIAS;
+  // the convolution state (read and rewritten) must not overlap any other
+  // argument; the module weights and gate logits (inputs) must not overlap
+  // an output
+  {
+    // (a range of size 0 overlaps nothing)
+    const Range rcs = range_of(mo.conv_state, conv ? units * 3 * (2 * (size_t)d_k + d_v) * es : 0);
+    const Range ro = range_of(o, toks * d_v * es), rso = range_of(S_out, s_bytes);
+    const Range rw[] = {range_of(mo.conv_q, conv ? (size_t)H * d_k * 4 * sizeof(float) : 0),
+                        range_of(mo.conv_k, conv ? (size_t)H * d_k * 4 * sizeof(float) : 0),
+                        range_of(mo.conv_v, conv ? (size_t)H * d_v * 4 * sizeof(float) : 0),
+                        range_of(mo.norm_weight, mo.norm_weight ? (size_t)d_v * sizeof(float) : 0),
+                        range_of(mo.out_gate, mo.out_gate ? toks * d_v * es : 0)};
+    const Range args[] = {range_of(q, toks * d_k * es), range_of(k, toks * d_k * es),
+                          range_of(v, toks * d_v * es), range_of(alpha, alpha ? a_bytes : 0),
+                          range_of(beta, toks * sizeof(float)), range_of(S_in, s_bytes), rso, ro};
+    for (const Range &r : args)
+      if (overlaps(rcs, r)) return KDA_ERR_ALIAS;
+    for (const Range &x : rw)
+      if (overlaps(x, rcs) || overlaps(x, ro) || overlaps(x, rso)) return KDA_ERR_ALIAS;
+  }
   if (toks > 0) {
     // o and S_out must not overlap each other or an input (S_out == S_in is
     // the in-place update, checked above)
@@ -480,7 +515,7 @@ kda_status kda_decode_tokens_ex(const void *q, const void *k, const void *v, con
       return st;
   }
 
-  kda::DecodeArgs a;
+  kda::DecodeArgs a{};
   a.q = q;
   a.k = k;
   a.v = v;
@@ -498,7 +533,24 @@ kda_status kda_decode_tokens_ex(const void *q, const void *k, const void *v, con
   a.Tk = Tk;
   a.scale = default_scale(scale, d_k);
   a.bf16 = dtype == KDA_BF16;
+  if (conv) {
+    a.conv_q = mo.conv_q;
+    a.conv_k = mo.conv_k;
+    a.conv_v = mo.conv_v;
+    a.conv_state = mo.conv_state;
+  }
+  a.norm_w = mo.norm_weight;
+  a.norm_eps = mo.norm_eps;
+  a.out_gate = mo.out_gate;
   return kda::launch_decode(a, stream) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_decode_tokens_ex(const void *q, const void *k, const void *v, const float *alpha, kda_gate gate,
+                                const float *beta, unsigned input_act, const float *S_in, float *S_out, int N,
+                                int Tk, int H, int d_k, int d_v, float scale, kda_dtype dtype, void *o,
+                                hipStream_t stream) {
+  return kda_decode_tokens_module(q, k, v, alpha, gate, beta, input_act, nullptr, S_in, S_out, N, Tk, H, d_k, d_v,
+                                  scale, dtype, o, stream);
 }
 
 }  // extern "C"

@@ -42,6 +42,11 @@ struct DecodeKArgs {
   unsigned act;    // kAct* input activations
   unsigned units;  // sequences x heads (< 2^31)
   int H, Tk;     // heads; tokens per sequence (inputs are [N, Tk, H, .])
+  // CONV instantiations: convolution taps [H, d, kConvTaps] of q, k, v and
+  // the convolution state [units, 3, 2 d_k + d_v] (the three raw tokens
+  // before the launch's first, q | k | v; read only here)
+  const float *conv_q, *conv_k, *conv_v;
+  const void *conv_state;
 };
 
 template <typename E>
@@ -98,11 +103,19 @@ __device__ __forceinline__ void consume(const TokIn<NI> &x) {
 // 265 us with 8 KiB per workgroup, 229 with 16, 221-227 with 32 and 272 with
 // 64 (occupancy two waves per SIMD).
 constexpr int kMultiAPW = 32;
-template <int DK, int DV, int G> using DecodeShapeG = DecodeShape<DK, DV, G == 1 ? 8 : kMultiAPW>;
+// With the convolution each lane also holds the taps of its rows and a window
+// of four tokens per input: two rows per lane (8 KiB per workgroup) keep that
+// in registers.
+template <int DK, int DV, int G, bool CONV = false>
+using DecodeShapeG = DecodeShape<DK, DV, (G == 1 || CONV) ? 8 : kMultiAPW>;
 
-template <int DK, int DV, typename E, int GATE, int G>
+// CONV: q, k and v go through the short causal convolution (the token and the
+// three before it, the first three from the convolution state) before
+// anything else, each result rounded to E as the prefill rounds it.
+template <int DK, int DV, typename E, int GATE, int G, bool CONV = false>
 __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
-  typedef DecodeShapeG<DK, DV, G> SH;
+  typedef DecodeShapeG<DK, DV, G, CONV> SH;
+  static_assert(!CONV || G > 1, "the convolution runs in the multi-token kernel");
   constexpr int LPR = DK / 4;                 // lanes per state row
   constexpr int RPA = 64 / LPR;               // rows per wave-wide KiB access
   constexpr int NI = SH::NI;                  // accesses per wave
@@ -138,6 +151,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     rows[i] = (part * SH::APW + (valid[i] ? acc : 0)) * RPA + rsub;
   }
 
+  // CONV: the taps of this lane's channels and rows, and where a token's raw
+  // inputs are (t >= 0: the launch's inputs; t in -3..-1: the state)
+  constexpr int CW = 2 * DK + DV;  // elements per token of the convolution state
+  f32x4 wk[4], wq[4], wv[NI];
+  if constexpr (CONV) {
+    const int h = (int)(u % (unsigned)a.H);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      wk[j] = *reinterpret_cast<const f32x4 *>(a.conv_k + ((size_t)h * DK + c0 + j) * kConvTaps);
+      wq[j] = *reinterpret_cast<const f32x4 *>(a.conv_q + ((size_t)h * DK + c0 + j) * kConvTaps);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      wv[i] = *reinterpret_cast<const f32x4 *>(a.conv_v + ((size_t)h * DV + rows[i]) * kConvTaps);
+  }
+  const E *cstate = CONV ? reinterpret_cast<const E *>(a.conv_state) + (size_t)u * 3 * CW : nullptr;
+  auto raw_k = [&](int t) {
+    return t >= 0 ? reinterpret_cast<const E *>(a.k) + tok_index(t) * DK : cstate + (size_t)(3 + t) * CW + DK;
+  };
+  auto raw_q = [&](int t) {
+    return t >= 0 ? reinterpret_cast<const E *>(a.q) + tok_index(t) * DK : cstate + (size_t)(3 + t) * CW;
+  };
+  auto raw_v = [&](int t) {
+    return t >= 0 ? reinterpret_cast<const E *>(a.v) + tok_index(t) * DV : cstate + (size_t)(3 + t) * CW + 2 * DK;
+  };
+
   // the inputs of G tokens are requested together, so a group costs one
   // memory latency; indexes past the last token re-read the last token
   TokIn<NI> x[G];
@@ -146,8 +185,28 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     for (int g = 0; g < G; ++g) {
       const int t = min(t0 + g, Tk - 1);
       const size_t ix = tok_index(t);
-      load4<E>(reinterpret_cast<const E *>(a.k) + ix * DK + c0, x[g].kk);
-      load4<E>(reinterpret_cast<const E *>(a.q) + ix * DK + c0, x[g].qq);
+      if constexpr (CONV) {
+        float xk[kConvTaps][4], xq[kConvTaps][4], xv[kConvTaps][NI];
+#pragma unroll
+        for (int i = 0; i < kConvTaps; ++i) {
+          const int tt = t - (kConvTaps - 1) + i;
+          load4<E>(raw_k(tt) + c0, xk[i]);
+          load4<E>(raw_q(tt) + c0, xq[i]);
+          const E *vr = raw_v(tt);
+#pragma unroll
+          for (int r = 0; r < NI; ++r) xv[i][r] = (float)vr[rows[r]];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[g].kk[j] = (float)(E)conv_taps(wk[j], xk[0][j], xk[1][j], xk[2][j], xk[3][j]);
+          x[g].qq[j] = (float)(E)conv_taps(wq[j], xq[0][j], xq[1][j], xq[2][j], xq[3][j]);
+        }
+#pragma unroll
+        for (int r = 0; r < NI; ++r) x[g].vv[r] = (float)(E)conv_taps(wv[r], xv[0][r], xv[1][r], xv[2][r], xv[3][r]);
+      } else {
+        load4<E>(reinterpret_cast<const E *>(a.k) + ix * DK + c0, x[g].kk);
+        load4<E>(reinterpret_cast<const E *>(a.q) + ix * DK + c0, x[g].qq);
+      }
       if constexpr (gate_per_channel(GATE)) {
         load4<float>(a.alpha + ix * DK + c0, x[g].al);
       } else {
@@ -156,9 +215,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
         for (int j = 0; j < 4; ++j) x[g].al[j] = al;
       }
       x[g].beta = a.beta[ix];
-      const E *vrow = reinterpret_cast<const E *>(a.v) + ix * DV;
+      if constexpr (!CONV) {
+        const E *vrow = reinterpret_cast<const E *>(a.v) + ix * DV;
 #pragma unroll
-      for (int i = 0; i < NI; ++i) x[g].vv[i] = (float)vrow[rows[i]];
+        for (int i = 0; i < NI; ++i) x[g].vv[i] = (float)vrow[rows[i]];
+      }
     }
   };
   // this lane's state rows stay in registers across the tokens: one read and
@@ -247,6 +308,37 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     if (valid[i]) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4 *>(Sout + (size_t)rows[i] * DK + c0));
 }
 
+// The convolution state after a launch: the last three raw tokens of (the
+// three before the launch, then its Tk tokens), per (sequence, head).  A
+// thread owns one channel of a unit and reads its three old values before
+// writing, so the update is in place.
+template <typename E>
+__global__ __launch_bounds__(256) void conv_state_advance_kernel(const E *q, const E *k, const E *v, E *cs, int H,
+                                                                 int dk, int dv, int Tk, unsigned units) {
+  const unsigned u = blockIdx.x;
+  if (u >= units) return;
+  const int W = 2 * dk + dv;
+  const size_t n = u / (unsigned)H, h = u % (unsigned)H;
+  E *st = cs + (size_t)u * 3 * W;
+  for (int c = threadIdx.x; c < W; c += blockDim.x) {
+    E old[3];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) old[s] = st[(size_t)s * W + c];
+#pragma unroll
+    for (int s = 0; s < 3; ++s) {
+      const int wi = Tk + s;  // position in (old 0..2, then the Tk tokens)
+      E x;
+      if (wi < 3) {
+        x = old[wi];
+      } else {
+        const size_t th = (n * Tk + (wi - 3)) * H + h;
+        x = c < dk ? q[th * dk + c] : (c < 2 * dk ? k[th * dk + c - dk] : v[th * dv + c - 2 * dk]);
+      }
+      st[(size_t)s * W + c] = x;
+    }
+  }
+}
+
 // tokens whose inputs are requested together: two measured faster than four
 // (with eight rows per lane: 125 VGPRs and four waves per SIMD against 171
 // and two; 221-227 against 263 us per four-token launch on the decode
@@ -259,7 +351,11 @@ hipError_t run_decode_dv(const DecodeArgs &a, const DecodeKArgs &ka, hipStream_t
   if ((units + 7) / 8 * 8 * DecodeShape<DK, 128>::SPLIT > 0x7fffffffull) return hipErrorInvalidConfiguration;
 #define KDA_DECODE_LAUNCH(DV)                                                                          \
   {                                                                                                    \
-    if (a.Tk == 1) {                                                                                   \
+    if (a.conv_q) {                                                                                    \
+      const dim3 grid((unsigned)((units + 7) / 8 * 8 * DecodeShapeG<DK, DV, kTokGroup, true>::SPLIT)); \
+      hipLaunchKernelGGL((decode_kernel<DK, DV, E, GATE, kTokGroup, true>), grid, dim3(kThreads), 0, s,  \
+                         ka);                                                                          \
+    } else if (a.Tk == 1) {                                                                            \
       const dim3 grid((unsigned)((units + 7) / 8 * 8 * DecodeShapeG<DK, DV, 1>::SPLIT));               \
       hipLaunchKernelGGL((decode_kernel<DK, DV, E, GATE, 1>), grid, dim3(kThreads), 0, s, ka);          \
     } else {                                                                                           \
@@ -295,14 +391,23 @@ hipError_t run_decode_gate(const DecodeArgs &a, const DecodeKArgs &ka, hipStream
 template <typename E>
 hipError_t run_decode(const DecodeArgs &a, hipStream_t s) {
   DecodeKArgs ka{a.q, a.k, a.v, a.alpha, a.beta, a.S_in, a.S, a.o, a.scale, a.act, (unsigned)((size_t)a.N * a.H),
-                 a.H, a.Tk};
+                 a.H, a.Tk, a.conv_q, a.conv_k, a.conv_v, a.conv_state};
+  hipError_t e = hipErrorInvalidValue;
   switch (a.dk) {
-    case 16: return run_decode_gate<16, E>(a, ka, s);
-    case 32: return run_decode_gate<32, E>(a, ka, s);
-    case 64: return run_decode_gate<64, E>(a, ka, s);
-    case 128: return run_decode_gate<128, E>(a, ka, s);
+    case 16: e = run_decode_gate<16, E>(a, ka, s); break;
+    case 32: e = run_decode_gate<32, E>(a, ka, s); break;
+    case 64: e = run_decode_gate<64, E>(a, ka, s); break;
+    case 128: e = run_decode_gate<128, E>(a, ka, s); break;
   }
-  return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  if (a.conv_q) {  // after the step has read the state
+    hipLaunchKernelGGL(conv_state_advance_kernel<E>, dim3((unsigned)((size_t)a.N * a.H)), dim3(256), 0, s,
+                       reinterpret_cast<const E *>(a.q), reinterpret_cast<const E *>(a.k),
+                       reinterpret_cast<const E *>(a.v), reinterpret_cast<E *>(a.conv_state), a.H, a.dk, a.dv, a.Tk,
+                       (unsigned)((size_t)a.N * a.H));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return launch_out_norm_gate(a.o, a.out_gate, a.norm_w, a.norm_eps, a.H, (long long)a.N * a.Tk, a.dv, a.bf16, s);
 }
 
 }  // namespace

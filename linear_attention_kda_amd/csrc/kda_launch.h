@@ -212,6 +212,7 @@ struct PrefillArgs {
   const float *norm_w;
   const void *out_gate;
   float norm_eps;
+  void *conv_state;  // with the convolution: the last three raw tokens per (sequence, head), written (optional)
 };
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream);
@@ -259,7 +260,20 @@ struct DecodeArgs {
   int Tk;             // tokens per sequence (1 for a single step)
   float scale;
   bool bf16;
+  // module operations (kda_module_ops), optional: convolution taps of q, k
+  // and v with the convolution state [N, H, 3, 2 d_k + d_v] (read, then
+  // replaced), output norm gains and gate logits
+  const float *conv_q, *conv_k, *conv_v;
+  void *conv_state;
+  const float *norm_w;
+  const void *out_gate;
+  float norm_eps;
 };
+
+// The output norm and gate pass of the module operations over n_tok x H rows
+// of d_v values of o (gate logits of the same layout), on `stream`.
+hipError_t launch_out_norm_gate(void *o, const void *gate, const float *w, float eps, int H, long long n_tok, int dv,
+                                bool is_bf16, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 

@@ -2156,19 +2156,21 @@ __global__ __launch_bounds__(kThreads) void out_norm_gate_kernel(void *o, const 
   __builtin_nontemporal_store(out, reinterpret_cast<RV *>(po));
 }
 
+// The norm and gate pass over n_tok x H rows (n_tok: an upper bound when
+// seq_tok0 gives the rows' range).
 template <typename E>
-hipError_t launch_out_post(const PrefillArgs &a, const int32_t *seq_tok0, hipStream_t stream) {
-  if (!a.norm_w && !a.out_gate) return hipSuccess;
-  const long long n_tok = seq_tok0 ? a.T : (long long)a.B * a.T;
+hipError_t launch_norm_gate_rows(void *o, const void *gate, const float *w, float eps, int H, long long n_tok, int dv,
+                                 const int32_t *seq_tok0, int n_seq, hipStream_t stream) {
+  if (!w && !gate) return hipSuccess;
   constexpr int VE = Row16<E>::N;
-  const int lpr = a.dv / VE;
-  const long long rows = n_tok * a.H;
+  const int lpr = dv / VE;
+  const long long rows = n_tok * H;
   if (rows == 0) return hipSuccess;
   const dim3 grid((unsigned)((rows * lpr + kThreads - 1) / kThreads));
-#define KDA_POST(L)                                                                                           \
-  case L:                                                                                                     \
-    hipLaunchKernelGGL((out_norm_gate_kernel<E, L>), grid, dim3(kThreads), 0, stream, a.o, a.out_gate, a.norm_w, \
-                       a.norm_eps, a.H, n_tok, seq_tok0, a.plan.n_seq);                                       \
+#define KDA_POST(L)                                                                                            \
+  case L:                                                                                                      \
+    hipLaunchKernelGGL((out_norm_gate_kernel<E, L>), grid, dim3(kThreads), 0, stream, o, gate, w, eps, H, n_tok, \
+                       seq_tok0, n_seq);                                                                       \
     break;
   switch (lpr) {
     KDA_POST(2)
@@ -2180,6 +2182,41 @@ hipError_t launch_out_post(const PrefillArgs &a, const int32_t *seq_tok0, hipStr
   }
 #undef KDA_POST
   return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_out_post(const PrefillArgs &a, const int32_t *seq_tok0, hipStream_t stream) {
+  const long long n_tok = seq_tok0 ? a.T : (long long)a.B * a.T;
+  return launch_norm_gate_rows<E>(a.o, a.out_gate, a.norm_w, a.norm_eps, a.H, n_tok, a.dv, seq_tok0, a.plan.n_seq,
+                                  stream);
+}
+
+// The convolution state at the end of a prefill (kda_module_ops.conv_state):
+// the last three raw tokens of each (sequence, head), oldest first, q | k | v
+// per token, zeros for positions before the sequence's first token.  One
+// workgroup per unit; sequences from the packed tables when given.
+template <typename E>
+__global__ __launch_bounds__(256) void conv_state_kernel(const E *q, const E *k, const E *v, E *cs, int H, int dk,
+                                                         int dv, int T, const int32_t *seq_tok0, int n_units) {
+  const int unit = blockIdx.x;
+  if (unit >= n_units) return;
+  const int n = unit / H, h = unit % H, W = 2 * dk + dv;
+  long long tb = (long long)n * T, te = tb + T;
+  if (seq_tok0) {
+    tb = seq_tok0[n];
+    te = seq_tok0[n + 1];
+  }
+  E *out = cs + (size_t)unit * 3 * W;
+  for (int i = threadIdx.x; i < 3 * W; i += blockDim.x) {
+    const int slot = i / W, c = i % W;
+    const long long t = te - 3 + slot;
+    E x = (E)0.f;
+    if (t >= tb) {
+      const size_t th = (size_t)t * H + h;
+      x = c < dk ? q[th * dk + c] : (c < 2 * dk ? k[th * dk + c - dk] : v[th * dv + c - 2 * dk]);
+    }
+    out[i] = x;
+  }
 }
 
 // Zeroes the control words and the ready words of the overlapped schedule
@@ -2778,6 +2815,14 @@ hipError_t run_prefill(const PrefillArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (a.conv_q && a.conv_state && P.n_seq > 0) {
+    hipLaunchKernelGGL(conv_state_kernel<E>, dim3((unsigned)(P.n_seq * a.H)), dim3(256), 0, stream,
+                       reinterpret_cast<const E *>(a.q), reinterpret_cast<const E *>(a.k),
+                       reinterpret_cast<const E *>(a.v), reinterpret_cast<E *>(a.conv_state), a.H, a.dk, a.dv, a.T,
+                       packed ? tables + P.seq_tok0 : nullptr, P.n_seq * a.H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 
   if constexpr (DK == 128 && sizeof(E) == 2) {
     if (split) {
@@ -2880,6 +2925,12 @@ void release_overlap() {
 
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t stream) {
   return a.bf16 ? run_prefill_dk<bf16>(a, stream) : run_prefill_dk<float>(a, stream);
+}
+
+hipError_t launch_out_norm_gate(void *o, const void *gate, const float *w, float eps, int H, long long n_tok, int dv,
+                                bool is_bf16, hipStream_t stream) {
+  return is_bf16 ? launch_norm_gate_rows<bf16>(o, gate, w, eps, H, n_tok, dv, nullptr, 0, stream)
+                 : launch_norm_gate_rows<float>(o, gate, w, eps, H, n_tok, dv, nullptr, 0, stream);
 }
 
 }  // namespace kda

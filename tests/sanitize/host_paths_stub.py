@@ -81,10 +81,12 @@ def test_decode_calls(Tk, inplace):
     st = kda.lib.kda_decode_step(P(p["q"]), P(p["k"]), P(p["v"]), P(p["alpha"]), P(p["beta"]), P(p["S"]), 256,
                                  32, 128, 128, 0.0, 1, P(p["o"]), None)
     assert st == 0
+    assert kda.lib.kda_stub_calls(4) == 0, "the plain step passed module operations to the launcher"
     S_out = p["S"] if inplace else p["S0"]
     st = kda.lib.kda_decode_tokens_ex(P(p["q"]), P(p["k"]), P(p["v"]), P(p["alpha"]), 0, P(p["beta"]), 3,
                                       P(p["S"]), P(S_out), 256, Tk, 32, 128, 128, 0.0, 1, P(p["o"]), None)
     assert st == 0
+    assert kda.lib.kda_stub_calls(4) == 0
     assert kda.lib.kda_stub_calls(1) == 2
 
 

@@ -18,6 +18,7 @@
 namespace {
 int g_calls[3];        // prefill, decode, validation
 int g_bad_plans;       // plans that failed a consistency check
+bool g_last_decode_module;  // the last decode launch carried a module operation
 }  // namespace
 
 namespace kda {
@@ -47,6 +48,10 @@ hipError_t launch_prefill(const PrefillArgs &a, hipStream_t) {
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t) {
   ++g_calls[1];
   if (a.N <= 0 || a.H <= 0 || a.Tk < 0 || !a.S || !a.S_in || a.scale <= 0.f) ++g_bad_plans;
+  // the module operations: all convolution pointers or none
+  const bool any_conv = a.conv_q || a.conv_k || a.conv_v || a.conv_state;
+  if (any_conv && !(a.conv_q && a.conv_k && a.conv_v && a.conv_state)) ++g_bad_plans;
+  g_last_decode_module = any_conv || a.norm_w || a.out_gate;
   return hipSuccess;
 }
 
@@ -70,13 +75,16 @@ hipError_t scratch_address(void **ptr) {
 extern "C" {
 
 // which: 0 prefill launches, 1 decode launches, 2 validation runs, 3 plans
-// that failed a consistency check; -1 resets every count
+// that failed a consistency check, 4 whether the last decode launch carried
+// a module operation; -1 resets every count
 int kda_stub_calls(int which) {
   if (which < 0) {
     std::memset(g_calls, 0, sizeof(g_calls));
     g_bad_plans = 0;
+    g_last_decode_module = false;
     return 0;
   }
+  if (which == 4) return g_last_decode_module ? 1 : 0;
   return which < 3 ? g_calls[which] : g_bad_plans;
 }
 
