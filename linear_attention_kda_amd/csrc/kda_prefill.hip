@@ -2026,16 +2026,48 @@ void unit_scan_kernel(ScanKArgs a) {
     else wait_vmcnt<0>();
   };
 
+  // CP > 0: chunk ci's outputs, staged by the compute waves in chunk ci's
+  // value slot (row-major like the values), to o.  Copier cpi takes rows
+  // 16 cpi .. 16 cpi + 15, the rows its next value copy refills, 16 bytes per
+  // lane through a buffer descriptor clipped to the chunk's valid rows.
+  // (Written straight from the compute waves as 2-byte stores, the outputs
+  // cost 1.6 times their bytes in write traffic on the packed workload.)
+  auto store_staged = [&](int ci) {
+    const long long t0 = tstart + (long long)kChunk * ci;
+    const int L = (int)min((long long)kChunk, ntok - (long long)kChunk * ci);
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        O + (size_t)t0 * tok_stride, 0, (int)((size_t)L * tok_stride * sizeof(E)), 0x00020000);
+    constexpr int RPC = 64 / NCOPY;  // rows per copier
+    f32x4 vals[RPC / 4];
+#pragma unroll
+    for (int jj = 0; jj < RPC / 4; ++jj) {
+      const int row = RPC * cpi + 4 * jj + (l >> 4);
+      vals[jj] = *reinterpret_cast<const f32x4 *>(vbuf[ci & 1] + row * VROW + (l & 15) * 16);
+    }
+#pragma unroll
+    for (int jj = 0; jj < RPC / 4; ++jj) {
+      const int row = RPC * cpi + 4 * jj + (l >> 4);
+      const int off = (int)(((size_t)row * tok_stride + (size_t)h * DV) * sizeof(E)) + (l & 15) * 16;
+      __builtin_amdgcn_raw_buffer_store_b128(
+          __builtin_bit_cast(__attribute__((__vector_size__(16))) unsigned int, vals[jj]), rs, off, 0, 2);
+    }
+  };
+
   if constexpr (CP > 0) {
     if (copier) {
+      static_assert(64 % (4 * NCOPY) == 0 && VROW == 16 * 16, "copier rows cover 16-lane row segments");
       int touched = nchunks > 0 ? issue_copies(0) : 0;
       wait_copies(touched);
       __syncthreads();  // chunk 0 ready
       for (int ci = 0; ci < nchunks; ++ci) {
+        // chunk ci-1's outputs sit in the value slot the copies below refill
+        // (this copier's rows); their loads into registers come first
+        if (ci > 0) store_staged(ci - 1);
         touched = ci + 1 < nchunks ? issue_copies(ci + 1) : 0;
         wait_copies(touched);
-        __syncthreads();  // chunk ci done, chunk ci+1 ready
+        __syncthreads();  // chunk ci done and staged, chunk ci+1 ready
       }
+      if (nchunks > 0) store_staged(nchunks - 1);
       __builtin_amdgcn_s_waitcnt(0);
       return;
     }
@@ -2091,7 +2123,19 @@ void unit_scan_kernel(ScanKArgs a) {
         __hip_atomic_fetch_or(a.ctl + kCtlError, kSchedErrXcd, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     scan_chunk_lean<DK, E, NT, DV>(recb, reinterpret_cast<const E *>(vbuf[ci & 1]) + v0, st, ov);
-    store_o(ci, ov);
+    if constexpr (CP > 0) {
+      // into this chunk's value slot, over this wave's own columns (which
+      // only this wave read)
+      E *ot = reinterpret_cast<E *>(vbuf[ci & 1]);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ot[(16 * I + 4 * g + r) * DV + v0 + 16 * nt + col] = from_f<E>(ov[I][nt][r]);
+    } else {
+      store_o(ci, ov);
+    }
     if (CP == 0) wait_copies(touched);
     __syncthreads();  // chunk ci done, chunk ci+1 ready
   }
