@@ -449,8 +449,8 @@ __device__ __forceinline__ void tile_ij(int p, int &I, int &J) {
 // convolution is written to o, from where the scan reads it in place of v
 // (the scan reads the rows of a chunk before it writes that chunk's outputs
 // over them).
-template <int DK, typename E, int GATE, bool ACTQK, bool SCHED = false, bool CONV = false>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrepKArgs a) {
+template <int DK, typename E, int GATE, bool ACTQK, bool SCHED, bool CONV>
+__device__ __forceinline__ void chunk_prep_body(const PrepKArgs &a) {
   typedef LdsFrag<E, DK, 64> LK;   // Kbnd, Qbnd, k / a: rows = tokens, K = d_k
   typedef LdsFrag<E, 64, DK> LT;   // Kend^T: rows = channels, K = tokens
   typedef Four<E> F4;
@@ -1039,6 +1039,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   if (threadIdx.x == 0)
     __hip_atomic_fetch_or(a.ready + (size_t)u * a.ready_words + (ci >> 5), 1 << (ci & 31), __ATOMIC_RELAXED,
                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int DK, typename E, int GATE, bool ACTQK, bool SCHED = false>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void chunk_prep_kernel(PrepKArgs a) {
+  chunk_prep_body<DK, E, GATE, ACTQK, SCHED, false>(a);
+}
+
+// With the convolution the prep holds each lane's window of raw rows and the
+// taps besides its usual values: at three waves per SIMD that spilled up to
+// 39 registers; at two it spills none and was faster (prefill workload with
+// the block's operations: 102.4 -> 95.6 us per prep; the prep without the
+// convolution went the other way, 63.0 -> 70.5, so it keeps three).
+template <int DK, typename E, int GATE>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void chunk_prep_conv_kernel(PrepKArgs a) {
+  chunk_prep_body<DK, E, GATE, true, false, true>(a);
 }
 
 // ======================================================= kernel 2: chunk scan
@@ -2281,30 +2296,21 @@ __global__ void sched_clear_kernel(int *ctl, int *ready, int n_ready) {
 // the convolution).
 template <int DK, typename E, bool ACTQK, bool SCHED = false, bool CONV = false>
 void launch_prep(int gate, dim3 grid, hipStream_t stream, const PrepKArgs &pa) {
+#define KDA_PREP_LAUNCH(G)                                                                                         \
+  if constexpr (CONV)                                                                                              \
+    hipLaunchKernelGGL((chunk_prep_conv_kernel<DK, E, G>), grid, dim3(kThreads), 0, stream, pa);                   \
+  else                                                                                                             \
+    hipLaunchKernelGGL((chunk_prep_kernel<DK, E, G, ACTQK, SCHED>), grid, dim3(kThreads), 0, stream, pa);
   switch (gate) {
-    case kGateScalar:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateScalar, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
-      break;
-    case kGateNone:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateNone, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
-      break;
-    case kGateLogChannel:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogChannel, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
-      break;
-    case kGateLogScalar:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateLogScalar, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
-      break;
-    case kGateSoftplusChannel:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusChannel, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream,
-                         pa);
-      break;
-    case kGateSoftplusScalar:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateSoftplusScalar, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream,
-                         pa);
-      break;
-    default:
-      hipLaunchKernelGGL((chunk_prep_kernel<DK, E, kGateChannel, ACTQK, SCHED, CONV>), grid, dim3(kThreads), 0, stream, pa);
+    case kGateScalar: KDA_PREP_LAUNCH(kGateScalar) break;
+    case kGateNone: KDA_PREP_LAUNCH(kGateNone) break;
+    case kGateLogChannel: KDA_PREP_LAUNCH(kGateLogChannel) break;
+    case kGateLogScalar: KDA_PREP_LAUNCH(kGateLogScalar) break;
+    case kGateSoftplusChannel: KDA_PREP_LAUNCH(kGateSoftplusChannel) break;
+    case kGateSoftplusScalar: KDA_PREP_LAUNCH(kGateSoftplusScalar) break;
+    default: KDA_PREP_LAUNCH(kGateChannel)
   }
+#undef KDA_PREP_LAUNCH
 }
 
 // LDS held by one stage (record + value slices) of a scan configuration.

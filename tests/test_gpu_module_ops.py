@@ -191,3 +191,46 @@ def test_module_conv_runs_two_phase():
     o_ref, S_ref = _reference(inp, w, "softplus_channel", 128)
     check("o", o, o_ref, TOL[torch.bfloat16])
     check("S_final", S, S_ref, TOL[torch.bfloat16])
+
+
+def test_module_ops_in_graph_capture():
+    # the convolution, the norm and gate and the final convolution state in a
+    # captured call: replays with new inputs copied in match eager calls bitwise
+    import linear_attention_kda_amd as kda
+    announce("module ops under graph capture: 3 replays vs eager, B=2 T=150 H=2 d=128 bf16")
+    B, T, H, D = 2, 150, 2, 128
+    static = _raw_block(to_dev(inputs.dense(B, T, H, D, D, torch.bfloat16, s0_std=0.02, seed=67,
+                                            gate_form="softplus_channel")), 67)
+    w = _weights(H, D, D, torch.bfloat16, static["v"].shape, 67)
+    ws = torch.empty(kda.chunk_fwd_workspace_size(B, T, H, D, D), dtype=torch.uint8, device="cuda")
+    o = torch.empty_like(static["v"])
+    S = torch.empty((B, H, D, D), dtype=torch.float32, device="cuda")
+    cs = torch.empty((B, H, 3, 3 * D), dtype=torch.bfloat16, device="cuda")
+
+    def call(inp, out, S_out, state):
+        kda.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], S0=inp["S0"], gate="softplus_channel",
+                      act=QK | BETA, out=out, S_final=S_out, workspace=ws, conv_state=state, **w)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(static, o, S, cs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(static, o, S, cs)
+    torch.cuda.synchronize()
+    for seed in (68, 69, 70):
+        new = _raw_block(to_dev(inputs.dense(B, T, H, D, D, torch.bfloat16, s0_std=0.02, seed=seed,
+                                             gate_form="softplus_channel")), seed)
+        for name in ("q", "k", "v", "alpha", "beta", "S0"):
+            static[name].copy_(new[name])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_g, S_g, cs_g = o.clone(), S.clone(), cs.clone()
+        o_e, S_e, cs_e = torch.empty_like(o), torch.empty_like(S), torch.empty_like(cs)
+        call(new, o_e, S_e, cs_e)
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e) and torch.equal(S_g, S_e) and torch.equal(cs_g, cs_e)

@@ -124,3 +124,44 @@ def test_auto_takes_split_for_few_long_heads():
     assert st2 == ("two_phase", 0)
     assert rel(o, o2.double().cpu().numpy()) < 5e-3
     assert rel(S, S2.double().cpu().numpy()) < 5e-3
+
+
+def test_split_in_graph_capture():
+    # the split schedule is stream-ordered kernels only, so it can be
+    # captured: replays with new inputs copied in match eager calls bitwise
+    import linear_attention_kda_amd as kda
+    announce("split-sequence under graph capture: 3 replays vs eager, B=1 T=3000 H=2")
+    B, T, H = 1, 3000, 2
+    ws = _workspace(B, T, H)
+    static = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=0.02, seed=76))
+    o = torch.empty_like(static["v"])
+    S = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda")
+    prev = kda.set_schedule("split")
+    try:
+        def call():
+            kda.chunk_fwd(static["q"], static["k"], static["v"], static["alpha"], static["beta"], S0=static["S0"],
+                          out=o, S_final=S, workspace=ws)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            call()
+        torch.cuda.synchronize()
+        for seed in (77, 78, 79):
+            new = to_dev(inputs.dense(B, T, H, 128, 128, torch.bfloat16, s0_std=0.02, seed=seed))
+            for name in ("q", "k", "v", "alpha", "beta", "S0"):
+                static[name].copy_(new[name])
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            o_g, S_g = o.clone(), S.clone()
+            assert kda.chunk_fwd_status(ws) == ("split", 0)
+            o_e, S_e, st = _run(new, "split", _workspace(B, T, H))
+            assert st == ("split", 0)
+            assert torch.equal(o_g, o_e) and torch.equal(S_g, S_e)
+    finally:
+        kda.set_schedule(prev)
