@@ -37,14 +37,14 @@ NSETS = 4
 # Each figure belongs to the kernel source with the given sha256 prefix and is
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
-    "prefill": ("kda_prefill.hip", "83d1e598adf96fd7", 466_788_552),
-    "decode": ("kda_decode.hip", "d5a79493e7747a1c", 1_086_896_128),
-    "decode_tokens": ("kda_decode.hip", "d5a79493e7747a1c", 1_125_307_448),
+    "prefill": ("kda_prefill.hip", "2b9b811fe519a2b7", 466_794_263),
+    "decode": ("kda_decode.hip", "d5a79493e7747a1c", 1_086_895_862),
+    "decode_tokens": ("kda_decode.hip", "d5a79493e7747a1c", 1_125_499_484),
     # measured under the two-phase schedule: counter collection serialises
     # kernels, which the overlapped schedule cannot run under
-    "long_context": ("kda_prefill.hip", "83d1e598adf96fd7", 7_477_305_941),
-    "long_share": ("kda_prefill.hip", "83d1e598adf96fd7", 1_196_148_293),
-    "varlen": ("kda_prefill.hip", "83d1e598adf96fd7", 16_054_675_521),
+    "long_context": ("kda_prefill.hip", "2b9b811fe519a2b7", 7_478_887_616),
+    "long_share": ("kda_prefill.hip", "2b9b811fe519a2b7", 1_195_768_405),
+    "varlen": ("kda_prefill.hip", "2b9b811fe519a2b7", 16_051_319_325),
 }
 
 
