@@ -128,8 +128,32 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   const int part = (int)(slot % SH::SPLIT);                // which APW KiB of the unit
   if (u >= a.units) return;
   const int w = wave_id(), l = lane_id();
+  // RSC: the several-token kernel at d_k = 128 with eight state rows per
+  // lane.  Its per-token work is dominated by the two row sums of each row
+  // (k.s~ and q.s~, 16 values per lane), so instead of summing each of them
+  // over the row's 32 lanes it reduces all 16 together in a reduce-scatter:
+  // at each of the five exchange steps a lane keeps half of its values and
+  // adds its partner's copy of them, so after 8 + 4 + 2 + 1 + 1 adds a lane
+  // holds one complete sum.  For the halves kept to be fixed registers (no
+  // per-lane selects at every step), lanes hold their rows in a
+  // lane-dependent order and half of them take the q sum in the slots where
+  // the others take the k sum: slot i of lane bits b0..b3 holds row (i ^ m),
+  // m = 4 (b1^b2) + 2 (b2^b3) + b3, and lanes with b0^b2 set swap the two
+  // sums.  With the step partners l^1, l^2, l^7, l^15, l^16 (quad permutes,
+  // half-row and row mirrors, row swap) each partner then holds the same row
+  // in the slot sent, and every sum is added up in the order group_sum uses.
+  // The row's error term e is formed where its k sum landed and spread back
+  // to the 32 lanes in three steps (1 + 2 + 4 moves); the lane with the q sum
+  // writes the row's output.  The state is read and written in row order (each
+  // wave-wide access one contiguous KiB: reading the rows in slot order, 64
+  // bytes per row per access, measured 30 % slower) and put into slot order
+  // and back in registers, by three conditional swap stages each way.
+  constexpr bool RSC = G > 1 && !CONV && DK == 128 && NI == 8 && FULL;
   const int sub = l % LPR, rsub = l / LPR;
   const int c0 = 4 * sub;
+  const int b0 = sub & 1, b1 = (sub >> 1) & 1, b2 = (sub >> 2) & 1, b3 = (sub >> 3) & 1, b4 = (sub >> 4) & 1;
+  const int rperm = RSC ? 4 * (b1 ^ b2) + 2 * (b2 ^ b3) + b3 : 0;  // m above
+  const bool qkind = RSC && (b0 ^ b2) != 0;                         // slots 0..7 take the q sum
   const int Tk = G == 1 ? 1 : a.Tk;  // >= 1; the G = 1 kernel is launched for one token
   // token t of this unit in the [N, Tk, H, .] inputs (with one token per
   // launch that is the unit itself)
@@ -150,6 +174,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     valid[i] = FULL || acc < SH::APW;
     rows[i] = (part * SH::APW + (valid[i] ? acc : 0)) * RPA + rsub;
   }
+
+  // RSC: the row in slot 0 (its value entry and its output)
+  const int row0 = RSC ? (part * SH::APW + w * NI + rperm) * RPA + rsub : rows[0];
+  // RSC: slot i <- row (i ^ rperm) of the lane's rows, and back (the same
+  // permutation), one conditional swap stage per bit of rperm
+  auto slot_order = [&](f32x4 *st) {
+#pragma unroll
+    for (int bit = 4; bit >= 1; bit >>= 1) {
+      const bool sw = (rperm & bit) != 0;
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        if (i & bit) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x0 = st[i][j], x1 = st[i | bit][j];
+          st[i][j] = sw ? x1 : x0;
+          st[i | bit][j] = sw ? x0 : x1;
+        }
+      }
+    }
+  };
 
   // CONV: the taps of this lane's channels and rows, and where a token's raw
   // inputs are (t >= 0: the launch's inputs; t in -3..-1: the state)
@@ -179,7 +224,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 
   // the inputs of G tokens are requested together, so a group costs one
   // memory latency; indexes past the last token re-read the last token
-  TokIn<NI> x[G];
+  constexpr int NV = RSC ? 1 : NI;  // value entries a lane reads per token
+  TokIn<NV> x[G];
   auto load_group = [&](int t0) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -218,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
       if constexpr (!CONV) {
         const E *vrow = reinterpret_cast<const E *>(a.v) + ix * DV;
 #pragma unroll
-        for (int i = 0; i < NI; ++i) x[g].vv[i] = (float)vrow[rows[i]];
+        for (int i = 0; i < NV; ++i) x[g].vv[i] = (float)vrow[RSC ? row0 : rows[i]];
       }
     }
   };
@@ -242,11 +288,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // end) the compiler merges them into the loop header behind a full wait
   for (int t0 = 0; t0 < Tk; t0 += G) {
     load_group(t0);
+    if constexpr (RSC)
+      if (t0 == 0) slot_order(s);  // after the first inputs are requested
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int t = t0 + g;
       if (G > 1 && t >= Tk) break;
-      TokIn<NI> &y = x[g];
+      TokIn<NV> &y = x[g];
       if constexpr (gate_is_log(GATE)) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) y.al[j] = gate_from_log(y.al[j]);
@@ -276,21 +324,75 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) kq += y.kk[j] * y.qq[j];
       kq = group_sum<LPR>(kq);
+      // s~ . k = s . (alpha k) and s~ . q = s . (alpha q) (each lane's four
+      // channels in order, then summed over the row's lanes), and the update
+      // s <- alpha s + e k: the same arithmetic in every variant, so several
+      // tokens per launch equal as many single steps bit for bit
+      float ak[4], aq[4];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        float st[4], d1 = 0.f, d2 = 0.f;
+      for (int j = 0; j < 4; ++j) {
+        ak[j] = y.al[j] * y.kk[j];
+        aq[j] = y.al[j] * y.qq[j];
+      }
+      if constexpr (RSC) {
+        // this lane's slot sums (xs) and the ones it hands to its first
+        // partner (xo)
+        float ps[4], po[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          st[j] = s[i][j] * y.al[j];
-          d1 += st[j] * y.kk[j];
-          d2 += st[j] * y.qq[j];
+          ps[j] = qkind ? aq[j] : ak[j];
+          po[j] = qkind ? ak[j] : aq[j];
         }
-        d1 = group_sum<LPR>(d1);
-        d2 = group_sum<LPR>(d2);
-        const float e = y.beta * (y.vv[i] - d1);
+        float xs[8];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) s[i][j] = st[j] + e * y.kk[j];
-        if (valid[i] && sub == 0) orow[rows[i]] = (E)(a.scale * (d2 + e * kq));
+        for (int i = 0; i < 8; ++i) {
+          float xa = s[i][0] * ps[0], xo = s[i][0] * po[0];
+#pragma unroll
+          for (int j = 1; j < 4; ++j) {
+            xa = fmaf(s[i][j], ps[j], xa);
+            xo = fmaf(s[i][j], po[j], xo);
+          }
+          xs[i] = xa + dpp<0xB1>(xo);  // l ^ 1
+        }
+        float y2[4], y3[2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y2[i] = xs[i] + dpp<0x4E>(xs[i + 4]);   // l ^ 2
+#pragma unroll
+        for (int i = 0; i < 2; ++i) y3[i] = y2[i] + dpp<0x141>(y2[i + 2]);  // l ^ 7
+        const float y4 = y3[0] + dpp<0x140>(y3[1]);                        // l ^ 15
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(y4), __float_as_uint(y4), false, false);
+        const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // l ^ 16
+        // tot: the k sum (or the q sum) of row row0; its e from the k lane
+        const float eown = y.beta * (y.vv[0] - tot);
+        const float epart = dpp<0xB1>(eown);
+        float ee[8];
+        ee[0] = qkind ? epart : eown;
+        if (qkind && b4 == 0) orow[row0] = (E)(a.scale * (tot + ee[0] * kq));
+        ee[1] = dpp<0x140>(ee[0]);
+        ee[2] = dpp<0x141>(ee[0]);
+        ee[3] = dpp<0x141>(ee[1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ee[i + 4] = dpp<0x4E>(ee[i]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[i][j] = fmaf(s[i][j], y.al[j], ee[i] * y.kk[j]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          float d1 = s[i][0] * ak[0], d2 = s[i][0] * aq[0];
+#pragma unroll
+          for (int j = 1; j < 4; ++j) {
+            d1 = fmaf(s[i][j], ak[j], d1);
+            d2 = fmaf(s[i][j], aq[j], d2);
+          }
+          d1 = group_sum<LPR>(d1);
+          d2 = group_sum<LPR>(d2);
+          const float e = y.beta * (y.vv[i] - d1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s[i][j] = fmaf(s[i][j], y.al[j], e * y.kk[j]);
+          if (valid[i] && sub == 0) orow[rows[i]] = (E)(a.scale * (d2 + e * kq));
+        }
       }
     }
     // the inputs of a partial last group past Tk are never read; without
@@ -302,10 +404,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
     }
   }
 
-  float *Sout = a.S_out + (size_t)u * DV * DK;
+  if constexpr (RSC) slot_order(s);
+  // the store addresses are formed here rather than held in registers
+  // through the token loop (row i of a lane is its first row + i RPA)
+  int r0 = (part * SH::APW + w * NI) * RPA + rsub;
+  asm volatile("" : "+v"(r0));
+  float *sb = a.S_out + (size_t)u * DV * DK + (size_t)r0 * DK + c0;
 #pragma unroll
   for (int i = 0; i < NI; ++i)
-    if (valid[i]) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4 *>(Sout + (size_t)rows[i] * DK + c0));
+    if (valid[i]) __builtin_nontemporal_store(s[i], reinterpret_cast<f32x4 *>(sb + (size_t)(i * RPA) * DK));
 }
 
 // The convolution state after a launch: the last three raw tokens of (the

@@ -18,6 +18,7 @@ def _inputs(N, Tk, H, d, dtype, gate_form, seed):
 
 @pytest.mark.parametrize("gate_form", ["channel", "scalar"])
 @pytest.mark.parametrize("dtype,d,Tk", [(torch.bfloat16, 128, 1), (torch.bfloat16, 128, 8),
+                                       (torch.bfloat16, 128, 3), (torch.float32, 128, 5),
                                        (torch.float32, 32, 3), (torch.float32, 64, 5)])
 def test_decode_tokens_matches_oracle(gate_form, dtype, d, Tk):
     import linear_attention_kda_amd as kda
@@ -36,10 +37,11 @@ def test_decode_tokens_matches_oracle(gate_form, dtype, d, Tk):
     check("S_out", S_out, S_ref, TOL[dtype])
 
 
-def test_decode_tokens_equals_single_steps():
+@pytest.mark.parametrize("d,Tk", [(128, 4), (128, 3), (64, 4)])
+def test_decode_tokens_equals_single_steps(d, Tk):
     import linear_attention_kda_amd as kda
-    announce("decode_tokens vs single steps, N=6 Tk=4 H=2 d=128 bf16")
-    N, Tk, H, d = 6, 4, 2, 128
+    announce(f"decode_tokens vs single steps, N=6 Tk={Tk} H=2 d={d} bf16")
+    N, H = 6, 2
     inp = _inputs(N, Tk, H, d, torch.bfloat16, "channel", seed=22)
     S_step = inp["S0"].clone()
     outs = []
@@ -67,7 +69,7 @@ def test_decode_tokens_zero_tokens_copies_state():
     assert torch.equal(S_out, inp["S0"])
 
 
-@pytest.mark.parametrize("dk,dv,Tk", [(32, 64, 5), (64, 16, 4), (128, 32, 2), (16, 128, 7)])
+@pytest.mark.parametrize("dk,dv,Tk", [(32, 64, 5), (64, 16, 4), (128, 32, 2), (128, 64, 3), (16, 128, 7)])
 def test_decode_tokens_head_sizes(dk, dv, Tk):
     import linear_attention_kda_amd as kda
     announce(f"decode_tokens N=3 Tk={Tk} H=2 dk={dk} dv={dv} bf16")
