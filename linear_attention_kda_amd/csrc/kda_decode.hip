@@ -178,21 +178,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // RSC: the row in slot 0 (its value entry and its output)
   const int row0 = RSC ? (part * SH::APW + w * NI + rperm) * RPA + rsub : rows[0];
   // RSC: slot i <- row (i ^ rperm) of the lane's rows, and back (the same
-  // permutation), one conditional swap stage per bit of rperm
+  // permutation), through a lane-private strip of LDS: written in one order,
+  // read in the other (slot-major, so each access is conflict-free)
+  __shared__ f32x4 perm_lds[RSC ? kThreads / 64 : 1][RSC ? NI : 1][64];
   auto slot_order = [&](f32x4 *st) {
+    if constexpr (RSC) {
 #pragma unroll
-    for (int bit = 4; bit >= 1; bit >>= 1) {
-      const bool sw = (rperm & bit) != 0;
+      for (int i = 0; i < NI; ++i) perm_lds[w][i][l] = st[i];
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        if (i & bit) continue;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x0 = st[i][j], x1 = st[i | bit][j];
-          st[i][j] = sw ? x1 : x0;
-          st[i | bit][j] = sw ? x0 : x1;
-        }
-      }
+      for (int i = 0; i < NI; ++i) st[i] = perm_lds[w][i ^ rperm][l];
     }
   };
 
