@@ -147,7 +147,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
   // writes the row's output.  The state is read and written in row order (each
   // wave-wide access one contiguous KiB: reading the rows in slot order, 64
   // bytes per row per access, measured 30 % slower) and put into slot order
-  // and back in registers, by three conditional swap stages each way.
+  // and back through LDS (three conditional swap stages in registers, 96
+  // selects each way, measured 1.5 % slower).
   constexpr bool RSC = G > 1 && !CONV && DK == 128 && NI == 8 && FULL;
   const int sub = l % LPR, rsub = l / LPR;
   const int c0 = 4 * sub;
