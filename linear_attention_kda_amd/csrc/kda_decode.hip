@@ -321,8 +321,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
       kq = group_sum<LPR>(kq);
       // s~ . k = s . (alpha k) and s~ . q = s . (alpha q) (each lane's four
       // channels in order, then summed over the row's lanes), and the update
-      // s <- alpha s + e k: the same arithmetic in every variant, so several
-      // tokens per launch equal as many single steps bit for bit
+      // s <- (alpha s) + e k with e k fused into the add: the same arithmetic
+      // in every variant, so several tokens per launch equal as many single
+      // steps bit for bit, and a gate of one equals no gate
       float ak[4], aq[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -371,7 +372,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s[i][j] = fmaf(s[i][j], y.al[j], ee[i] * y.kk[j]);
+          for (int j = 0; j < 4; ++j) s[i][j] = fmaf(ee[i], y.kk[j], s[i][j] * y.al[j]);
       } else {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
@@ -385,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeKArgs a) {
           d2 = group_sum<LPR>(d2);
           const float e = y.beta * (y.vv[i] - d1);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) s[i][j] = fmaf(s[i][j], y.al[j], e * y.kk[j]);
+          for (int j = 0; j < 4; ++j) s[i][j] = fmaf(e, y.kk[j], s[i][j] * y.al[j]);
           if (valid[i] && sub == 0) orow[rows[i]] = (E)(a.scale * (d2 + e * kq));
         }
       }
