@@ -38,8 +38,8 @@ NSETS = 4
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
     "prefill": ("kda_prefill.hip", "2b9b811fe519a2b7", 466_794_263),
-    "decode": ("kda_decode.hip", "d5a79493e7747a1c", 1_086_895_862),
-    "decode_tokens": ("kda_decode.hip", "d5a79493e7747a1c", 1_125_499_484),
+    "decode": ("kda_decode.hip", "00e70acbccc2d272", 1_086_896_743),
+    "decode_tokens": ("kda_decode.hip", "00e70acbccc2d272", 1_125_807_616),
     # measured under the two-phase schedule: counter collection serialises
     # kernels, which the overlapped schedule cannot run under
     "long_context": ("kda_prefill.hip", "2b9b811fe519a2b7", 7_478_887_616),
