@@ -108,19 +108,25 @@ def test_decode_full_size_steps():
 
 def test_decode_tokens_full_size():
     """The multi-token decode in the configuration the benchmark times: 256 x
-    32 heads, 512 MiB state updated in place, Tk = 4 tokens per launch, two
-    launches; the oracle follows 96 sampled (sequence, head) states."""
+    32 heads, 512 MiB state updated in place, Tk = 4 tokens per launch, over
+    the decode workload's whole chain (256 launches, 1024 tokens per
+    sequence); the oracle follows 96 sampled (sequence, head) states.
+    Outputs are checked at every token (the worst is reported) and the
+    states after launches 1, 64 and 256."""
     import linear_attention_kda_amd as kda
     import oracle
-    announce("decode_tokens N256 H32 d128 bf16 Tk=4, 2 launches in place (oracle on 96 units)")
     w = inputs.WORKLOADS["decode"]
     N, H, dk, dv, Tk = w["N"], w["H"], w["dk"], w["dv"], 4
+    launches = w["steps"] // Tk
+    announce(f"decode_tokens N{N} H{H} d{dk} bf16 Tk={Tk}, {launches} launches in place (oracle on 96 units)")
     S = inputs.decode_state(N, H, dk, dv, w["s0_std"], seed=0, device="cuda")
     g = torch.Generator().manual_seed(6)
     units = torch.randperm(N * H, generator=g)[:96]
     nsel, hsel = units.cuda() // H, units.cuda() % H
+    sel = lambda x: x[nsel, hsel].cpu()[:, None]
     S_ref = S[nsel, hsel].double().cpu().numpy()[:, None]
-    for b in range(2):
+    worst_o, worst_tok = 0.0, -1
+    for b in range(launches):
         toks = [inputs.decode_token(N, H, dk, dv, w["dtype"], w["alpha_lo"], step=b * Tk + t, device="cuda")
                 for t in range(Tk)]
         blk = {key: torch.stack([t[key] for t in toks], 1).contiguous() for key in toks[0]}
@@ -128,9 +134,16 @@ def test_decode_tokens_full_size():
         torch.cuda.synchronize()
         assert S2.data_ptr() == S.data_ptr()
         for t in range(Tk):
-            sel = lambda x: x[nsel, hsel].cpu()[:, None]
             o_ref, S_ref = oracle.decode(sel(toks[t]["q"]), sel(toks[t]["k"]), sel(toks[t]["v"]),
                                          sel(toks[t]["alpha"]), sel(toks[t]["beta"]), S_ref)
-            check(f"o launch {b} token {t}", o[nsel, :, hsel][:, t][:, None], o_ref, TOL[torch.bfloat16])
-    check("S after 2 launches", S[nsel, hsel][:, None], S_ref, TOL[torch.bfloat16])
-    assert torch.isfinite(o).all()
+            o_got = o[nsel, :, hsel][:, t][:, None]
+            per = oracle.unit_rel_l2(o_got, o_ref)
+            if float(per.max()) > worst_o:
+                worst_o, worst_tok = float(per.max()), b * Tk + t + 1
+            if b == 0:
+                check(f"o launch 1 token {t}", o_got, o_ref, TOL[torch.bfloat16])
+        if b + 1 in (1, 64, launches):
+            check(f"S after launch {b + 1}", S[nsel, hsel][:, None], S_ref, TOL[torch.bfloat16])
+        assert torch.isfinite(o).all()
+    print(f"    o: worst unit over all {launches * Tk} tokens = {worst_o:.3e} (token {worst_tok})", flush=True)
+    assert worst_o <= TOL[torch.bfloat16]
