@@ -66,12 +66,14 @@ constexpr int kSchedErrTimeout = 1, kSchedErrXcd = 2;
 // segments at once.  The pass over the maps costs about as much per chunk as
 // the scan, so the split pays only when the units leave most of the chip
 // idle: G is chosen by a cost model in scan steps (the map pass at 0.8 of a
-// scan step, whole waves of 256 workgroups), and taken automatically when
-// it saves a quarter of the sequential chain.
+// scan step with two compute waves per workgroup, or half the workgroups at
+// 1.3 times that with four; whole waves of 256 workgroups), and taken
+// automatically when it saves a quarter of the sequential chain.
 struct SplitPlan {
   int G = 1;          // segments per sequence (1: no split)
   int cps = 0;        // chunks per segment (all but the last)
   bool worth = false; // the automatic schedule takes it
+  int map_cw = 2;     // compute waves (16 columns each) per map-scan workgroup: 2 or 4
 };
 constexpr int kSplitMinChunks = 16;  // chunks per segment, at least
 constexpr int kSplitMaxSegments = 16;
@@ -85,12 +87,21 @@ inline SplitPlan split_plan(int B, int T, int H, int dk, int dv, int esize) {
     const long long cps = (nct + G - 1) / G;
     if (cps < kSplitMinChunks) break;
     if ((G - 1) * cps >= nct) continue;  // the last segment would be empty
-    const double waves1 = (double)(((G - 1) * wg_map + 255) / 256), waves3 = (double)((G * wg_scan + 255) / 256);
-    const double est = waves1 * cps * 0.8 + waves3 * cps + 2.0 * (G - 1);
+    // maps: with two compute waves per workgroup a state-only step costs
+    // about 0.8 of a scan step; with four (half the workgroups, twice the
+    // columns each) about 1.3 times that, which pays only once the
+    // two-wave maps need more than one round of 256 workgroups
+    const long long wg2 = (G - 1) * wg_map, wg4 = wg2 / 2;
+    const double map2 = (double)((wg2 + 255) / 256) * cps * 0.8;
+    const double map4 = (double)((wg4 + 255) / 256) * cps * 0.8 * 1.3;
+    const bool four = wg2 > 256 && map4 < map2;
+    const double waves3 = (double)((G * wg_scan + 255) / 256);
+    const double est = (four ? map4 : map2) + waves3 * cps + 2.0 * (G - 1);
     if (est < best) {
       best = est;
       sp.G = G;
       sp.cps = (int)cps;
+      sp.map_cw = four ? 4 : 2;
     }
   }
   sp.worth = sp.G > 1 && best < 0.75 * (double)nct;

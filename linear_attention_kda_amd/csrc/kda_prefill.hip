@@ -2427,9 +2427,11 @@ void map_scan_kernel(MapKArgs a) {
         if (vcopier) copy_v(ci + 1, vt[(ci + 1) & 1]);
       }
       if (a.touch_ahead && cpi == 1 && !vcopier && ci + 2 < nchunks) {
-        // record ci+2 into L2: block grp of its eight 8 KiB blocks
-        touch_record<1>(a.ws_records + ((size_t)(chunk0 + ci + 2) * a.H + h) * RS::bytes, RS::bytes, grp, touch_lds);
-        wait_vmcnt<1>();  // the copies; the touch may still fly
+        // record ci+2 into L2: this workgroup's share of its eight 8 KiB blocks
+        constexpr int TB = 8 / (GX + GM);
+        touch_record<TB>(a.ws_records + ((size_t)(chunk0 + ci + 2) * a.H + h) * RS::bytes, RS::bytes, TB * grp,
+                         touch_lds);
+        wait_vmcnt<TB>();  // the copies; the touches may still fly
       } else {
         __builtin_amdgcn_s_waitcnt(0);
       }
@@ -2766,9 +2768,18 @@ hipError_t run_split(const PrefillArgs &a, hipStream_t stream, char *records, co
   ma.cps = cps;
   ma.n_maps = a.B * (G - 1) * a.H;
   ma.touch_ahead = touch;
-  constexpr int kMapCW = 2, kMapCP = 4, kMapGroups = (128 + 128) / (16 * kMapCW);
-  const dim3 mg((unsigned)((ma.n_maps + 7) / 8 * 8 * kMapGroups));
-  hipLaunchKernelGGL((map_scan_kernel<kMapCW, kMapCP>), mg, dim3(64 * (kMapCW + kMapCP)), 0, stream, ma);
+  // two or four compute waves per workgroup, as the plan chose (measured
+  // with records from the Infinity Cache, 4 heads x 16 segments: 480
+  // two-wave workgroups in two rounds 140 us, 240 four-wave ones in one
+  // round 91 us; 16 heads x 4 segments: 256 two-wave workgroups 384 us,
+  // 128 four-wave ones 485 us)
+  constexpr int kMapCP = 4;
+  const int map_cw = P.split.map_cw == 4 ? 4 : 2;
+  const dim3 mg((unsigned)((ma.n_maps + 7) / 8 * 8 * ((128 + 128) / (16 * map_cw))));
+  if (map_cw == 4)
+    hipLaunchKernelGGL((map_scan_kernel<4, kMapCP>), mg, dim3(64 * (4 + kMapCP)), 0, stream, ma);
+  else
+    hipLaunchKernelGGL((map_scan_kernel<2, kMapCP>), mg, dim3(64 * (2 + kMapCP)), 0, stream, ma);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   hipLaunchKernelGGL(split_chain_kernel, dim3((unsigned)(a.B * a.H * 16)), dim3(256), 0, stream, a.S0, maps, start,
