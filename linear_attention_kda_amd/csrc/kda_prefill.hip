@@ -467,6 +467,7 @@ __device__ __forceinline__ void chunk_prep_body(const PrepKArgs &a) {
   __shared__ __attribute__((aligned(16))) char arena[ARENA];
   __shared__ float sBeta[kChunk];
   __shared__ float sInvNorm[2][kChunk];  // 1/|SiLU(k)|, 1/|SiLU(q)| per token (input activation only)
+  __shared__ float sDiag[kChunk];        // s k_i . q_i per token (the diagonal of A, fast path)
 
   static_assert(!CONV || (ACTQK && !SCHED), "the convolution comes with the q, k activation, two-phase");
   // one record: chunk slot c, head h
@@ -655,10 +656,19 @@ __device__ __forceinline__ void chunk_prep_body(const PrepKArgs &a) {
         }
         kraw[u] = F4::pack(kx);
         qraw[u] = F4::pack(qx);
+        // the diagonal of A (see below) for a partial chunk, from the
+        // values as packed, here where few values are live
+        float kq = 0.f;
+        if (L < kChunk) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) kq = fmaf((float)kraw[u][j], (float)qraw[u][j], kq);
+          kq = group_sum<CG>(kq);
+        }
         // for the exact path, which reads q and k again from memory
         if (cg == 0) {
           sInvNorm[0][tb0 + u] = rk;
           sInvNorm[1][tb0 + u] = rq;
+          sDiag[tb0 + u] = tb0 + u < L ? kq * a.scale : 0.f;
         }
         __builtin_amdgcn_sched_barrier(0);  // one token at a time: bounds the live values
       }
@@ -705,6 +715,28 @@ __device__ __forceinline__ void chunk_prep_body(const PrepKArgs &a) {
       }
       *reinterpret_cast<typename F4::vec *>(sKh + LK::elem_off(tok, c0)) = F4::pack(kh);
       *reinterpret_cast<typename F4::vec *>(sQh + LK::elem_off(tok, c0)) = F4::pack(qh);
+    }
+    // A partial chunk (the end of a sequence; all of a short one) also gets
+    // the diagonal of A, s k_i . q_i, summed in fp32 from the values as the
+    // kernel holds them (its decays cancel).  The fast path's products take
+    // k / a and s q a rounded to E, whose rounding errors do not cancel when
+    // k_i . q_i does: a one-token sequence's output is that one term times
+    // beta v, so its relative error would be the dot product's condition
+    // number times the rounding.  In a full chunk each output row sums up to
+    // 64 such terms and the errors average out; there the products' diagonal
+    // stands (the sums cost about 1 % of the prefill workload's time).
+    const bool diag_exact = L < kChunk;  // uniform over the workgroup
+    if constexpr (!ACTQK) {  // (with the activation: summed as q and k are activated)
+      if (diag_exact) {
+#pragma unroll
+        for (int u = 0; u < TPL; ++u) {
+          float kq = kval(u, 0) * qval(u, 0);
+#pragma unroll
+          for (int j = 1; j < 4; ++j) kq = fmaf(kval(u, j), qval(u, j), kq);
+          kq = group_sum<CG>(kq);
+          if (cg == 0) sDiag[tb0 + u] = kq * a.scale;
+        }
+      }
     }
     if (!exact) {
 #pragma unroll
@@ -798,7 +830,7 @@ __device__ __forceinline__ void chunk_prep_body(const PrepKArgs &a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             rv[r] = jb + r < i ? sBeta[i] * rt[s][r] : 0.f;
-            av[r] = jb + r <= i ? at[s][r] : 0.f;
+            av[r] = jb + r < i ? at[s][r] : (jb + r == i ? (diag_exact ? sDiag[i] : at[s][r]) : 0.f);
           }
           *reinterpret_cast<f32x4 *>(sR + i * LDR + jb) = f32x4{rv[0], rv[1], rv[2], rv[3]};
           *reinterpret_cast<typename F4::vec *>(gA + tri_index<E>(i, jb)) = F4::pack(av);
