@@ -37,14 +37,14 @@ NSETS = 4
 # Each figure belongs to the kernel source with the given sha256 prefix and is
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
-    "prefill": ("kda_prefill.hip", "8a6b0b76788ed929", 466_807_655),
+    "prefill": ("kda_prefill.hip", "abbb5e52a3f6398e", 466_967_200),
     "decode": ("kda_decode.hip", "00e70acbccc2d272", 1_086_896_743),
     "decode_tokens": ("kda_decode.hip", "00e70acbccc2d272", 1_125_807_616),
     # measured under the two-phase schedule: counter collection serialises
     # kernels, which the overlapped schedule cannot run under
-    "long_context": ("kda_prefill.hip", "8a6b0b76788ed929", 7_478_741_456),
-    "long_share": ("kda_prefill.hip", "8a6b0b76788ed929", 1_207_587_019),
-    "varlen": ("kda_prefill.hip", "8a6b0b76788ed929", 16_049_888_216),
+    "long_context": ("kda_prefill.hip", "abbb5e52a3f6398e", 7_481_837_525),
+    "long_share": ("kda_prefill.hip", "abbb5e52a3f6398e", 1_206_094_187),
+    "varlen": ("kda_prefill.hip", "abbb5e52a3f6398e", 16_052_519_462),
 }
 
 
