@@ -1,7 +1,8 @@
 """Seeded random cases through the C ABI against the fp64 oracle: prefill
 (dense and packed, both dtypes, every head size, every gate form, with and
-without S0, every schedule) and decode (one token and several, in place or
-not).  The shapes are drawn once from a fixed seed, so every run checks the
+without S0, every schedule), decode (one token and several, in place or
+not) and the block's operations around the method (short convolution,
+output norm and gate).  The shapes are drawn once from a fixed seed, so every run checks the
 same cases; each is small enough for the oracle and spans ragged chunks.
 Gate forms reach the oracle as per-channel gates in fp64 (broadcast, ones,
 exp of the logarithm, 1 / (1 + e^g) of the softplus logit), the way the page
@@ -12,7 +13,6 @@ import random
 import pytest
 import torch
 
-import oracle
 from linear_attention_kda_amd import inputs
 from tests.gpu_cases import TOL, announce, check, oracle_prefill, to_dev
 
@@ -137,3 +137,58 @@ def test_random_decode_tokens(c):
         assert torch.equal(S_in, dev["S0"]), "S_in is the checkpoint and must not change"
     check("o", o, o_ref, TOL[dtype])
     check("S_out", S, S_ref, TOL[dtype])
+
+
+def _module_cases(n=12, seed=20261205):
+    rng = random.Random(seed)
+    cases = []
+    for i in range(n):
+        packed = rng.random() < 0.4
+        lengths = ([rng.choice([1, 2, 3, rng.randint(4, 63), 64, rng.randint(65, 200)]) for _ in range(rng.randint(1, 3))]
+                   if packed else None)
+        cases.append(dict(i=i, dtype=rng.choice(["bf16", "fp32"]), dk=rng.choice(DIMS), dv=rng.choice(DIMS),
+                          H=rng.randint(1, 3), B=1 if packed else rng.randint(1, 2),
+                          T=sum(lengths) if packed else rng.randint(2, 300), lengths=lengths,
+                          gate=rng.choice(["channel", "scalar", "softplus_channel", "softplus_scalar"]),
+                          ops=rng.choice(["conv", "norm_gate", "all"]), s0=rng.random() < 0.5,
+                          sched=rng.choice(["auto", "two_phase", "split"])))
+    return cases
+
+
+def _mid(c):
+    shape = f"packed{c['lengths']}" if c["lengths"] is not None else f"B{c['B']}T{c['T']}"
+    return (f"{c['i']}-{c['dtype']}-{shape}-H{c['H']}-dk{c['dk']}dv{c['dv']}-{c['gate']}-{c['ops']}-"
+            f"{'S0' if c['s0'] else 'noS0'}-{c['sched']}")
+
+
+MODULE = _module_cases()
+
+
+@pytest.mark.parametrize("c", MODULE, ids=[_mid(c) for c in MODULE])
+def test_random_module_ops(c):
+    """The block's operations around the method (short convolution, output
+    norm and gate) on random shapes, against the float64 block steps of
+    tests/module_ref.py around the oracle."""
+    import linear_attention_kda_amd as kda
+    from tests.test_gpu_module_ops import _raw_block, _reference, _run, _weights
+    announce(f"random module ops {_mid(c)}")
+    dtype = torch.bfloat16 if c["dtype"] == "bf16" else torch.float32
+    seed = 9700 + c["i"]
+    if c["lengths"] is not None:
+        inp = inputs.packed(c["lengths"], c["H"], c["dk"], c["dv"], dtype, s0_std=0.02 if c["s0"] else None,
+                            seed=seed, gate_form=c["gate"])
+    else:
+        inp = inputs.dense(c["B"], c["T"], c["H"], c["dk"], c["dv"], dtype, s0_std=0.02 if c["s0"] else None,
+                           seed=seed, gate_form=c["gate"])
+    inp = _raw_block(to_dev(inp), seed)
+    w = _weights(c["H"], c["dk"], c["dv"], dtype, inp["v"].shape, seed, conv=c["ops"] in ("conv", "all"),
+                 norm=c["ops"] in ("norm_gate", "all"), gate=c["ops"] in ("norm_gate", "all"))
+    o_ref, S_ref = _reference(inp, w, c["gate"], c["dk"])
+    kda.set_schedule(c["sched"])
+    try:
+        o, S = _run(inp, c["gate"], w)
+    finally:
+        kda.set_schedule("auto")
+    cu = inp.get("cu_seqlens")
+    check("o", o, o_ref, TOL[dtype], cu=None if cu is None else cu.cpu())
+    check("S_final", S, S_ref, TOL[dtype])
