@@ -2497,30 +2497,36 @@ void map_scan_kernel(MapKArgs a) {
 // Segment start states: S_0 = S0 (or zero), S_{g+1} = S_g M_g + X_g in fp32
 // (S-form, d_v x d_k; M_g's rows are the stored M^T rows, so the product is
 // sum_j S_g[r][j] Mt_g[j][c]).  Rows are independent: one workgroup per
-// (sequence, head, block of 8 rows), a thread per (row, 4 columns); start is
-// [B G H] x d_v x d_k.  Each segment's Mt (64 KiB) sits in LDS, and the next
-// one is loaded into registers while the current product runs.  (Measured:
-// with 32 rows per workgroup, 16 per thread, and S read as scalars the
-// product took 9.4 us per segment, bound by LDS reads; reading Mt straight
-// from memory inside the loop, 28 us.)
+// (sequence, head, block of RB rows), a thread per row and 128 RB / 256
+// columns (4 at RB = 8, 2 at RB = 4); start is [B G H] x d_v x d_k.  Each segment's Mt
+// (64 KiB) sits in LDS, and the next one is loaded into registers while the
+// current product runs.  (Measured on 4 heads x 16 segments: 3.7 us per
+// segment at 8 rows per workgroup, about 3 at 4, which halves each thread's
+// products at twice the Mt reads from L2; with 32 rows per workgroup, 16 per
+// thread, and S read as scalars the product took 9.4 us per segment, bound
+// by LDS reads; reading Mt straight from memory inside the loop, 28 us.)
+template <int RB>
 __global__ __launch_bounds__(256) void split_chain_kernel(const float *S0, const float *maps, float *start, int H,
                                                           int G, int n_units) {
-  constexpr int DK = 128, DV = 128, RB = 8, NV = DK * DK / 4 / 256;  // 16-byte loads of Mt per thread
+  constexpr int DK = 128, DV = 128, NV = DK * DK / 4 / 256;  // 16-byte loads of Mt per thread
+  constexpr int TPR = 256 / RB, NC = DK / TPR;                 // threads per row, columns per thread
+  static_assert(NC == 2 || NC == 4, "two or four columns per thread");
+  typedef float vec __attribute__((ext_vector_type(NC)));
   __shared__ __attribute__((aligned(16))) float sS[RB][DK];
   __shared__ __attribute__((aligned(16))) float sM[DK][DK];
   const int unit = blockIdx.x / (DV / RB), rb = blockIdx.x % (DV / RB);
   if (unit >= n_units) return;  // whole workgroup
   const int n = unit / H, h = unit % H;
-  const int t = threadIdx.x, row = t / 32, c4 = (t % 32) * 4;  // this thread's row and first column
+  const int t = threadIdx.x, row = t / TPR, cc = (t % TPR) * NC;  // this thread's row and first column
   auto seg_maps = [&](int sg) { return maps + (((size_t)n * (G - 1) + sg) * H + h) * (size_t)(DV + DK) * DK; };
   auto start_row = [&](int sg) {
-    return start + (((size_t)n * G + sg) * H + h) * DV * DK + (size_t)(rb * RB + row) * DK + c4;
+    return start + (((size_t)n * G + sg) * H + h) * DV * DK + (size_t)(rb * RB + row) * DK + cc;
   };
   {
-    f32x4 x = zero4();
-    if (S0) x = *reinterpret_cast<const f32x4 *>(S0 + ((size_t)unit * DV + rb * RB + row) * DK + c4);
-    *reinterpret_cast<f32x4 *>(&sS[row][c4]) = x;
-    *reinterpret_cast<f32x4 *>(start_row(0)) = x;
+    vec x = {};
+    if (S0) x = *reinterpret_cast<const vec *>(S0 + ((size_t)unit * DV + rb * RB + row) * DK + cc);
+    *reinterpret_cast<vec *>(&sS[row][cc]) = x;
+    *reinterpret_cast<vec *>(start_row(0)) = x;
   }
   f32x4 mv[NV];
   if (G > 1) {
@@ -2531,7 +2537,7 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *S0, const
   for (int sg = 0; sg + 1 < G; ++sg) {
 #pragma unroll
     for (int i = 0; i < NV; ++i) reinterpret_cast<f32x4 *>(&sM[0][0])[t + 256 * i] = mv[i];
-    f32x4 acc = *reinterpret_cast<const f32x4 *>(seg_maps(sg) + (size_t)(rb * RB + row) * DK + c4);
+    vec acc = *reinterpret_cast<const vec *>(seg_maps(sg) + (size_t)(rb * RB + row) * DK + cc);
     __syncthreads();  // sM and S_g complete
     if (sg + 2 < G) {  // the next segment's Mt, in flight during the product
       const f32x4 *Mt4 = reinterpret_cast<const f32x4 *>(seg_maps(sg + 1) + (size_t)DV * DK);
@@ -2543,14 +2549,14 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *S0, const
       const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&sS[row][j]);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const f32x4 m = *reinterpret_cast<const f32x4 *>(&sM[j + jj][c4]);
+        const vec m = *reinterpret_cast<const vec *>(&sM[j + jj][cc]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(s4[jj], m[e], acc[e]);
+        for (int e = 0; e < NC; ++e) acc[e] = __builtin_fmaf(s4[jj], m[e], acc[e]);
       }
     }
     __syncthreads();  // every thread is done reading S_g and sM
-    *reinterpret_cast<f32x4 *>(&sS[row][c4]) = acc;
-    *reinterpret_cast<f32x4 *>(start_row(sg + 1)) = acc;
+    *reinterpret_cast<vec *>(&sS[row][cc]) = acc;
+    *reinterpret_cast<vec *>(start_row(sg + 1)) = acc;
   }
 }
 
@@ -2814,7 +2820,9 @@ hipError_t run_split(const PrefillArgs &a, hipStream_t stream, char *records, co
     hipLaunchKernelGGL((map_scan_kernel<2, kMapCP>), mg, dim3(64 * (2 + kMapCP)), 0, stream, ma);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  hipLaunchKernelGGL(split_chain_kernel, dim3((unsigned)(a.B * a.H * 16)), dim3(256), 0, stream, a.S0, maps, start,
+  constexpr int kChainRows = 4;
+  hipLaunchKernelGGL(split_chain_kernel<kChainRows>, dim3((unsigned)(a.B * a.H * (128 / kChainRows))), dim3(256), 0,
+                     stream, a.S0, maps, start,
                      a.H, G, a.B * a.H);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
