@@ -1113,6 +1113,13 @@ struct ScanKArgs {
   // copied to LDS (set when the records outgrow the 256 MB Infinity Cache,
   // so they come from HBM)
   int touch_ahead;
+  // split-sequence scan (two-phase kernels): the packed sequences are
+  // segments, seg_per_seq of them per sequence; the last segment's end state
+  // goes to S_last (the sequence's final state) and the others' are not
+  // stored; sched_id is the schedule word the call records (0: two-phase)
+  float *S_last;
+  int seg_per_seq;
+  int sched_id;
 };
 
 // B operands built from accumulator tiles.  Tile q of a K x 16 operand holds
@@ -1471,7 +1478,7 @@ void chunk_scan_kernel(ScanKArgs a) {
     grp = slot % a.wg_per_unit;
     // the schedule this call ran, and no schedule errors
     if (bid == 0 && threadIdx.x == 0) {
-      a.ctl[kCtlSchedule] = kScheduleTwoPhase;
+      a.ctl[kCtlSchedule] = a.sched_id ? a.sched_id : kScheduleTwoPhase;
       a.ctl[kCtlError] = 0;
     }
   }
@@ -1734,11 +1741,16 @@ void chunk_scan_kernel(ScanKArgs a) {
     if (nchunks > 0) store_o(nchunks - 1, ov);
   }
 
+  float *sf = a.S_final + sbase;
+  if (!SCHED && a.S_last) {  // split-sequence: only the sequence's last segment
+    if (n % a.seg_per_seq != a.seg_per_seq - 1) return;
+    sf = a.S_last + ((size_t)(n / a.seg_per_seq) * H + h) * DV * DK + (size_t)(v0 + col) * DK;
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-      *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
+      *reinterpret_cast<f32x4 *>(sf + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
 }
 
 // ================================================= one-CU-per-unit scan
@@ -1952,7 +1964,7 @@ void unit_scan_kernel(ScanKArgs a) {
   } else {
     u = blockIdx.x;
     if (blockIdx.x == 0 && threadIdx.x == 0) {
-      a.ctl[kCtlSchedule] = kScheduleTwoPhase;
+      a.ctl[kCtlSchedule] = a.sched_id ? a.sched_id : kScheduleTwoPhase;
       a.ctl[kCtlError] = 0;
     }
   }
@@ -2192,11 +2204,16 @@ void unit_scan_kernel(ScanKArgs a) {
     if (CP == 0) wait_copies(touched);
     __syncthreads();  // chunk ci done, chunk ci+1 ready
   }
+  float *sf = a.S_final + sbase;
+  if (!SCHED && a.S_last) {  // split-sequence: only the sequence's last segment
+    if (n % a.seg_per_seq != a.seg_per_seq - 1) return;
+    sf = a.S_last + ((size_t)(n / a.seg_per_seq) * H + h) * DV * DK + (size_t)(v0 + col) * DK;
+  }
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
-      *reinterpret_cast<f32x4 *>(a.S_final + sbase + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
+      *reinterpret_cast<f32x4 *>(sf + (size_t)16 * nt * DK + 16 * ct + 4 * g) = st[ct][nt];
 }
 
 // ======================================================= output norm + gate
@@ -2494,6 +2511,21 @@ void map_scan_kernel(MapKArgs a) {
   for (int ct = 0; ct < CT; ++ct) *reinterpret_cast<f32x4 *>(out + 16 * ct + 4 * g) = st[ct][0];
 }
 
+// Segment tables in the packed-batch form the scan reads: segment i = n G + g
+// starts at token n T + min(g cps 64, T) and at chunk slot n nct + g cps
+// (written by the chain pass's first workgroup; the scan runs after it).
+struct SplitTables {
+  int32_t *tok0, *chunk0;
+  int B, T, nct, cps;
+};
+__device__ __forceinline__ void write_split_tables(const SplitTables &tb, int G) {
+  for (int i = threadIdx.x; i <= tb.B * G; i += blockDim.x) {
+    const int n = i / G, sg = i % G;
+    tb.tok0[i] = (int32_t)((long long)n * tb.T + min((long long)sg * tb.cps * kChunk, (long long)tb.T));
+    tb.chunk0[i] = (int32_t)((long long)n * tb.nct + (long long)sg * tb.cps);
+  }
+}
+
 // Segment start states: S_0 = S0 (or zero), S_{g+1} = S_g M_g + X_g in fp32
 // (S-form, d_v x d_k; M_g's rows are the stored M^T rows, so the product is
 // sum_j S_g[r][j] Mt_g[j][c]).  Rows are independent: one workgroup per
@@ -2507,7 +2539,8 @@ void map_scan_kernel(MapKArgs a) {
 // by LDS reads; reading Mt straight from memory inside the loop, 28 us.)
 template <int RB>
 __global__ __launch_bounds__(256) void split_chain_kernel(const float *S0, const float *maps, float *start, int H,
-                                                          int G, int n_units) {
+                                                          int G, int n_units, SplitTables tb) {
+  if (blockIdx.x == 0) write_split_tables(tb, G);
   constexpr int DK = 128, DV = 128, NV = DK * DK / 4 / 256;  // 16-byte loads of Mt per thread
   constexpr int TPR = 256 / RB, NC = DK / TPR;                 // threads per row, columns per thread
   static_assert(NC == 2 || NC == 4, "two or four columns per thread");
@@ -2560,31 +2593,7 @@ __global__ __launch_bounds__(256) void split_chain_kernel(const float *S0, const
   }
 }
 
-// Segment tables in the packed-batch form the scan reads: segment i = n G + g
-// starts at token n T + min(g cps 64, T) and at chunk slot n nct + g cps.
-__global__ void split_tables_kernel(int32_t *tok0, int32_t *chunk0, int B, int T, int nct, int G, int cps) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i <= B * G; i += gridDim.x * blockDim.x) {
-    const int n = i / G, sg = i % G;
-    tok0[i] = (int32_t)((long long)n * T + min((long long)sg * cps * kChunk, (long long)T));
-    chunk0[i] = (int32_t)((long long)n * nct + (long long)sg * cps);
-  }
-}
 
-// The last segments' end states are the sequences' final states; records the
-// schedule this call ran.
-__global__ void split_final_kernel(const float *end, float *S_final, int *ctl, int B, int H, int G, int state) {
-  const size_t per = (size_t)state / 4, total = (size_t)B * H * per;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
-    const size_t unit = i / per, e = i % per;
-    const size_t n = unit / H, h = unit % H;
-    reinterpret_cast<f32x4 *>(S_final)[i] =
-        reinterpret_cast<const f32x4 *>(end + (((size_t)n * G + G - 1) * H + h) * state)[e];
-  }
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    ctl[kCtlSchedule] = kScheduleSplit;
-    ctl[kCtlError] = 0;
-  }
-}
 
 // ================================================================ dispatch
 // CU-masked streams of the overlapped schedule, one set per device: the scan
@@ -2776,9 +2785,9 @@ hipError_t launch_scan_phase(const PrefillArgs &a, ScanKArgs sa, hipStream_t str
   return hipGetLastError();
 }
 
-// Split-sequence schedule after the prep (d = 128 bf16, dense): segment
-// tables, the maps of all segments but the last, the chained start states,
-// the scan of every segment, and the final states.
+// Split-sequence schedule after the prep (d = 128 bf16, dense): the maps of
+// all segments but the last, the chained start states (and the segment
+// tables), the scan of every segment, and the final states.
 template <int DK, typename E>
 hipError_t run_split(const PrefillArgs &a, hipStream_t stream, char *records, const ChunkRecordLayout &lay) {
   const WorkspacePlan &P = a.plan;
@@ -2791,9 +2800,7 @@ hipError_t run_split(const PrefillArgs &a, hipStream_t stream, char *records, co
   int *ctl = reinterpret_cast<int *>(a.ws);
   const bool touch = (size_t)P.max_chunks * a.H * lay.bytes > ((size_t)256 << 20);
   const void *vsrc = a.conv_q ? a.o : a.v;  // the prep left v's convolution in o
-  hipLaunchKernelGGL(split_tables_kernel, dim3(1), dim3(256), 0, stream, tok0, ch0, a.B, a.T, nct, G, cps);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e = hipSuccess;
 
   MapKArgs ma{};
   ma.v = vsrc;
@@ -2821,9 +2828,9 @@ hipError_t run_split(const PrefillArgs &a, hipStream_t stream, char *records, co
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   constexpr int kChainRows = 4;
+  const SplitTables tables{tok0, ch0, a.B, a.T, nct, cps};
   hipLaunchKernelGGL(split_chain_kernel<kChainRows>, dim3((unsigned)(a.B * a.H * (128 / kChainRows))), dim3(256), 0,
-                     stream, a.S0, maps, start,
-                     a.H, G, a.B * a.H);
+                     stream, a.S0, maps, start, a.H, G, a.B * a.H, tables);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   ScanKArgs sa{};
@@ -2844,13 +2851,10 @@ hipError_t run_split(const PrefillArgs &a, hipStream_t stream, char *records, co
   sa.n_units = a.B * G * a.H;
   sa.ctl = ctl;
   sa.touch_ahead = touch;
-  if ((e = launch_scan_phase<DK, E>(a, sa, stream)) != hipSuccess) return e;
-
-  const int state = a.dv * a.dk;
-  const long long vec4 = (long long)a.B * a.H * state / 4;
-  hipLaunchKernelGGL(split_final_kernel, dim3((unsigned)std::min<long long>(1024, (vec4 + 255) / 256)), dim3(256), 0,
-                     stream, end, a.S_final, ctl, a.B, a.H, G, state);
-  return hipGetLastError();
+  sa.S_last = a.S_final;  // the last segments' end states are the final states
+  sa.seg_per_seq = G;
+  sa.sched_id = kScheduleSplit;
+  return launch_scan_phase<DK, E>(a, sa, stream);
 }
 
 template <int DK, typename E>
