@@ -282,6 +282,9 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v,
  *           S_final must not overlap an input unless it is exactly S0.
  *
  * T = 0 (or an empty packed batch) copies S0 (or zeros) to S_final.
+ * Size limits: B T < 2^31 tokens, and H d_v < 2^23 (64 token rows of every
+ * head's outputs in fp32 span less than 2^31 bytes); beyond either the call
+ * returns KDA_ERR_BAD_SHAPE and the workspace query returns 0.
  */
 kda_status kda_chunk_fwd(const void *q, const void *k, const void *v,
                          const float *alpha, const float *beta,

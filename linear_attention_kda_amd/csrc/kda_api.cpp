@@ -18,6 +18,9 @@
 namespace {
 
 bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+// The scan stores a chunk's outputs through one buffer range of 32-bit size:
+// 64 token rows of all heads' values, at most 4 bytes each.
+bool width_ok(int H, int d_v) { return (size_t)H * d_v * 64 * 4 <= (size_t)INT32_MAX; }
 constexpr unsigned kActAll = KDA_ACT_QK_SILU_L2NORM | KDA_ACT_BETA_SIGMOID;
 bool valid_gate(kda_gate g) {
   return g == KDA_GATE_CHANNEL || g == KDA_GATE_SCALAR || g == KDA_GATE_NONE || g == KDA_GATE_LOG_CHANNEL ||
@@ -171,7 +174,7 @@ kda_status chunk_fwd_impl(const void *q, const void *k, const void *v, const flo
   if (mo.norm_weight && !(mo.norm_eps >= 0.f)) return KDA_ERR_BAD_SHAPE;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return KDA_ERR_UNSUPPORTED_DTYPE;
   if (!dim_ok(d_k) || !dim_ok(d_v)) return KDA_ERR_UNSUPPORTED_DIM;
-  if (B < 0 || T < 0 || H <= 0) return KDA_ERR_BAD_SHAPE;
+  if (B < 0 || T < 0 || H <= 0 || !width_ok(H, d_v)) return KDA_ERR_BAD_SHAPE;
   const bool packed = cu_seqlens != nullptr;
   if (packed) {
     if (B != 1) return KDA_ERR_VARLEN_REQUIRES_B1;
@@ -333,7 +336,7 @@ int kda_set_schedule(int schedule) {
 }
 
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int d_k, int d_v, int N, kda_dtype dtype) {
-  if (B < 0 || T < 0 || H <= 0 || !dim_ok(d_k) || !dim_ok(d_v)) return 0;
+  if (B < 0 || T < 0 || H <= 0 || !dim_ok(d_k) || !dim_ok(d_v) || !width_ok(H, d_v)) return 0;
   if (dtype != KDA_F32 && dtype != KDA_BF16) return 0;
   const int esize = dtype == KDA_BF16 ? 2 : 4;
   size_t need = kda::plan_workspace(false, B, T, H, d_k, B, esize, d_v).total;

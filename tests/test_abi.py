@@ -66,6 +66,10 @@ def test_workspace_size(kda):
     assert kda.chunk_fwd_workspace_size(1, 10, 2, 48, 64, -1, kda.KDA_BF16) == 0
     assert kda.chunk_fwd_workspace_size(1, 10, 0, 64, 64, -1, kda.KDA_BF16) == 0
     assert kda.chunk_fwd_workspace_size(1, 10, 2, 64, 64, -1, 7) == 0
+    # 64 token rows of all heads' outputs must span less than 2^31 bytes in fp32
+    assert kda.chunk_fwd_workspace_size(1, 10, 65536, 16, 128, -1, kda.KDA_BF16) == 0
+    assert kda.chunk_fwd_workspace_size(1, 10, 65535, 16, 128, -1, kda.KDA_BF16) > 0
+    assert kda.chunk_fwd_workspace_size(1, 10, 1 << 19, 16, 16, -1, kda.KDA_BF16) == 0
 
 
 def _fwd(kda, **kw):
@@ -88,6 +92,9 @@ def test_chunk_fwd_validation(kda):
     assert _fwd(kda, dv=256) == 3
     assert _fwd(kda, H=0) == 2                       # bad shape
     assert _fwd(kda, T=-1) == 2
+    assert _fwd(kda, H=65536, dv=128) == 2           # H d_v >= 2^23
+    assert _fwd(kda, H=1 << 19, dv=16) == 2
+    assert _fwd(kda, H=65535, dv=128, S_final=None) == 1   # within the bound: the next check
     assert _fwd(kda, q=None) == 1                    # null input
     assert _fwd(kda, S_final=None) == 1
     assert _fwd(kda, o=P(0x60004)) == 5              # misaligned
