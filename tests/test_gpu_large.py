@@ -1,4 +1,6 @@
-"""One sequence of 2^20 tokens on eight heads (d = 128, bf16) through every
+"""Sizes whose byte offsets pass 2^31 and 2^32.
+
+One sequence of 2^20 tokens on eight heads (d = 128, bf16) through every
 prefill schedule: the context length the pages build the method for (page
 "Kimi Delta Attention (KDA)", section on why the architecture matters beyond
 data centres: a state of constant size for contexts of a million tokens).
@@ -12,7 +14,11 @@ a unit key and beta_t in [0, 1]; a state 448 tokens back therefore reaches
 the present damped by 0.9^448 < 1e-20, far below fp32 rounding.  The outputs
 of the last 128 tokens of a 576-token window are then, to that residue, the
 oracle's run over the window alone from a zero state; the first window
-starts at token 0 from the true S0 and is exact throughout."""
+starts at token 0 from the true S0 and is exact throughout.
+
+Decode over 81,920 (sequence, head) states (5.4 GB of fp32 state, 64 KiB
+each): one step and a four-token launch, checked on the sequences whose
+states sit at the start, across 2^31 and 2^32 bytes and at the end."""
 import pytest
 import torch
 
@@ -72,3 +78,29 @@ def test_million_token_sequence(million, sched):
         if end == T:
             check("S_final", S, S_ref, TOL[torch.bfloat16])
     del o, S, ws
+
+
+DN, DH = 2048, 40                  # 81,920 states of 64 KiB
+# sequences holding unit 0, units 32767 / 32768 (2^31 bytes), 65535 / 65536
+# (2^32 bytes) and the last unit
+DSEQ = [0, 819, 1638, DN - 1]
+
+
+def test_decode_state_past_4gib():
+    import linear_attention_kda_amd as kda
+    Tk = 4
+    announce(f"decode over N{DN} H{DH} d{D} (5.4 GB of state): one step, then {Tk} tokens per launch")
+    inp = inputs.dense(DN, Tk, DH, D, D, torch.bfloat16, gate="uniform", alpha_lo=0.95, s0_std=0.02, seed=43,
+                       device="cuda")
+    S = inp["S0"].clone()
+    o1 = kda.decode_step(*(inp[key][:, 0].contiguous() for key in ("q", "k", "v", "alpha", "beta")), S)
+    o4, S4 = kda.decode_tokens(inp["q"], inp["k"], inp["v"], inp["alpha"], inp["beta"], inp["S0"],
+                               S_out=torch.empty_like(inp["S0"]))
+    torch.cuda.synchronize()
+    idx = torch.tensor(DSEQ, device="cuda")
+    for tk, o, St in ((1, o1[:, None], S), (Tk, o4, S4)):
+        sub = {key: inp[key].index_select(0, idx)[:, :tk] for key in ("q", "k", "v", "alpha", "beta")}
+        sub["S0"] = inp["S0"].index_select(0, idx)
+        o_ref, S_ref = oracle_prefill(sub)
+        check(f"o ({tk} token)", o.index_select(0, idx), o_ref, TOL[torch.bfloat16])
+        check(f"S ({tk} token)", St.index_select(0, idx), S_ref, TOL[torch.bfloat16])
