@@ -2529,67 +2529,87 @@ __device__ __forceinline__ void write_split_tables(const SplitTables &tb, int G)
 // Segment start states: S_0 = S0 (or zero), S_{g+1} = S_g M_g + X_g in fp32
 // (S-form, d_v x d_k; M_g's rows are the stored M^T rows, so the product is
 // sum_j S_g[r][j] Mt_g[j][c]).  Rows are independent: one workgroup per
-// (sequence, head, block of RB rows), a thread per row and 128 RB / 256
-// columns (4 at RB = 8, 2 at RB = 4); start is [B G H] x d_v x d_k.  Each segment's Mt
-// (64 KiB) sits in LDS, and the next one is loaded into registers while the
-// current product runs.  (Measured on 4 heads x 16 segments: 3.7 us per
-// segment at 8 rows per workgroup, about 3 at 4, which halves each thread's
-// products at twice the Mt reads from L2; with 32 rows per workgroup, 16 per
-// thread, and S read as scalars the product took 9.4 us per segment, bound
-// by LDS reads; reading Mt straight from memory inside the loop, 28 us.)
+// (sequence, head, block of RB = 4 rows); start is [B G H] x d_v x d_k.
+// Wave q takes the key channels j in [32 q, 32 q + 32) of the product and
+// lane c the columns 2c and 2c + 1: those 32 x 2 entries of Mt stay in the
+// lane's registers, loaded a segment ahead (one contiguous 512-byte row per
+// wave and load), the four rows of S_g are read from LDS as wave-wide
+// broadcasts, and the four waves' partial sums meet in LDS, where thread
+// (row q, columns 2c, 2c + 1) adds them to X_g.  Measured on 4 heads x 16
+// segments: 1.7 us per segment (the kernel 38 us), against about 3 us (49) for
+// the earlier form with all of Mt in LDS and a thread per row and column
+// pair, bound by its 256 KiB of LDS reads.  The bound now is moving Mt, 64
+// KiB per workgroup and segment: without those loads (results wrong, timing
+// only) a segment took 0.9 us, and loading Mt two segments ahead, or in eight
+// parts between the steps of the product, changed nothing.
 template <int RB>
 __global__ __launch_bounds__(256) void split_chain_kernel(const float *S0, const float *maps, float *start, int H,
                                                           int G, int n_units, SplitTables tb) {
   if (blockIdx.x == 0) write_split_tables(tb, G);
-  constexpr int DK = 128, DV = 128, NV = DK * DK / 4 / 256;  // 16-byte loads of Mt per thread
-  constexpr int TPR = 256 / RB, NC = DK / TPR;                 // threads per row, columns per thread
-  static_assert(NC == 2 || NC == 4, "two or four columns per thread");
-  typedef float vec __attribute__((ext_vector_type(NC)));
+  constexpr int DK = 128, DV = 128, JQ = DK / 4;  // key channels per wave
+  static_assert(RB == 4, "four rows per workgroup: one per wave in the sums");
+  typedef float f2 __attribute__((ext_vector_type(2)));
   __shared__ __attribute__((aligned(16))) float sS[RB][DK];
-  __shared__ __attribute__((aligned(16))) float sM[DK][DK];
+  __shared__ __attribute__((aligned(16))) f2 sP[4][RB][64];  // partial sums: wave, row, column pair
   const int unit = blockIdx.x / (DV / RB), rb = blockIdx.x % (DV / RB);
   if (unit >= n_units) return;  // whole workgroup
   const int n = unit / H, h = unit % H;
-  const int t = threadIdx.x, row = t / TPR, cc = (t % TPR) * NC;  // this thread's row and first column
+  // product: wave q's channels, lane c's columns; sums: row q, the same columns
+  const int q = threadIdx.x >> 6, c = threadIdx.x & 63, cc = 2 * c;
   auto seg_maps = [&](int sg) { return maps + (((size_t)n * (G - 1) + sg) * H + h) * (size_t)(DV + DK) * DK; };
   auto start_row = [&](int sg) {
-    return start + (((size_t)n * G + sg) * H + h) * DV * DK + (size_t)(rb * RB + row) * DK + cc;
+    return start + (((size_t)n * G + sg) * H + h) * DV * DK + (size_t)(rb * RB + q) * DK + cc;
   };
   {
-    vec x = {};
-    if (S0) x = *reinterpret_cast<const vec *>(S0 + ((size_t)unit * DV + rb * RB + row) * DK + cc);
-    *reinterpret_cast<vec *>(&sS[row][cc]) = x;
-    *reinterpret_cast<vec *>(start_row(0)) = x;
+    f2 x = {0.f, 0.f};
+    if (S0) x = *reinterpret_cast<const f2 *>(S0 + ((size_t)unit * DV + rb * RB + q) * DK + cc);
+    *reinterpret_cast<f2 *>(&sS[q][cc]) = x;
+    *reinterpret_cast<f2 *>(start_row(0)) = x;
   }
-  f32x4 mv[NV];
-  if (G > 1) {
-    const f32x4 *Mt4 = reinterpret_cast<const f32x4 *>(seg_maps(0) + (size_t)DV * DK);
+  // Mt_sg's rows 32 q .. 32 q + 31 at columns cc, cc + 1, and X_sg's entries of this thread's sum
+  auto load_map = [&](int sg, f2 *m, f2 &x) {
+    x = *reinterpret_cast<const f2 *>(seg_maps(sg) + (size_t)(rb * RB + q) * DK + cc);
+    const float *Mt = seg_maps(sg) + (size_t)DV * DK + (size_t)(JQ * q) * DK + cc;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) mv[i] = Mt4[t + 256 * i];
-  }
-  for (int sg = 0; sg + 1 < G; ++sg) {
+    for (int jj = 0; jj < JQ; ++jj) m[jj] = *reinterpret_cast<const f2 *>(Mt + (size_t)jj * DK);
+  };
+  // one segment with the map in (m, x), the next one's loads into (mn, xn)
+  auto hop = [&](int sg, const f2 *m, const f2 x, f2 *mn, f2 &xn) {
+    __syncthreads();  // S_sg complete in sS
+    // the next segment's map, in flight during the product (the last
+    // segment reloads its own: every segment issues the same loads, so the
+    // waits for this segment's map can leave the next one's in flight)
+    load_map(sg + 2 < G ? sg + 1 : sg, mn, xn);
+    __builtin_amdgcn_sched_barrier(0);  // issued before the product, not sunk below it
+    f2 acc[RB];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) reinterpret_cast<f32x4 *>(&sM[0][0])[t + 256 * i] = mv[i];
-    vec acc = *reinterpret_cast<const vec *>(seg_maps(sg) + (size_t)(rb * RB + row) * DK + cc);
-    __syncthreads();  // sM and S_g complete
-    if (sg + 2 < G) {  // the next segment's Mt, in flight during the product
-      const f32x4 *Mt4 = reinterpret_cast<const f32x4 *>(seg_maps(sg + 1) + (size_t)DV * DK);
+    for (int r = 0; r < RB; ++r) acc[r] = f2{0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < NV; ++i) mv[i] = Mt4[t + 256 * i];
-    }
-#pragma unroll 2
-    for (int j = 0; j < DK; j += 4) {
-      const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&sS[row][j]);
+    for (int j4 = 0; j4 < JQ; j4 += 4) {
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const vec m = *reinterpret_cast<const vec *>(&sM[j + jj][cc]);
+      for (int r = 0; r < RB; ++r) {
+        const f32x4 s4 = *reinterpret_cast<const f32x4 *>(&sS[r][JQ * q + j4]);
 #pragma unroll
-        for (int e = 0; e < NC; ++e) acc[e] = __builtin_fmaf(s4[jj], m[e], acc[e]);
+        for (int jj = 0; jj < 4; ++jj) {
+          acc[r].x = __builtin_fmaf(s4[jj], m[j4 + jj].x, acc[r].x);
+          acc[r].y = __builtin_fmaf(s4[jj], m[j4 + jj].y, acc[r].y);
+        }
       }
     }
-    __syncthreads();  // every thread is done reading S_g and sM
-    *reinterpret_cast<vec *>(&sS[row][cc]) = acc;
-    *reinterpret_cast<vec *>(start_row(sg + 1)) = acc;
+#pragma unroll
+    for (int r = 0; r < RB; ++r) sP[q][r][c] = acc[r];
+    __syncthreads();  // partial sums complete, and every wave is done reading S_sg
+    f2 y = x;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) y += sP[w][q][c];
+    *reinterpret_cast<f2 *>(&sS[q][cc]) = y;
+    *reinterpret_cast<f2 *>(start_row(sg + 1)) = y;
+  };
+  f2 mA[JQ], mB[JQ], xA, xB;
+  if (G > 1) load_map(0, mA, xA);
+  for (int sg = 0; sg + 1 < G; sg += 2) {
+    hop(sg, mA, xA, mB, xB);
+    if (sg + 2 < G) hop(sg + 1, mB, xB, mA, xA);
   }
 }
 
