@@ -67,8 +67,9 @@ constexpr int kSchedErrTimeout = 1, kSchedErrXcd = 2;
 // the scan, so the split pays only when the units leave most of the chip
 // idle: G is chosen by a cost model in scan steps (the map pass at 0.8 of a
 // scan step with two compute waves per workgroup, or half the workgroups at
-// 1.3 times that with four; whole waves of 256 workgroups), and taken
-// automatically when it saves a quarter of the sequential chain.
+// 1.3 times that with four; whole waves of 256 workgroups; a chained segment
+// at about 1.2 scan steps), and taken automatically when it saves a quarter
+// of the sequential chain.
 struct SplitPlan {
   int G = 1;          // segments per sequence (1: no split)
   int cps = 0;        // chunks per segment (all but the last)
@@ -96,7 +97,7 @@ inline SplitPlan split_plan(int B, int T, int H, int dk, int dv, int esize) {
     const double map4 = (double)((wg4 + 255) / 256) * cps * 0.8 * 1.3;
     const bool four = wg2 > 256 && map4 < map2;
     const double waves3 = (double)((G * wg_scan + 255) / 256);
-    const double est = (four ? map4 : map2) + waves3 * cps + 2.0 * (G - 1);
+    const double est = (four ? map4 : map2) + waves3 * cps + 1.2 * (G - 1);
     if (est < best) {
       best = est;
       sp.G = G;
