@@ -37,14 +37,14 @@ NSETS = 4
 # Each figure belongs to the kernel source with the given sha256 prefix and is
 # reported as null once that source has changed.
 MEASURED_TRAFFIC = {
-    "prefill": ("kda_prefill.hip", "3aade25723d29ec3", 467_136_580),
+    "prefill": ("kda_prefill.hip", "3277a6bfc4657d66", 467_075_141),
     "decode": ("kda_decode.hip", "00e70acbccc2d272", 1_086_896_743),
     "decode_tokens": ("kda_decode.hip", "00e70acbccc2d272", 1_125_807_616),
     # measured under the two-phase schedule: counter collection serialises
     # kernels, which the overlapped schedule cannot run under
-    "long_context": ("kda_prefill.hip", "3aade25723d29ec3", 7_463_875_387),
-    "long_share": ("kda_prefill.hip", "3aade25723d29ec3", 1_200_191_904),
-    "varlen": ("kda_prefill.hip", "3aade25723d29ec3", 16_085_674_692),
+    "long_context": ("kda_prefill.hip", "3277a6bfc4657d66", 7_466_443_120),
+    "long_share": ("kda_prefill.hip", "3277a6bfc4657d66", 1_202_456_800),
+    "varlen": ("kda_prefill.hip", "3277a6bfc4657d66", 16_085_273_910),
 }
 
 
